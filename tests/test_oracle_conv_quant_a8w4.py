@@ -1,0 +1,293 @@
+"""Pins of the oracle's convolution (O4), dynamic quantizer (O5), A8W4 matmul
+(O6) and packed-blob writer (O7).  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rand_i8(rng, shape, lo=-128, hi=127):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.int8)
+
+
+# ------------------------------------------------------------------ O4
+@pytest.mark.parametrize("case", [
+    dict(NB=1, H=7, W=6, C=5, OC=4, KH=3, KW=3, stride=(1, 1), pad=(1, 1, 1, 1)),
+    dict(NB=2, H=9, W=8, C=3, OC=6, KH=3, KW=2, stride=(2, 1), pad=(0, 1, 2, 0)),
+    dict(NB=1, H=5, W=5, C=8, OC=3, KH=1, KW=1, stride=(1, 1), pad=(0, 0, 0, 0)),
+])
+def test_o4_direct_equals_im2col_gemm(orc, case):
+    rng = np.random.default_rng(11)
+    X = _rand_i8(rng, (case["NB"], case["H"], case["W"], case["C"]))
+    Wt = _rand_i8(rng, (case["OC"], case["C"], case["KH"], case["KW"]), -127, 127)
+    bias = rng.integers(-1000, 1001, case["OC"]).astype(np.int32)
+    zp = 7
+    direct = orc.conv2d_direct(X, zp, Wt, case["stride"], case["pad"], bias)
+    col = orc.im2col(X, zp, case["KH"], case["KW"], case["stride"], case["pad"])
+    Bnk = Wt.transpose(0, 2, 3, 1).reshape(case["OC"], -1)   # K order (ky, kx, ic)
+    acc = orc.gemm_affine(col, zp, Bnk, 0, bias, b_is_nk=True)
+    assert np.array_equal(direct.reshape(-1, case["OC"]), acc)
+
+
+def test_o4_pointwise_conv_is_a_plain_matmul(orc):
+    rng = np.random.default_rng(12)
+    X = _rand_i8(rng, (2, 4, 5, 6))
+    Wt = _rand_i8(rng, (3, 6, 1, 1), -127, 127)
+    out = orc.conv2d_direct(X, -4, Wt)
+    want = (X.reshape(-1, 6).astype(np.int64) + 4) @ Wt[:, :, 0, 0].T.astype(np.int64)
+    assert np.array_equal(out.reshape(-1, 3), want)
+
+
+def test_o4_delta_kernel_closed_form(orc):
+    """A weight that is 1 at the centre tap with oc == ic copies x - zp_in."""
+    rng = np.random.default_rng(13)
+    C = 4
+    X = _rand_i8(rng, (1, 6, 7, C))
+    Wt = np.zeros((C, C, 3, 3), np.int8)
+    for c in range(C):
+        Wt[c, c, 1, 1] = 1
+    out = orc.conv2d_direct(X, 7, Wt, (1, 1), (1, 1, 1, 1))
+    assert np.array_equal(out, X.astype(np.int64) - 7)
+    q, _ = orc.requant_matrix(out.reshape(-1, C), 1.0, np.ones(C, np.float32), 1.0, 0, True)
+    assert np.array_equal(q.reshape(out.shape), np.maximum(X.astype(np.int64) - 7, 0))
+
+
+def test_o4_pad_value_only_matters_on_the_border(orc):
+    rng = np.random.default_rng(14)
+    X = _rand_i8(rng, (1, 8, 8, 3))
+    Wt = _rand_i8(rng, (2, 3, 3, 3), -127, 127)
+    zp = 7
+    good = orc.im2col(X, zp, 3, 3, (1, 1), (1, 1, 1, 1))
+    bad = orc.im2col(X, 0, 3, 3, (1, 1), (1, 1, 1, 1))
+    Bnk = Wt.transpose(0, 2, 3, 1).reshape(2, -1)
+    a_good = orc.gemm_affine(good, zp, Bnk, 0, b_is_nk=True).reshape(8, 8, 2)
+    a_bad = orc.gemm_affine(bad, zp, Bnk, 0, b_is_nk=True).reshape(8, 8, 2)
+    assert np.array_equal(a_good[1:-1, 1:-1], a_bad[1:-1, 1:-1])
+    assert not np.array_equal(a_good[0], a_bad[0])
+    assert np.array_equal(a_good, orc.conv2d_direct(X, zp, Wt, (1, 1), (1, 1, 1, 1))[0])
+
+
+# ------------------------------------------------------------------ O5
+def test_o5_hand_worked_rows(orc):
+    for row in _gold("dynquant_worked.json")["rows"]:
+        q, sc, zp = orc.quantize_rows_s8(np.array(row["x"], np.float32))
+        assert sc[0] == np.float32(row["scale"]) and zp[0] == row["zp"]
+        assert q[0].tolist() == row["q"]
+
+
+def _adversarial_rows(rng, K):
+    rows = [rng.standard_normal(K).astype(np.float32),
+            (rng.standard_normal(K) * 1e-3 + 5).astype(np.float32),      # all positive
+            (-rng.random(K) * 40).astype(np.float32),                      # all negative
+            rng.uniform(-1e4, 3e-3, K).astype(np.float32),
+            np.zeros(K, np.float32)]
+    r = rng.standard_normal(K).astype(np.float32)
+    r[::3] = 0.0
+    rows.append(r)
+    return np.stack(rows)
+
+
+def test_o5_properties(orc):
+    rng = np.random.default_rng(15)
+    X = _adversarial_rows(rng, 257)
+    Q, S, Z = orc.quantize_rows_s8(X)
+    for x, q, s, z in zip(X, Q, S, Z):
+        q = q.astype(np.int64)
+        assert -128 <= z <= 127
+        assert np.all(q[x == 0] == z)                               # real zero is exact
+        order = np.argsort(x, kind="stable")
+        assert np.all(np.diff(q[order]) >= 0)                       # monotone
+        deq = (q - z).astype(np.float64) * np.float64(s)
+        assert np.all(np.abs(deq - x) <= np.float64(s) * (1 + 1e-6))  # within one step
+        if np.any(x != 0):
+            assert q[np.argmin(x)] in (-128, -127) or x.min() >= 0
+            assert s == np.float32((np.float32(max(0, x.max())) - np.float32(min(0, x.min()))) / np.float32(255))
+
+
+def test_o5_exact_ties_round_to_even(orc):
+    # scale 1 (range 255), zp -128: x = j + 1/2 is an exact tie.
+    x = np.array([0.0, 255.0] + [j + 0.5 for j in range(0, 254, 3)], np.float32)
+    q, s, z = orc.quantize_rows_s8(x)
+    assert s[0] == 1.0 and z[0] == -128
+    for xv, qv in zip(x[2:], q[0, 2:]):
+        j = int(xv - 0.5)
+        assert qv == (j if j % 2 == 0 else j + 1) - 128
+
+
+def test_o5_brute_force_grid(orc):
+    """Every row over a small grid of values: codes equal exact rational
+    rounding of x/scale (scale taken as the oracle's f32 value) whenever the
+    quotient is not within f32 rounding of a tie."""
+    vals = np.array([-3.0, -1.25, -0.5, 0.0, 0.75, 1.0, 2.5, 7.0], np.float32)
+    import itertools
+    for row in itertools.product(vals, repeat=3):
+        x = np.array(row, np.float32)
+        q, s, z = orc.quantize_rows_s8(x)
+        sf = Fraction(float(s[0]))
+        for xv, qv in zip(x, q[0]):
+            ex = Fraction(float(xv)) / sf
+            frac = ex - math.floor(ex)
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 16):
+                continue
+            want = max(-128, min(127, round(ex) + int(z[0])))
+            assert qv == want
+
+
+# ------------------------------------------------------------------ O6
+def test_o6_single_group_closed_form(orc):
+    rng = np.random.default_rng(16)
+    qa = _rand_i8(rng, (3, 32))
+    qw = _rand_i8(rng, (5, 32), -8, 7)
+    sa = np.array([0.5, 0.25, 0.125], np.float32)
+    za = np.array([3, -7, 0], np.int32)
+    sw = np.array([[2.0 ** -6], [2.0 ** -7], [2.0 ** -5], [2.0 ** -8], [2.0 ** -6]], np.float32)
+    bias = np.array([0.5, -0.25, 0, 1, -1], np.float32)
+    Y = orc.a8w4_blockwise(qa, sa, za, qw, sw, bias, -1e9, 1e9)
+    D = (qa.astype(np.int64) - za[:, None]) @ qw.T.astype(np.int64)
+    want = sa[:, None].astype(np.float64) * sw[:, 0][None, :] * D + bias[None, :]
+    assert np.array_equal(Y, want.astype(np.float32))   # powers of two: exact
+
+
+def test_o6_uniform_scales_reduce_to_integer_gemm(orc):
+    rng = np.random.default_rng(17)
+    qa = _rand_i8(rng, (4, 96))
+    qw = _rand_i8(rng, (6, 96), -8, 7)
+    sw = np.full((6, 3), 2.0 ** -4, np.float32)
+    Y = orc.a8w4_blockwise(qa, np.ones(4, np.float32), np.zeros(4, np.int32), qw, sw, None, -1e9, 1e9)
+    want = (qa.astype(np.int64) @ qw.T.astype(np.int64)) * 2.0 ** -4
+    assert np.array_equal(Y, want.astype(np.float32))
+
+
+def test_o6_each_group_uses_its_own_scale(orc):
+    K, G = 128, 4
+    qa = np.ones((1, K), np.int8)
+    sw = np.array([[1.0, 10.0, 100.0, 1000.0]], np.float32)
+    for g in range(G):
+        qw = np.zeros((1, K), np.int8)
+        qw[0, g * 32 + 5] = 3
+        Y = orc.a8w4_blockwise(qa, np.ones(1, np.float32), np.zeros(1, np.int32), qw, sw, None, -1e9, 1e9)
+        assert Y[0, 0] == 3 * sw[0, g]
+
+
+def test_o6_zero_point_and_clamp(orc):
+    qa = np.full((1, 64), -9, np.int8)
+    qw = np.full((2, 64), 7, np.int8)
+    sw = np.full((2, 2), 0.01, np.float32)
+    bias = np.array([0.25, 9.0], np.float32)
+    Y = orc.a8w4_blockwise(qa, np.array([0.3], np.float32), np.array([-9], np.int32), qw, sw, bias, -6, 6)
+    assert Y.tolist() == [[0.25, 6.0]]            # qa == za contributes real zero
+    Y = orc.a8w4_blockwise(qa, np.array([1.0], np.float32), np.array([0], np.int32), qw, sw, -bias, -6, 6)
+    assert Y[0, 1] == -6.0
+
+
+def test_o6_brute_force_against_exact_rationals(orc):
+    rng = np.random.default_rng(18)
+    for _ in range(20):
+        M, N, G = rng.integers(1, 4), rng.integers(1, 5), rng.integers(1, 4)
+        K = int(G * 32 - rng.integers(0, 31))
+        qa = _rand_i8(rng, (M, K))
+        qw = _rand_i8(rng, (N, K), -8, 7)
+        sa = rng.uniform(0.001, 0.1, M).astype(np.float32)
+        za = rng.integers(-128, 128, M).astype(np.int32)
+        sw = rng.uniform(0.002, 0.02, (N, G)).astype(np.float32)
+        bias = rng.uniform(-1, 1, N).astype(np.float32)
+        Y = orc.a8w4_blockwise(qa, sa, za, qw, sw, bias, -6, 6)
+        for m in range(M):
+            for n in range(N):
+                tot = Fraction(0)
+                for g in range(G):
+                    d = sum((int(qa[m, k]) - int(za[m])) * int(qw[n, k]) for k in range(g * 32, min(K, g * 32 + 32)))
+                    tot += Fraction(float(sw[n, g])) * d
+                y = Fraction(float(sa[m])) * tot + Fraction(float(bias[n]))
+                y = min(max(y, Fraction(-6)), Fraction(6))
+                ulp = np.spacing(np.float32(abs(float(y)))) if y != 0 else np.float32(1e-45)
+                assert abs(Fraction(float(Y[m, n])) - y) <= Fraction(float(ulp))
+
+
+def test_o6_full_path_from_float_activations(orc):
+    d = synth.a8w4(synth.BASE_SEED + 99, 2, 16, 64)
+    Y = orc.a8w4_forward(d["X"], d["W"], d["sw"], d["bias"], -6, 6)
+    # dequantized-activation float reference: the quantization error bound
+    qa, sa, za = orc.quantize_rows_s8(d["X"])
+    Xd = (qa.astype(np.float64) - za[:, None]) * sa[:, None]
+    Wd = d["W"].astype(np.float64) * np.repeat(d["sw"].astype(np.float64), 32, axis=1)
+    want = np.clip(Xd @ Wd.T + d["bias"], -6, 6)
+    assert np.allclose(Y, want, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ O7
+def _hdr(blob):
+    h = blob[:256]
+    u32 = h[:16].view(np.uint32)
+    i64 = h[16:104].view(np.int64)
+    keys = ["N", "K", "Npad", "Kpad", "group", "data_off", "data_bytes", "scale_off",
+            "sum_off", "zp_off", "total_bytes"]
+    d = dict(zip(keys, (int(v) for v in i64)))
+    d.update(magic=int(u32[0]), version=int(u32[1]), format=int(u32[2]), scheme=int(u32[3]),
+             has_zp=int(h[104:108].view(np.int32)[0]))
+    assert not h[108:].any()
+    return d
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (70, 129), (64, 64), (65, 200), (3, 576)])
+def test_o7_s8_blob_decodes_back(orc, N, K):
+    rng = np.random.default_rng(19)
+    W = _rand_i8(rng, (N, K))
+    sc = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    zp = rng.integers(-3, 3, N).astype(np.int32)
+    blob = orc.pack_s8_ref(W, sc, zp, per_channel=True)
+    h = _hdr(blob)
+    assert h["magic"] == 0x4B505149 and h["format"] == 1 and h["scheme"] == 1
+    assert (h["N"], h["K"]) == (N, K)
+    assert h["Npad"] % 64 == 0 and h["Kpad"] % 64 == 0 and h["Npad"] >= N and h["Kpad"] >= K
+    assert h["total_bytes"] == blob.size == orc.lib().orc_packed_s8_bytes(N, K)
+    data = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].view(np.int8).reshape(h["Npad"], h["Kpad"])
+    assert np.array_equal(data[:N, :K], W)
+    assert not data[N:].any() and not data[:, K:].any()
+    scales = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"]].view(np.float32)
+    assert np.array_equal(scales[:N], sc) and not scales[N:].any()
+    cs = blob[h["sum_off"]:h["sum_off"] + 4 * h["Npad"]].view(np.int32)
+    assert np.array_equal(cs[:N], W.astype(np.int64).sum(1)) and not cs[N:].any()
+    zz = blob[h["zp_off"]:h["zp_off"] + 4 * h["Npad"]].view(np.int32)
+    assert np.array_equal(zz[:N], zp) and h["has_zp"] == int(zp.any())
+    # same blob from a [K, N] source view
+    assert np.array_equal(orc.pack_s8_ref(np.ascontiguousarray(W.T).T, sc, zp), blob)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 100), (64, 4096 // 8), (130, 64)])
+def test_o7_s4_blob_decodes_back(orc, N, K):
+    rng = np.random.default_rng(20)
+    W = _rand_i8(rng, (N, K), -8, 7)
+    G = (K + 31) // 32
+    sw = rng.uniform(0.002, 0.02, (N, G)).astype(np.float32)
+    blob = orc.pack_s4_ref(W, sw, 32)
+    h = _hdr(blob)
+    assert h["format"] == 2 and h["group"] == 32 and h["Kpad"] == G * 32
+    raw = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].reshape(h["Npad"], h["Kpad"] // 32, 4, 4)
+    lo = (raw & 0xF).astype(np.int16)
+    hi = (raw >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    dec = np.concatenate([lo, hi], axis=3).reshape(h["Npad"], h["Kpad"])   # (run, w, [j | 4+j])
+    assert np.array_equal(dec[:N, :K], W) and not dec[N:].any() and not dec[:, K:].any()
+    sc = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"] * G].view(np.float32).reshape(h["Npad"], G)
+    assert np.array_equal(sc[:N], sw) and not sc[N:].any()
+    Wp = np.zeros((N, G * 32), np.int64)
+    Wp[:, :K] = W
+    gs = Wp.reshape(N, G, 32).sum(2)
+    ws = blob[h["sum_off"]:h["sum_off"] + 4 * h["Npad"]].view(np.float32)
+    want = np.array([math.fsum(float(a) * float(b) for a, b in zip(sw[n], gs[n])) for n in range(N)],
+                    np.float64).astype(np.float32)
+    assert np.array_equal(ws[:N], want) and not ws[N:].any()
