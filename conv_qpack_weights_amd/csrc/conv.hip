@@ -1,0 +1,93 @@
+// conv.hip -- INT8 NHWC convolution as explicit im2col + the INT8 GEMM.
+//
+// MNN "ConvInt8TiledExecutor.cpp" (DenseConvInt8TiledExecutor: static int8
+// convolution = im2col of the int8 input, padded with the input zero point,
+// then the int8 GEMM with the requantizing post-treatment).  The weights are
+// an int8 blob packed from OIHW with K ordered (kh, kw, ic).
+#include "qp_internal.hpp"
+
+namespace qp {
+namespace {
+
+struct ConvPlan {
+  int64_t OH, OW, M, ldcol, ws_col, ws_gemm;
+};
+
+qp_status plan_conv(const qp_qtensor* x, const qp_packed_info* w, int32_t KH, int32_t KW,
+                    int32_t sh, int32_t sw, int32_t pt, int32_t pl, int32_t pb, int32_t pr,
+                    ConvPlan* p) {
+  QP_REQUIRE(x && w, QP_EINVAL, "qconv2d: null descriptor");
+  QP_REQUIRE(x->dtype == QP_S8 && x->rank == 4, QP_EINVAL, "qconv2d: x must be rank-4 NHWC QP_S8");
+  QP_REQUIRE(w->format == 1, QP_EINVAL, "qconv2d: weights must be an int8 blob");
+  const int64_t NB = x->shape[0], H = x->shape[1], W = x->shape[2], C = x->shape[3];
+  QP_REQUIRE(NB > 0 && H > 0 && W > 0 && C > 0, QP_EINVAL, "qconv2d: empty input");
+  QP_REQUIRE(x->stride[3] == 1 && x->stride[2] == C && x->stride[1] == W * C &&
+                 x->stride[0] == H * W * C,
+             QP_EUNSUPPORTED, "qconv2d: x must be contiguous NHWC");
+  QP_REQUIRE(w->K == (int64_t)KH * KW * C, QP_EINVAL,
+             "qconv2d: weights have K=%lld, kernel needs KH*KW*C=%lld", (long long)w->K,
+             (long long)KH * KW * C);
+  qp_status st = conv_out_dims(H, W, KH, KW, sh, sw, pt, pl, pb, pr, &p->OH, &p->OW);
+  if (st) return st;
+  p->M = NB * p->OH * p->OW;
+  p->ldcol = w->Kpad;
+  p->ws_col = round_up(p->M * p->ldcol, 256);
+  p->ws_gemm = w->has_zero_points ? round_up(4 * p->M, 256) : 0;
+  return QP_OK;
+}
+
+}  // namespace
+}  // namespace qp
+
+extern "C" qp_status qconv2d_s8_im2col_ws_size(const qp_qtensor* x, const qp_packed_info* w,
+                                               int32_t KH, int32_t KW, int32_t stride_h,
+                                               int32_t stride_w, int32_t pad_t, int32_t pad_l,
+                                               int32_t pad_b, int32_t pad_r, size_t* bytes) {
+  using namespace qp;
+  QP_REQUIRE(bytes, QP_EINVAL, "qconv2d_s8_im2col_ws_size: null output");
+  ConvPlan p;
+  qp_status st = plan_conv(x, w, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, &p);
+  if (st) return st;
+  *bytes = (size_t)(p.ws_col + p.ws_gemm);
+  return QP_OK;
+}
+
+extern "C" qp_status qconv2d_s8_im2col(const qp_qtensor* x, const int8_t* X,
+                                       const qp_packed_info* w, const void* packedW_dev,
+                                       int32_t KH, int32_t KW, int32_t stride_h, int32_t stride_w,
+                                       int32_t pad_t, int32_t pad_l, int32_t pad_b, int32_t pad_r,
+                                       const int32_t* bias_dev, int64_t max_abs_bias,
+                                       const qp_qtensor* y, int32_t relu, void* Y, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  ConvPlan p;
+  qp_status st = plan_conv(x, w, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, &p);
+  if (st) return st;
+  QP_REQUIRE(x->scheme == QP_PER_TENSOR, QP_EUNSUPPORTED, "qconv2d: x must be per-tensor");
+  QP_REQUIRE(x->rounding == QP_ROUND_HALF_EVEN, QP_EUNSUPPORTED,
+             "qconv2d: only round-half-to-even is implemented");
+  bool out32 = false;
+  st = validate_gemm(w, w->K, x->scale, x->zero_point, bias_dev, max_abs_bias, y, &out32);
+  if (st) return st;
+  QP_REQUIRE(y->rank == 4 && y->shape[0] == x->shape[0] && y->shape[1] == p.OH &&
+                 y->shape[2] == p.OW && y->shape[3] == w->N,
+             QP_EINVAL, "qconv2d: y must be [N, OH, OW, OC] = [%lld, %lld, %lld, %lld]",
+             (long long)x->shape[0], (long long)p.OH, (long long)p.OW, (long long)w->N);
+  QP_REQUIRE(y->stride[3] == 1 && y->stride[2] == w->N && y->stride[1] == p.OW * w->N &&
+                 y->stride[0] == p.OH * p.OW * w->N,
+             QP_EUNSUPPORTED, "qconv2d: y must be contiguous NHWC");
+  QP_REQUIRE(X && packedW_dev && Y && ws, QP_EINVAL, "qconv2d: null data pointer");
+  QP_REQUIRE(ws_bytes >= (size_t)(p.ws_col + p.ws_gemm), QP_ESIZE,
+             "qconv2d: workspace holds %zu bytes, needs %lld", ws_bytes,
+             (long long)(p.ws_col + p.ws_gemm));
+  QP_REQUIRE(((uintptr_t)ws % 256) == 0, QP_EALIGN, "qconv2d: workspace must be 256-byte aligned");
+  int8_t* col = static_cast<int8_t*>(ws);
+  st = launch_im2col(X, x->shape[0], x->shape[1], x->shape[2], x->shape[3], x->zero_point, KH, KW,
+                     stride_h, stride_w, pad_t, pad_l, p.OH, p.OW, col, p.ldcol, stream);
+  if (st) return st;
+  void* gws = static_cast<uint8_t*>(ws) + p.ws_col;
+  return run_gemm_s8(col, p.M, p.ldcol, x->scale, x->zero_point, w, packedW_dev, bias_dev, y->scale,
+                     y->zero_point, out32, relu, Y, w->N, gws, ws_bytes - (size_t)p.ws_col, true,
+                     stream);
+}

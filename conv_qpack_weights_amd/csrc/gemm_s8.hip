@@ -1,0 +1,546 @@
+// gemm_s8.hip -- INT8 x INT8 GEMM with exact INT32 accumulation, zero-point
+// correction and a fused requantizing (or raw INT32) epilogue, for gfx950.
+//
+// Numeric contract: "Quantized GEMM: numeric contract, SRAM, DMA and result
+// verification" (teaching-NPU case study) --
+//   section 1: real = scale*(q - zp); bias at the accumulator scale; a
+//     per-channel weight scale gives a per-column integer multiplier/shift;
+//   section 2: padding must stand for real zero (here: zero bytes in both
+//     operands, with the zero-point terms computed over the real K -- the
+//     "equivalent mask");
+//   section 4: one INT32 accumulator per output, cleared once and kept over
+//     all of K; bias, activation and rescale only at the end;
+//   section 5: row-major A (base + m*lda + k); the blob rows play B.
+// MNN "ConvInt8TiledExecutor.cpp" (tileSplitFunction): clamp [-128,127], and
+// with ReLU the lower clamp is the output zero point.
+//
+// Kernel design (gfx950, prior art only from the pages): a workgroup owns a
+// BM x BN output tile; A and B tiles of BK bytes of K are staged through LDS,
+// double buffered (one barrier per K step); each wave runs
+// v_mfma_i32_16x16x64_i8 on 16-byte per-lane fragments read with one
+// ds_read_b128 each.  Both operands are K-contiguous rows, so the same loader
+// serves A and the packed B.  The MFMA is issued as (B-fragment, A-fragment),
+// so every lane ends up holding 4 consecutive output channels of one row:
+// one 4-byte (int8) or 16-byte (int32) store per 4 outputs.
+// The zero-point identity used is
+//   sum (a-zA)(b-zB) = sum ab - zB*rowsum(a) - zA*colsum(b) + K*zA*zB,
+// evaluated in wrapping 32-bit arithmetic, which is exact whenever the true
+// result fits INT32 (checked on the host with the K*65025+|bias| bound).
+#include <cmath>
+#include <cstring>
+
+#include "qp_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace qp {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+  const int8_t* A;
+  int64_t lda;
+  const int8_t* B;  // blob data, [Npad][Kpad]
+  int64_t M, N, K, Kpad, Npad;
+  const int32_t* colsum;
+  const int32_t* zpB;
+  const float* sB;
+  const int32_t* rowsum;  // [M] when the weights have zero points
+  const int32_t* bias;    // [N] or null
+  float sA, sOut;
+  int32_t zA, zp_out, lo, hi;
+  void* C;
+  int64_t ldc;
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;
+};
+
+namespace {
+
+// ---- per-column requantization parameters (device derivation) ------------
+// M_n = sA*sB/s_out in fp64; M_n = f*2^e, f in [0.5,1); m0 = rint(f*2^31),
+// 2^31 -> 2^30 with e+1; shift = 31 - e.  A column whose multiplier is not
+// positive and finite (the zero-scale padding columns) gets m0 = 0.
+__device__ __forceinline__ void derive_mult(float sA, float sB, float sOut, int32_t* m0,
+                                            int32_t* sh) {
+  double num = (double)sA * (double)sB;
+  double mr = num / (double)sOut;
+  if (!(mr > 0.0) || !(mr < INFINITY)) {
+    *m0 = 0;
+    *sh = 63;
+    return;
+  }
+  int e = 0;
+  double f = frexp(mr, &e);
+  int64_t q = (int64_t)rint(f * 2147483648.0);
+  if (q == ((int64_t)1 << 31)) {
+    q = (int64_t)1 << 30;
+    e += 1;
+  }
+  int s = 31 - e;
+  if (s < 0) {  // rejected on the host whenever the scales are known there
+    s = 0;
+    q = 0x7fffffff;
+  }
+  if (s > 63) s = 63;
+  *m0 = (int32_t)q;
+  *sh = s;
+}
+
+// RHE(acc*m0 / 2^sh) + zp, clamped to [lo, hi].
+__device__ __forceinline__ int32_t requant_one(int32_t acc, int32_t m0, int32_t sh, int32_t zp,
+                                               int32_t lo, int32_t hi) {
+  int64_t t = (int64_t)acc * (int64_t)m0;
+  int64_t r;
+  if (sh == 0) {
+    r = t;
+  } else if (sh >= 63) {
+    r = 0;
+  } else {
+    // floor((t + half - 1 + odd) / 2^sh) with odd = bit sh of t
+    int64_t odd = (t >> sh) & 1;
+    int64_t half_m1 = ((int64_t)1 << (sh - 1)) - 1;
+    r = (t + half_m1 + odd) >> sh;
+  }
+  int64_t v = r + zp;
+  v = v < lo ? lo : (v > hi ? hi : v);
+  return (int32_t)v;
+}
+
+// ---- LDS swizzle ----------------------------------------------------------
+// A tile row holds BK bytes as BK/16 chunks of 16 bytes; chunk c of row r is
+// stored at chunk position c ^ swz(r).  The XOR keeps both the 16-row
+// fragment reads and the row-wise tile writes free of bank conflicts for
+// 32 or 64 four-byte banks.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 128)
+    return (row ^ (row >> 3)) & 7;
+  else
+    return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool kOut32, bool kRowSum>
+__global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int CH = BK / 16;          // 16-byte chunks per tile row
+  constexpr int TM = BM / WM;          // wave tile, rows of A
+  constexpr int TN = BN / WN;          // wave tile, rows of B (output channels)
+  constexpr int FM = TM / 16;
+  constexpr int FN = TN / 16;
+  constexpr int A_CHUNKS = BM * CH / NT;
+  constexpr int B_CHUNKS = BN * CH / NT;
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(BM * CH % NT == 0 && BN * CH % NT == 0, "tile loads must divide evenly");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- tile index: XCD-aware, then grouped along M ----
+  const int nblk = gridDim.x;
+  int lin = blockIdx.x;
+  if ((nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
+  const int per_group = g.group_m * g.tiles_n;
+  const int grp = lin / per_group;
+  const int first_m = grp * g.group_m;
+  const int gsz = min(g.tiles_m - first_m, g.group_m);
+  const int within = lin - grp * per_group;
+  const int tile_m = first_m + within % gsz;
+  const int tile_n = within / gsz;
+  const int64_t m0 = (int64_t)tile_m * BM;
+  const int64_t n0 = (int64_t)tile_n * BN;
+
+  // ---- per-column epilogue constants ----
+  for (int j = tid; j < BN; j += NT) {
+    const int64_t n = n0 + j;
+    int32_t mm = 0, ss = 63, cc = 0, zb = 0;
+    if (n < g.N) {
+      derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
+      zb = g.zpB[n];
+      uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
+      c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
+      c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
+      cc = (int32_t)c;
+    }
+    col_m0[j] = mm;
+    col_sh[j] = ss;
+    col_c[j] = cc;
+    col_zb[j] = zb;
+  }
+
+  // ---- global -> register -> LDS tile loader ----
+  // Chunk i of this thread: row = row0 + i*RS of the tile, 16-byte chunk c.
+  constexpr int RS = NT / CH;
+  static_assert(NT % CH == 0, "threads must cover whole rows");
+  const int row0 = tid / CH, c0 = tid % CH;
+  const int8_t* a_base = g.A + c0 * 16;
+  const int8_t* b_base = g.B + c0 * 16;
+
+  v4i acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+  const int nk = (int)(g.Kpad / BK);
+
+#define QP_GLOAD(kt_)                                                                   \
+  do {                                                                                  \
+    const int64_t koff = (int64_t)(kt_) * BK;                                           \
+    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                               \
+      int64_t gm = m0 + row0 + i * RS;                                                  \
+      gm = gm < g.M ? gm : g.M - 1;                                                     \
+      ra[i] = *reinterpret_cast<const uint4*>(a_base + gm * g.lda + koff);               \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                               \
+      int64_t gn = n0 + row0 + i * RS;                                                  \
+      gn = gn < g.Npad ? gn : g.Npad - 1;                                               \
+      rb[i] = *reinterpret_cast<const uint4*>(b_base + gn * g.Kpad + koff);              \
+    }                                                                                   \
+  } while (0)
+
+#define QP_SSTORE(stage_)                                                               \
+  do {                                                                                  \
+    int8_t* base = smem + (stage_) * STAGE;                                             \
+    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                               \
+      const int row = row0 + i * RS;                                                    \
+      *reinterpret_cast<uint4*>(base + row * BK + ((c0 ^ swz<BK>(row)) * 16)) = ra[i];   \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                               \
+      const int row = row0 + i * RS;                                                    \
+      *reinterpret_cast<uint4*>(base + BM * BK + row * BK + ((c0 ^ swz<BK>(row)) * 16)) = \
+          rb[i];                                                                        \
+    }                                                                                   \
+  } while (0)
+
+  // fragment read offsets (within a stage)
+  const int frow = lane & 15;
+  const int fchunk = lane >> 4;  // 0..3 within a 64-byte K step
+
+  QP_GLOAD(0);
+  QP_SSTORE(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) QP_GLOAD(kt + 1);
+    const int8_t* sa = smem + cur * STAGE;
+    const int8_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int s = 0; s < BK / 64; ++s) {
+      v4i bf[FN], af[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int row = wn * TN + i * 16 + frow;
+        const int c = s * 4 + fchunk;
+        bf[i] = *reinterpret_cast<const v4i*>(sb + row * BK + ((c ^ swz<BK>(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int row = wm * TM + j * 16 + frow;
+        const int c = s * 4 + fchunk;
+        af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) QP_SSTORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef QP_GLOAD
+#undef QP_SSTORE
+
+  // ---- epilogue: lane holds channels n = 4*(lane/16)+i of row m = lane%16 ----
+  const bool c_vec = kOut32 ? ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 15) == 0)
+                            : ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 3) == 0);
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t m = m0 + wm * TM + j * 16 + (lane & 15);
+    if (m >= g.M) continue;
+    const int32_t rs = kRowSum ? g.rowsum[m] : 0;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int jn = wn * TN + i * 16 + 4 * (lane >> 4);
+      const int64_t n = n0 + jn;
+      int32_t out[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t a = (uint32_t)acc[i][j][r] + (uint32_t)col_c[jn + r];
+        if (kRowSum) a -= (uint32_t)col_zb[jn + r] * (uint32_t)rs;
+        if (kOut32)
+          out[r] = (int32_t)a;
+        else
+          out[r] = requant_one((int32_t)a, col_m0[jn + r], col_sh[jn + r], g.zp_out, g.lo, g.hi);
+      }
+      if (kOut32) {
+        int32_t* crow = static_cast<int32_t*>(g.C) + m * g.ldc;
+        if (c_vec && n + 3 < g.N) {
+          *reinterpret_cast<v4i*>(crow + n) = v4i{out[0], out[1], out[2], out[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < g.N) crow[n + r] = out[r];
+        }
+      } else {
+        int8_t* crow = static_cast<int8_t*>(g.C) + m * g.ldc;
+        if (c_vec && n + 3 < g.N) {
+          uint32_t w = (uint32_t)(uint8_t)out[0] | ((uint32_t)(uint8_t)out[1] << 8) |
+                       ((uint32_t)(uint8_t)out[2] << 16) | ((uint32_t)(uint8_t)out[3] << 24);
+          *reinterpret_cast<uint32_t*>(crow + n) = w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < g.N) crow[n + r] = (int8_t)out[r];
+        }
+      }
+    }
+  }
+}
+
+// ---- A preparation: copy to an aligned, K-padded buffer and/or row sums ---
+// One wave per row.  Writes Ap[m][0..Kpad) (zeros beyond K) when `copy`, and
+// rowsum[m] = sum_{k<K} A[m,k] when `rowsum` is non-null.
+__global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ A, int64_t M,
+                                                     int64_t K, int64_t lda, int8_t* __restrict__ Ap,
+                                                     int64_t Kpad, int32_t* __restrict__ rowsum) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= M) return;
+  const int8_t* src = A + m * lda;
+  int32_t s = 0;
+  if (Ap) {
+    int8_t* dst = Ap + m * Kpad;
+    for (int64_t k0 = (int64_t)lane * 16; k0 < Kpad; k0 += 64 * 16) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = k0 + 4 * q + j;
+          int32_t b = k < K ? src[k] : 0;
+          s += b;
+          v |= (uint32_t)(uint8_t)b << (8 * j);
+        }
+        w[q] = v;
+      }
+      *reinterpret_cast<uint4*>(dst + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    for (int64_t k = lane; k < K; k += 64) s += src[k];
+  }
+  if (rowsum) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) rowsum[m] = s;
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool kOut32, bool kRowSum>
+qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
+  GemmArgs a = a0;
+  a.tiles_m = (int32_t)ceil_div(a.M, BM);
+  a.tiles_n = (int32_t)ceil_div(a.N, BN);
+  a.group_m = 4;
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if (blocks == 0) return QP_OK;
+  QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
+  const size_t lds = 2 * (size_t)(BM + BN) * BK;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, WM, WN, kOut32, kRowSum>;
+  static bool lds_attr_set = false;  // once per instantiation; repeating it is harmless
+  if (!lds_attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      QP_FAIL(QP_EHIP, "qgemm: cannot reserve %zu bytes of LDS", lds);
+    lds_attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WM * WN * 64), lds, stream, a);
+  return check_launch("qgemm_s8s8 kernel");
+}
+
+template <bool kOut32, bool kRowSum>
+qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
+  const bool k128 = (a.Kpad % 128) == 0;
+  const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
+  if (k128 && big_tiles >= 256)
+    return launch_cfg<256, 256, 128, 2, 4, kOut32, kRowSum>(a, stream);
+  if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
+    return launch_cfg<128, 128, 128, 2, 2, kOut32, kRowSum>(a, stream);
+  return launch_cfg<64, 64, 64, 2, 2, kOut32, kRowSum>(a, stream);
+}
+
+}  // namespace
+
+// Host copy of the device multiplier derivation (validation only).
+static bool host_mult_ok(double mr) {
+  if (!(mr > 0.0) || !std::isfinite(mr)) return false;
+  int e = 0;
+  double f = std::frexp(mr, &e);
+  int64_t q = (int64_t)std::nearbyint(f * 2147483648.0);
+  if (q == ((int64_t)1 << 31)) e += 1;
+  return 31 - e >= 0;
+}
+
+struct GemmPlan {
+  bool copy_a;
+  bool rowsum;
+  int64_t ws_a, ws_rowsum, ws_total;
+};
+
+static GemmPlan plan_gemm(int64_t M, int64_t K, int64_t lda, const void* A,
+                          const qp_packed_info* b) {
+  GemmPlan p;
+  p.rowsum = b->has_zero_points != 0;
+  p.copy_a = (K != b->Kpad) || (lda % 16 != 0) || (((uintptr_t)A) % 16 != 0);
+  p.ws_a = p.copy_a ? round_up(M * b->Kpad, 256) : 0;
+  p.ws_rowsum = p.rowsum ? round_up(4 * M, 256) : 0;
+  p.ws_total = p.ws_a + p.ws_rowsum;
+  return p;
+}
+
+qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t zA,
+                      const qp_packed_info* b, const void* packedB, const int32_t* bias,
+                      float sOut, int32_t zp_out, bool out32, int32_t relu, void* C, int64_t ldc,
+                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream) {
+  const uint8_t* blob = static_cast<const uint8_t*>(packedB);
+  GemmPlan p = plan_gemm(M, b->K, lda, A, b);
+  if (a_is_padded) {
+    p.copy_a = false;
+    p.ws_a = 0;
+    p.ws_total = p.ws_rowsum;
+  }
+  QP_REQUIRE(ws_bytes >= (size_t)p.ws_total, QP_ESIZE, "qgemm: workspace holds %zu bytes, needs %lld",
+             ws_bytes, (long long)p.ws_total);
+  QP_REQUIRE(p.ws_total == 0 || (ws && ((uintptr_t)ws % 256) == 0), QP_EALIGN,
+             "qgemm: workspace must be non-null and 256-byte aligned");
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  int8_t* Ap = p.copy_a ? reinterpret_cast<int8_t*>(wsb) : nullptr;
+  int32_t* rs = p.rowsum ? reinterpret_cast<int32_t*>(wsb + p.ws_a) : nullptr;
+  if (M == 0) return QP_OK;
+  if (p.copy_a || p.rowsum) {
+    hipLaunchKernelGGL(prep_a_kernel, dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, stream, A, M,
+                       b->K, lda, Ap, b->Kpad, rs);
+    qp_status st = check_launch("qgemm prep A");
+    if (st) return st;
+  }
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = p.copy_a ? Ap : A;
+  a.lda = p.copy_a ? b->Kpad : lda;
+  a.B = reinterpret_cast<const int8_t*>(blob + b->data_off);
+  a.M = M;
+  a.N = b->N;
+  a.K = b->K;
+  a.Kpad = b->Kpad;
+  a.Npad = b->Npad;
+  a.colsum = reinterpret_cast<const int32_t*>(blob + b->sum_off);
+  a.zpB = reinterpret_cast<const int32_t*>(blob + b->zp_off);
+  a.sB = reinterpret_cast<const float*>(blob + b->scale_off);
+  a.rowsum = rs;
+  a.bias = bias;
+  a.sA = sA;
+  a.sOut = sOut;
+  a.zA = zA;
+  a.zp_out = zp_out;
+  a.lo = relu ? zp_out : -128;
+  a.hi = 127;
+  a.C = C;
+  a.ldc = ldc;
+  if (out32)
+    return p.rowsum ? launch_gemm_sel<true, true>(a, stream) : launch_gemm_sel<true, false>(a, stream);
+  return p.rowsum ? launch_gemm_sel<false, true>(a, stream) : launch_gemm_sel<false, false>(a, stream);
+}
+
+qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
+                        const int32_t* bias, int64_t max_abs_bias, const qp_qtensor* out,
+                        bool* out32) {
+  QP_REQUIRE(b && b->format == 1, QP_EINVAL, "qgemm: weights must be an int8 blob");
+  QP_REQUIRE(K == b->K, QP_EINVAL, "qgemm: activation K=%lld but the weights have K=%lld",
+             (long long)K, (long long)b->K);
+  QP_REQUIRE(zA >= -128 && zA <= 127, QP_EINVAL, "qgemm: activation zero point %d outside int8", zA);
+  QP_REQUIRE(std::isfinite(sA) && sA > 0, QP_EINVAL, "qgemm: activation scale must be > 0");
+  QP_REQUIRE(out, QP_EINVAL, "qgemm: output descriptor is NULL");
+  QP_REQUIRE(out->rounding == QP_ROUND_HALF_EVEN, QP_EUNSUPPORTED,
+             "qgemm: only round-half-to-even is implemented");
+  const int64_t bb = bias ? max_abs_bias : 0;
+  QP_REQUIRE(bb >= 0, QP_EINVAL, "qgemm: max_abs_bias must be >= 0");
+  QP_REQUIRE(K <= (INT64_C(2147483647) - bb) / 65025 && K * 65025 + bb <= INT64_C(2147483647),
+             QP_EOVERFLOW, "qgemm: K*65025 + max|bias| = %lld exceeds INT32",
+             (long long)(K * 65025 + bb));
+  if (out->dtype == QP_S8) {
+    *out32 = false;
+    QP_REQUIRE(out->qmin == -128 && out->qmax == 127, QP_EUNSUPPORTED,
+               "qgemm: int8 output saturation must be [-128,127]");
+    QP_REQUIRE(out->scheme == QP_PER_TENSOR, QP_EUNSUPPORTED, "qgemm: output must be per-tensor");
+    QP_REQUIRE(std::isfinite(out->scale) && out->scale > 0, QP_EINVAL,
+               "qgemm: output scale must be > 0");
+    QP_REQUIRE(out->zero_point >= -128 && out->zero_point <= 127, QP_EINVAL,
+               "qgemm: output zero point outside int8");
+    if (b->scale_max > 0.0f) {
+      const double mmax = ((double)sA * (double)b->scale_max) / (double)out->scale;
+      const double mmin = ((double)sA * (double)b->scale_min) / (double)out->scale;
+      QP_REQUIRE(host_mult_ok(mmax) && mmin > 0.0, QP_EUNSUPPORTED,
+                 "qgemm: requantization multiplier out of range (max %g)", mmax);
+    }
+  } else if (out->dtype == QP_S32) {
+    *out32 = true;
+  } else {
+    QP_FAIL(QP_EUNSUPPORTED, "qgemm: output dtype must be QP_S8 or QP_S32");
+  }
+  return QP_OK;
+}
+
+}  // namespace qp
+
+extern "C" qp_status qgemm_s8s8_requant_ws_size(const qp_qtensor* a, const qp_packed_info* b,
+                                                size_t* bytes) {
+  using namespace qp;
+  QP_REQUIRE(a && b && bytes, QP_EINVAL, "qgemm_s8s8_requant_ws_size: null argument");
+  QP_REQUIRE(a->rank == 2, QP_EINVAL, "qgemm: activations must be rank 2");
+  // The alignment of A is not known here; size for the copying plan.
+  GemmPlan p = plan_gemm(a->shape[0], a->shape[1], a->stride[0], nullptr, b);
+  if (!p.copy_a) {
+    p.copy_a = true;
+    p.ws_a = round_up(a->shape[0] * b->Kpad, 256);
+    p.ws_total = p.ws_a + p.ws_rowsum;
+  }
+  *bytes = (size_t)p.ws_total;
+  return QP_OK;
+}
+
+extern "C" qp_status qgemm_s8s8_requant(const qp_qtensor* a, const int8_t* A,
+                                        const qp_packed_info* b, const void* packedB_dev,
+                                        const int32_t* bias_dev, int64_t max_abs_bias,
+                                        const qp_qtensor* out, int32_t relu, void* C, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  QP_REQUIRE(a && b && out, QP_EINVAL, "qgemm: null descriptor");
+  QP_REQUIRE(a->dtype == QP_S8 && a->rank == 2, QP_EINVAL, "qgemm: A must be rank-2 QP_S8");
+  QP_REQUIRE(a->scheme == QP_PER_TENSOR, QP_EUNSUPPORTED, "qgemm: A must be per-tensor");
+  QP_REQUIRE(a->stride[1] == 1, QP_EUNSUPPORTED, "qgemm: A must be K-contiguous (stride[1] == 1)");
+  QP_REQUIRE(a->rounding == QP_ROUND_HALF_EVEN, QP_EUNSUPPORTED,
+             "qgemm: only round-half-to-even is implemented");
+  const int64_t M = a->shape[0], K = a->shape[1], lda = a->stride[0];
+  QP_REQUIRE(M >= 0 && K > 0 && lda >= K, QP_EINVAL, "qgemm: bad A shape/stride");
+  bool out32 = false;
+  qp_status st = validate_gemm(b, K, a->scale, a->zero_point, bias_dev, max_abs_bias, out, &out32);
+  if (st) return st;
+  QP_REQUIRE(out->rank == 2 && out->shape[0] == M && out->shape[1] == b->N, QP_EINVAL,
+             "qgemm: output shape must be [M, N] = [%lld, %lld]", (long long)M, (long long)b->N);
+  QP_REQUIRE(out->stride[1] == 1 && out->stride[0] >= b->N, QP_EINVAL,
+             "qgemm: output must be row-major with ldc >= N");
+  QP_REQUIRE(M == 0 || (A && packedB_dev && C), QP_EINVAL, "qgemm: null data pointer");
+  return run_gemm_s8(A, M, lda, a->scale, a->zero_point, b, packedB_dev, bias_dev, out->scale,
+                     out->zero_point, out32, relu, C, out->stride[0], ws, ws_bytes, false, stream);
+}

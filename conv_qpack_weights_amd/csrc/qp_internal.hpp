@@ -1,0 +1,79 @@
+// qp_internal.hpp -- helpers shared by the library's translation units:
+// error recording, the packed-blob header layout, integer helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/qpack.h"
+
+namespace qp {
+
+// ---- error recording (thread-local message behind qp_last_error) ----------
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+#define QP_FAIL(code, ...)     \
+  do {                         \
+    ::qp::set_error(__VA_ARGS__); \
+    return (code);             \
+  } while (0)
+
+#define QP_REQUIRE(cond, code, ...) \
+  do {                              \
+    if (!(cond)) QP_FAIL(code, __VA_ARGS__); \
+  } while (0)
+
+// Returns QP_EHIP with the runtime's message if the last launch failed.
+qp_status check_launch(const char* what);
+
+// ---- packed blob header (little endian, 256 bytes) ------------------------
+constexpr uint32_t kMagic = 0x4B505149u;  // "IQPK"
+constexpr uint32_t kVersion = 1u;
+constexpr int64_t kHeaderBytes = 256;
+constexpr int64_t kRegionAlign = 256;
+constexpr int64_t kPadN = 64;       // Npad multiple
+constexpr int64_t kPadK8 = 64;      // int8 Kpad multiple (one MFMA K-step)
+constexpr int64_t kRunK4 = 32;      // int4: 32 nibbles = 16 bytes per run
+constexpr int kInvalidFlagOffset = 108;
+
+struct alignas(16) BlobHeader {
+  uint32_t magic, version, format, scheme;
+  int64_t N, K, Npad, Kpad, group;
+  int64_t data_off, data_bytes, scale_off, sum_off, zp_off, total_bytes;
+  int32_t has_zp;
+  int32_t invalid_values;
+  uint8_t zero[256 - 112];
+};
+static_assert(sizeof(BlobHeader) == 256, "header is 256 bytes");
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// The blob geometry for a given format; shared by the size query, the packer
+// and qp_packed_info_from_header.
+qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, int64_t group,
+                        qp_packed_info* info);
+
+// ---- entry points shared between translation units ------------------------
+qp_status launch_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                               int64_t ldq, int64_t kfill, float* row_scale, int32_t* row_zp,
+                               hipStream_t stream);
+qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
+                        int32_t pt, int32_t pl, int32_t pb, int32_t pr, int64_t* OH, int64_t* OW);
+qp_status launch_im2col(const int8_t* X, int64_t NB, int64_t H, int64_t W, int64_t C,
+                        int32_t pad_value, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
+                        int32_t pt, int32_t pl, int64_t OH, int64_t OW, int8_t* col,
+                        int64_t ldcol, hipStream_t stream);
+qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
+                        const int32_t* bias, int64_t max_abs_bias, const qp_qtensor* out,
+                        bool* out32);
+qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t zA,
+                      const qp_packed_info* b, const void* packedB, const int32_t* bias,
+                      float sOut, int32_t zp_out, bool out32, int32_t relu, void* C, int64_t ldc,
+                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream);
+
+}  // namespace qp

@@ -1,0 +1,91 @@
+// status.cpp -- error strings, version, blob geometry.
+#include <cstdarg>
+#include <cstring>
+
+#include "qp_internal.hpp"
+
+namespace qp {
+
+static thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+qp_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) QP_FAIL(QP_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return QP_OK;
+}
+
+qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, int64_t group,
+                        qp_packed_info* info) {
+  QP_REQUIRE(N > 0 && K > 0, QP_EINVAL, "packed weights need N > 0 and K > 0 (got %lld, %lld)",
+             (long long)N, (long long)K);
+  qp_packed_info g;
+  std::memset(&g, 0, sizeof(g));
+  g.format = format;
+  g.scheme = scheme;
+  g.N = N;
+  g.K = K;
+  g.Npad = round_up(N, kPadN);
+  g.data_off = kHeaderBytes;
+  if (format == 1) {
+    g.group = 0;
+    g.Kpad = round_up(K, kPadK8);
+    g.data_bytes = g.Npad * g.Kpad;
+    g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
+    g.sum_off = g.scale_off + round_up(4 * g.Npad, kRegionAlign);
+    g.zp_off = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
+    g.total_bytes = g.zp_off + round_up(4 * g.Npad, kRegionAlign);
+  } else if (format == 2) {
+    QP_REQUIRE(group > 0 && group % kRunK4 == 0, QP_EUNSUPPORTED,
+               "int4 group size must be a positive multiple of 32 (got %lld)", (long long)group);
+    g.group = group;
+    g.Kpad = round_up(K, group);
+    g.data_bytes = g.Npad * g.Kpad / 2;
+    g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
+    g.sum_off = g.scale_off + round_up(4 * g.Npad * (g.Kpad / group), kRegionAlign);
+    g.zp_off = 0;
+    g.total_bytes = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
+  } else {
+    QP_FAIL(QP_EINVAL, "unknown packed format %d", format);
+  }
+  *info = g;
+  return QP_OK;
+}
+
+}  // namespace qp
+
+extern "C" {
+
+const char* qp_version(void) { return "qpack 0.1 gfx950"; }
+
+const char* qp_last_error(void) { return qp::g_last_error; }
+
+qp_status qp_packed_info_from_header(const void* header_host, qp_packed_info* info) {
+  QP_REQUIRE(header_host && info, QP_EINVAL, "qp_packed_info_from_header: null argument");
+  qp::BlobHeader h;
+  std::memcpy(&h, header_host, sizeof(h));
+  QP_REQUIRE(h.magic == qp::kMagic && h.version == qp::kVersion, QP_EINVAL,
+             "not a packed-weight blob (magic %08x, version %u)", h.magic, h.version);
+  qp_packed_info g;
+  qp_status st = qp::blob_geometry((int32_t)h.format, (int32_t)h.scheme, h.N, h.K, h.group, &g);
+  if (st != QP_OK) return st;
+  QP_REQUIRE(g.Npad == h.Npad && g.Kpad == h.Kpad && g.scale_off == h.scale_off &&
+                 g.sum_off == h.sum_off && g.total_bytes == h.total_bytes,
+             QP_EINVAL, "blob header is inconsistent with its own geometry");
+  QP_REQUIRE(h.invalid_values == 0, QP_EINVAL, "blob was packed from out-of-range int4 values");
+  g.has_zero_points = h.has_zp;
+  g.scale_min = 0.0f;
+  g.scale_max = 0.0f;
+  *info = g;
+  return QP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host -- with a status code
+and a message, before any launch."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def qp():
+    import conv_qpack_weights_amd as qp
+    return qp
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "qpack.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(q\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["qpack_weights", "qpack_weights_size", "qquantize_rows_s8", "qgemm_s8s8_requant",
+              "qgemm_a8w4_blockwise_f32", "qconv2d_s8_im2col", "qim2col_s8", "qp_last_error",
+              "qp_version", "qp_packed_info_from_header", "qgemm_a8w4_prequant_f32"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(qp):
+    raw = C.CDLL(qp.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(raw, n), "missing export " + n
+        assert n in qp.SIGNATURES, "binding lacks " + n
+    assert b"gfx950" in qp.lib().qp_version()
+
+
+def _expect(qp, status, code, needle=None):
+    assert status == code, (status, qp.last_error())
+    msg = qp.last_error()
+    assert msg
+    if needle:
+        assert needle in msg, msg
+
+
+def _w8_desc(qp, N=70, K=129, **kw):
+    return qp.qtensor(qp.QP_S8, [N, K], [K, 1], **kw)
+
+
+def test_pack_size_matches_the_reference_geometry(qp, orc):
+    for N, K in [(1, 1), (70, 129), (64, 576), (8192, 8192), (65, 63)]:
+        nb, al = qp.qpack_weights_size(_w8_desc(qp, N, K), 1, 0)
+        assert nb == orc.lib().orc_packed_s8_bytes(N, K) and al == 256
+        d4 = qp.qtensor(qp.QP_S4, [N, K], [K, 1], scheme=qp.QP_BLOCKWISE, group_size=32)
+        assert qp.qpack_weights_size(d4, 1, 0)[0] == orc.lib().orc_packed_s4_bytes(N, K, 32)
+
+
+def test_header_parser_reads_the_reference_blob(qp, orc):
+    rng = np.random.default_rng(1)
+    W = rng.integers(-128, 128, (70, 129)).astype(np.int8)
+    blob = orc.pack_s8_ref(W, np.full(70, 0.01, np.float32), np.full(70, -5, np.int32))
+    info = qp.qp_packed_info_from_header(blob[:256].tobytes())
+    assert (info.format, info.N, info.K, info.Npad, info.Kpad) == (1, 70, 129, 128, 192)
+    assert info.total_bytes == blob.size and info.has_zero_points == 1
+    W4 = rng.integers(-8, 8, (5, 100)).astype(np.int8)
+    blob4 = orc.pack_s4_ref(W4, np.ones((5, 4), np.float32))
+    info4 = qp.qp_packed_info_from_header(blob4[:256].tobytes())
+    assert (info4.format, info4.group, info4.Kpad, info4.total_bytes) == (2, 32, 128, blob4.size)
+    bad = bytearray(blob[:256].tobytes())
+    bad[0] ^= 0xFF
+    with pytest.raises(qp.QPackError):
+        qp.qp_packed_info_from_header(bytes(bad))
+
+
+def test_pack_rejects_bad_descriptors(qp):
+    nb, al = C.c_size_t(), C.c_size_t()
+    L = qp.lib()
+    d = _w8_desc(qp)
+    _expect(qp, L.qpack_weights_size(C.byref(d), 0, 0, C.byref(nb), C.byref(al)), qp.QP_EINVAL,
+            "permutation")
+    d3 = qp.qtensor(qp.QP_S8, [2, 3, 4], None)
+    _expect(qp, L.qpack_weights_size(C.byref(d3), 1, 0, C.byref(nb), C.byref(al)), qp.QP_EINVAL)
+    d4 = qp.qtensor(qp.QP_S4, [8, 64], [64, 1], scheme=qp.QP_BLOCKWISE, group_size=48)
+    _expect(qp, L.qpack_weights_size(C.byref(d4), 1, 0, C.byref(nb), C.byref(al)),
+            qp.QP_EUNSUPPORTED, "multiple of 32")
+    dz = qp.qtensor(qp.QP_S4, [8, 64], [64, 1], scheme=qp.QP_BLOCKWISE, group_size=32,
+                    zero_point=3)
+    _expect(qp, L.qpack_weights_size(C.byref(dz), 1, 0, C.byref(nb), C.byref(al)),
+            qp.QP_EUNSUPPORTED, "zero points")
+    dr = _w8_desc(qp, rounding=1)
+    _expect(qp, L.qpack_weights_size(C.byref(dr), 1, 0, C.byref(nb), C.byref(al)),
+            qp.QP_EUNSUPPORTED, "half-to-even")
+    info = qp.PackedInfo()
+    _expect(qp, L.qpack_weights(C.byref(d), C.c_void_p(FAKE), 1, 0, C.c_void_p(FAKE * 16), 100,
+                                C.byref(info), None), qp.QP_ESIZE)
+    _expect(qp, L.qpack_weights(C.byref(d), C.c_void_p(FAKE), 1, 0, C.c_void_p(FAKE + 16), 1 << 20,
+                                C.byref(info), None), qp.QP_EALIGN)
+
+
+def _info8(qp, N=70, K=129, has_zp=0, smin=0.001, smax=0.01):
+    i = qp.PackedInfo()
+    i.format, i.scheme, i.N, i.K = 1, qp.QP_PER_CHANNEL, N, K
+    i.Npad, i.Kpad = (N + 63) // 64 * 64, (K + 63) // 64 * 64
+    i.has_zero_points, i.scale_min, i.scale_max = has_zp, smin, smax
+    i.data_off, i.total_bytes = 256, 1 << 20
+    return i
+
+
+def _gemm(qp, a, info, out, bias=None, mab=0, ws_bytes=1 << 20):
+    return qp.lib().qgemm_s8s8_requant(C.byref(a), C.c_void_p(FAKE), C.byref(info),
+                                       C.c_void_p(FAKE * 16), bias, mab, C.byref(out), 0,
+                                       C.c_void_p(FAKE * 32), C.c_void_p(FAKE * 64), ws_bytes, None)
+
+
+def test_gemm_rejects_overflow_and_bad_arguments(qp):
+    K = 129
+    a = qp.qtensor(qp.QP_S8, [130, K], [K, 1], scale=0.02, zero_point=3)
+    out = qp.qtensor(qp.QP_S8, [130, 70], [70, 1], scale=0.5, zero_point=-2)
+    # [NPU] section 4: K*65025 + |bias| must fit INT32
+    limit = 2 ** 31 - 1 - K * 65025
+    _expect(qp, _gemm(qp, a, _info8(qp), out, C.c_void_p(FAKE), limit + 1), qp.QP_EOVERFLOW,
+            "exceeds INT32")
+    big = qp.qtensor(qp.QP_S8, [4, 40000], [40000, 1], scale=0.02)
+    _expect(qp, _gemm(qp, big, _info8(qp, K=40000), qp.qtensor(qp.QP_S32, [4, 70], [70, 1])),
+            qp.QP_EOVERFLOW)
+    _expect(qp, _gemm(qp, a, _info8(qp, K=128), out), qp.QP_EINVAL, "K=")
+    f32 = qp.qtensor(qp.QP_F32, [130, 70], [70, 1])
+    _expect(qp, _gemm(qp, a, _info8(qp), f32), qp.QP_EUNSUPPORTED)
+    sym = qp.qtensor(qp.QP_S8, [130, 70], [70, 1], scale=0.5, qmin=-127)
+    _expect(qp, _gemm(qp, a, _info8(qp), sym), qp.QP_EUNSUPPORTED, "[-128,127]")
+    _expect(qp, _gemm(qp, a, _info8(qp, smax=1e12), out), qp.QP_EUNSUPPORTED, "multiplier")
+    wrong = qp.qtensor(qp.QP_S8, [130, 71], [71, 1], scale=0.5)
+    _expect(qp, _gemm(qp, a, _info8(qp), wrong), qp.QP_EINVAL, "output shape")
+    kstride = qp.qtensor(qp.QP_S8, [130, K], [1, 130], scale=0.02)
+    _expect(qp, _gemm(qp, kstride, _info8(qp), out), qp.QP_EUNSUPPORTED, "K-contiguous")
+    # lda=129 forces the padded copy of A: a 0-byte workspace is too small
+    _expect(qp, _gemm(qp, a, _info8(qp), out, ws_bytes=0), qp.QP_ESIZE, "workspace")
+
+
+def test_gemm_overflow_limit_is_inclusive(qp):
+    # the largest allowed bound passes validation and fails only at the workspace check
+    K = 129
+    a = qp.qtensor(qp.QP_S8, [130, K], [K, 1], scale=0.02, zero_point=3)
+    out = qp.qtensor(qp.QP_S8, [130, 70], [70, 1], scale=0.5, zero_point=-2)
+    limit = 2 ** 31 - 1 - K * 65025
+    _expect(qp, _gemm(qp, a, _info8(qp), out, C.c_void_p(FAKE), limit, ws_bytes=0), qp.QP_ESIZE)
+
+
+def test_a8w4_quantize_im2col_conv_reject_bad_arguments(qp):
+    L = qp.lib()
+    i4 = qp.PackedInfo()
+    i4.format, i4.N, i4.K, i4.Npad, i4.Kpad, i4.group = 2, 64, 128, 64, 128, 64
+    _expect(qp, L.qgemm_a8w4_blockwise_f32(C.c_void_p(FAKE), 1, 128, 128, C.byref(i4),
+                                           C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 64,
+                                           None, 0, None), qp.QP_EUNSUPPORTED, "group")
+    i4.group = 32
+    _expect(qp, L.qgemm_a8w4_blockwise_f32(C.c_void_p(FAKE), 1, 100, 128, C.byref(i4),
+                                           C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 64,
+                                           None, 0, None), qp.QP_EINVAL, "K=")
+    _expect(qp, L.qgemm_a8w4_blockwise_f32(C.c_void_p(FAKE), 1, 128, 128, C.byref(i4),
+                                           C.c_void_p(FAKE), None, 6.0, -6.0, C.c_void_p(FAKE), 64,
+                                           None, 0, None), qp.QP_EINVAL, "clamp")
+    _expect(qp, L.qgemm_a8w4_blockwise_f32(C.c_void_p(FAKE), 4, 128, 128, C.byref(i4),
+                                           C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 64,
+                                           None, 0, None), qp.QP_ESIZE, "workspace")
+    i8 = _info8(qp)
+    _expect(qp, L.qgemm_a8w4_blockwise_f32(C.c_void_p(FAKE), 1, 129, 129, C.byref(i8),
+                                           C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 70,
+                                           None, 0, None), qp.QP_EINVAL, "int4")
+    _expect(qp, L.qquantize_rows_s8(C.c_void_p(FAKE), 2, 100, 100, C.c_void_p(FAKE), 99,
+                                    C.c_void_p(FAKE), C.c_void_p(FAKE), None), qp.QP_EINVAL)
+    _expect(qp, L.qim2col_s8(C.c_void_p(FAKE), 1, 8, 8, 4, 0, 3, 3, 1, 1, 1, 1, 1, 1,
+                             C.c_void_p(FAKE), 40, None), qp.QP_EINVAL, "multiple of 16")
+    _expect(qp, L.qim2col_s8(C.c_void_p(FAKE), 1, 8, 8, 4, 0, 3, 3, 0, 1, 1, 1, 1, 1,
+                             C.c_void_p(FAKE), 48, None), qp.QP_EINVAL, "positive")
+    x = qp.qtensor(qp.QP_S8, [1, 8, 8, 4], [256, 32, 4, 1], scale=0.05, zero_point=7)
+    y = qp.qtensor(qp.QP_S8, [1, 8, 8, 71], None, scale=0.1)
+    n = C.c_size_t()
+    _expect(qp, L.qconv2d_s8_im2col_ws_size(C.byref(x), C.byref(i8), 3, 3, 1, 1, 1, 1, 1, 1,
+                                            C.byref(n)), qp.QP_EINVAL, "KH*KW*C")
+    xs = qp.qtensor(qp.QP_S8, [1, 8, 8, 4], [512, 64, 8, 1], scale=0.05)
+    i36 = _info8(qp, K=36)
+    _expect(qp, L.qconv2d_s8_im2col_ws_size(C.byref(xs), C.byref(i36), 3, 3, 1, 1, 1, 1, 1, 1,
+                                            C.byref(n)), qp.QP_EUNSUPPORTED, "contiguous")
+    assert L.qconv2d_s8_im2col_ws_size(C.byref(x), C.byref(i36), 3, 3, 1, 1, 1, 1, 1, 1,
+                                       C.byref(n)) == qp.QP_OK
+    assert n.value >= 64 * 64
+    _expect(qp, L.qconv2d_s8_im2col(C.byref(x), C.c_void_p(FAKE), C.byref(i36), C.c_void_p(FAKE),
+                                    3, 3, 1, 1, 1, 1, 1, 1, None, 0, C.byref(y), 1,
+                                    C.c_void_p(FAKE), C.c_void_p(FAKE * 16), 1 << 20, None),
+            qp.QP_EINVAL, "y must be")

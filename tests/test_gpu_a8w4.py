@@ -1,0 +1,92 @@
+"""GPU parity of the A8W4 blockwise path (dynamic row quantization, int4
+group-32 weights, f32 dequantize + bias + clamp) against the oracle:
+|gpu - oracle| <= 1e-5 * max(1, |oracle|) for every output."""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def qp():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import conv_qpack_weights_amd as qp
+    return qp
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _host(t):
+    return t.cpu().numpy()
+
+
+def _check_close(got, want, what):
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    tol = RTOL * np.maximum(1.0, np.abs(want.astype(np.float64)))
+    bad = np.argwhere(err > tol)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d outside 1e-5*max(1,|o|); first at %s gpu=%r oracle=%r"
+                             % (what, len(bad), i, float(got[i]), float(want[i])))
+    return float((err / np.maximum(1.0, np.abs(want))).max())
+
+
+def _case(qp, orc, d, rows=None):
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]))
+    Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
+                                          d["clamp_lo"], d["clamp_hi"]))
+    X = d["X"] if rows is None else d["X"][rows]
+    want = orc.a8w4_forward(X, d["W"], d["sw"], d["bias"], d["clamp_lo"], d["clamp_hi"])
+    got = Y if rows is None else Y[rows]
+    return _check_close(got, want, "a8w4 f32 output")
+
+
+def test_a8w4_gemv_workload(qp, orc):
+    _case(qp, orc, synth.a8w4_gemv())
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_a8w4_gemm_workload(qp, orc, M):
+    rows = None if M == 16 else np.r_[0:8, 60:68, 120:128]
+    _case(qp, orc, synth.a8w4_gemm(M), rows)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 70, 96), (1, 1, 32), (2, 130, 200), (3, 64, 4096),
+                                   (5, 77, 1000), (17, 100, 256), (40, 33, 64), (1, 4096, 33)])
+def test_a8w4_small_shapes_and_tails(qp, orc, M, N, K):
+    _case(qp, orc, synth.a8w4(synth.BASE_SEED + 7 * M + N + K, M, N, K))
+
+
+def test_a8w4_prequantized_entry(qp, orc):
+    d = synth.a8w4(synth.BASE_SEED + 50, 3, 300, 512)
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]))
+    import torch
+    q = torch.zeros((3, info.Kpad), dtype=torch.int8, device="cuda")
+    q, s, z = qp.qquantize_rows_s8(_dev(d["X"]), q=q)
+    Y = _host(qp.qgemm_a8w4_prequant_f32(q, s, z, blob, info, _dev(d["bias"]), -6.0, 6.0))
+    want = orc.a8w4_forward(d["X"], d["W"], d["sw"], d["bias"], -6, 6)
+    _check_close(Y, want, "prequant a8w4")
+
+
+def test_a8w4_no_bias_no_clamp(qp, orc):
+    d = synth.a8w4(synth.BASE_SEED + 60, 1, 256, 512)
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]))
+    Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info))
+    want = orc.a8w4_forward(d["X"], d["W"], d["sw"], None, -3.4e38, 3.4e38)
+    _check_close(Y, want, "a8w4 without bias or clamp")
+
+
+def test_a8w4_deterministic(qp):
+    d = synth.a8w4_gemv()
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]))
+    X, b = _dev(d["X"]), _dev(d["bias"])
+    first = _host(qp.qgemm_a8w4_blockwise_f32(X, blob, info, b, -6.0, 6.0))
+    for _ in range(10):
+        assert np.array_equal(first, _host(qp.qgemm_a8w4_blockwise_f32(X, blob, info, b, -6.0, 6.0)))

@@ -231,3 +231,18 @@ def test_o3_matrix_is_per_column(orc):
     acc = np.array([[100, 100], [-7, 9]], np.int64)
     out, nd = orc.requant_matrix(acc, 1.0, np.array([0.5, 0.25], np.float32), 1.0, 0, False)
     assert out.tolist() == [[50, 25], [-4, 2]] and nd == 0
+
+
+def test_fp64_matmul_formulation_equals_o1(orc):
+    from oracle.matmul_f64 import gemm_affine_f64
+    rng = np.random.default_rng(8)
+    A, Bnk = _rand_i8(rng, (37, 300)), _rand_i8(rng, (29, 300))
+    zB = rng.integers(-128, 128, 29).astype(np.int32)
+    bias = rng.integers(-1000, 1001, 29).astype(np.int32)
+    want = orc.gemm_affine(A, -11, Bnk, zB, bias, b_is_nk=True)
+    assert np.array_equal(gemm_affine_f64(A, -11, Bnk, zB, bias), want)
+    assert np.array_equal(gemm_affine_f64(A, -11, Bnk, zB, bias, rows=[3, 5]), want[[3, 5]])
+    # the attained INT32 bound is reproduced exactly
+    K = 129
+    acc = gemm_affine_f64(np.full((1, K), -128, np.int8), 127, np.full((1, K), 127, np.int8), -128)
+    assert acc[0, 0] == -K * 65025
