@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized integer matmul path on one MI355X.
+
+One step = one call of the INT8 GEMM with the fused zero-point correction and
+requantizing epilogue (qgemm_s8s8_requant) on the 8192^3 per-channel workload,
+inputs resident in HBM, weights packed once beforehand (a load-time step).
+The timed region is exactly --steps calls, bracketed by device
+synchronization; HIP events on the launch stream give the per-kernel average.
+
+Also reported (same JSON line, key "workloads"): the A8W4 GEMV (cold weights
+rotated through > 2x the 256 MiB Infinity Cache, and warm), the A8W4 GEMM at
+M=16/128, the raw-INT32 variant of the large GEMM, the 3x3 conv and the
+130x70x129 GEMM.  "cpu_baseline" times the scalar C oracle on a bounded
+sample of the primary workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "INT8 GEMM/conv TOPS & % MFMA peak; A8W4 GEMV GB/s & % HBM peak"
+PEAK_INT8_TOPS = 5000.0    # MI355X dense INT8 MFMA, TOPS
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
+INFINITY_CACHE = 256 << 20
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only-primary", action="store_true",
+                   help="skip the secondary workloads (used for profiling runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: --gpus %d is not supported (this build has no "
+              "multi-GPU path; see DESIGN.md for how the work would shard)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import conv_qpack_weights_amd as qp
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def ev_time(fn, reps):
+        """Average milliseconds per call, HIP events on the current stream."""
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / reps
+
+    # ------------------------------------------------------------ primary
+    g = synth.gemm_large()
+    M = N = K = 8192
+    blob, info = qp.pack_s8(d(g["W"]), scales=d(g["s_w"]))
+    A = d(g["A"])
+    C8 = torch.empty((M, N), dtype=torch.int8, device=dev)
+    C32 = torch.empty((M, N), dtype=torch.int32, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+
+    def step():
+        qp.qgemm_s8s8_requant(A, g["sA"], g["zA"], blob, info, None, 0, g["s_out"], g["zp_out"],
+                              False, out=C8, ws=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(a.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / a.steps
+    ops = 2.0 * M * N * K
+    ms_per_step = wall * 1e3 / a.steps
+    value = ops * a.steps / wall / 1e12
+    achieved = ops / (kern_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded SplitMix64; uniform int8 activations, symmetric int8 weights, "
+                "per-channel scales U[0.001,0.01])",
+        "config": {"workload": "int8_gemm_8192x8192x8192_per_channel_requant_int8",
+                   "M": M, "N": N, "K": K, "out": "int8", "zp_a": 0, "scale_a": 0.01,
+                   "scale_out": 1.0},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None, "kernel_ms": round(kern_ms, 4),
+                     "algorithmic": "2*M*N*K = %.4e int8 ops per launch" % ops},
+    }
+
+    workloads = {}
+    if not a.only_primary:
+        # raw INT32 variant of the same GEMM
+        def step32():
+            qp.qgemm_s8s8_requant(A, g["sA"], g["zA"], blob, info, None, 0, out_dtype="s32",
+                                  out=C32, ws=ws)
+        for _ in range(3):
+            step32()
+        ms32 = ev_time(step32, 20)
+        workloads["int8_gemm_8192_int32_out"] = {
+            "ms": round(ms32, 4), "TOPS": round(ops / ms32 / 1e9, 1),
+            "frac_mfma_peak": round(ops / ms32 / 1e9 / PEAK_INT8_TOPS, 4)}
+        del C32
+
+        # A8W4 GEMV, M=1, K=N=4096: cold (rotating weight copies) and warm
+        gv = synth.a8w4_gemv()
+        Wd, swd = d(gv["W"]), d(gv["sw"])
+        blob4, info4 = qp.pack_s4(Wd, swd)
+        Xg, bg = d(gv["X"]), d(gv["bias"])
+        Yg = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+        nbytes_alg = 4096 * 4096 // 2 + 4096 * 128 * 4 + 3 * 4096 * 4
+        copies = int(np.ceil(2 * INFINITY_CACHE / blob4.numel())) + 1
+        blobs = [blob4] + [blob4.clone() for _ in range(copies - 1)]
+        ws4 = torch.empty(256, dtype=torch.uint8, device=dev)
+        idx = [0]
+
+        def gemv_cold():
+            i = idx[0] = (idx[0] + 1) % copies
+            qp.qgemm_a8w4_blockwise_f32(Xg, blobs[i], info4, bg, -6.0, 6.0, out=Yg, ws=ws4)
+
+        def gemv_warm():
+            qp.qgemm_a8w4_blockwise_f32(Xg, blob4, info4, bg, -6.0, 6.0, out=Yg, ws=ws4)
+
+        for _ in range(copies):
+            gemv_cold()
+        ms_cold = ev_time(gemv_cold, 4 * copies)
+        for _ in range(10):
+            gemv_warm()
+        ms_warm = ev_time(gemv_warm, 200)
+        q, sa, za = qp.qquantize_rows_s8(Xg, q=torch.zeros((1, info4.Kpad), dtype=torch.int8,
+                                                             device=dev))
+
+        def gemv_pre_cold():
+            i = idx[0] = (idx[0] + 1) % copies
+            qp.qgemm_a8w4_prequant_f32(q, sa, za, blobs[i], info4, bg, -6.0, 6.0, out=Yg)
+        for _ in range(copies):
+            gemv_pre_cold()
+        ms_pre = ev_time(gemv_pre_cold, 4 * copies)
+        gbs = nbytes_alg / ms_cold / 1e6
+        workloads["a8w4_gemv_1x4096x4096"] = {
+            "quantize_plus_gemv_cold_us": round(ms_cold * 1e3, 3),
+            "GBps_cold": round(gbs, 1), "frac_hbm_peak_cold": round(gbs / PEAK_HBM_GBS, 4),
+            "gemv_only_cold_us": round(ms_pre * 1e3, 3),
+            "warm_cache_resident_us": round(ms_warm * 1e3, 3),
+            "algorithmic_bytes": nbytes_alg, "weight_copies_rotated": copies,
+            "note": "per-launch average over back-to-back launches (events)"}
+        del blobs
+
+        # A8W4 GEMM, M in {16, 128}, N=11008, K=4096
+        for Mg in (16, 128):
+            gg = synth.a8w4_gemm(Mg)
+            b4, i4 = qp.pack_s4(d(gg["W"]), d(gg["sw"]))
+            Xm, bm = d(gg["X"]), d(gg["bias"])
+            Ym = torch.empty((Mg, 11008), dtype=torch.float32, device=dev)
+            wsm = torch.empty(qp.qgemm_a8w4_blockwise_f32_ws_size(Mg, i4), dtype=torch.uint8,
+                              device=dev)
+            cps = int(np.ceil(2 * INFINITY_CACHE / b4.numel())) + 1
+            bl = [b4] + [b4.clone() for _ in range(cps - 1)]
+            j = [0]
+
+            def gm_cold():
+                k = j[0] = (j[0] + 1) % cps
+                qp.qgemm_a8w4_blockwise_f32(Xm, bl[k], i4, bm, -6.0, 6.0, out=Ym, ws=wsm)
+            for _ in range(cps):
+                gm_cold()
+            msg = ev_time(gm_cold, 3 * cps)
+            byt = 11008 * 4096 // 2 + 11008 * 128 * 4 + Mg * 4096 * 4 + 11008 * 4 + Mg * 11008 * 4
+            mac = Mg * 11008 * 4096
+            workloads["a8w4_gemm_%dx11008x4096" % Mg] = {
+                "cold_us": round(msg * 1e3, 2), "GBps": round(byt / msg / 1e6, 1),
+                "frac_hbm_peak": round(byt / msg / 1e6 / PEAK_HBM_GBS, 4),
+                "TOPS": round(2 * mac / msg / 1e9, 2),
+                "frac_mfma_peak": round(2 * mac / msg / 1e9 / PEAK_INT8_TOPS, 5)}
+            del bl
+
+        # 3x3 conv 56x56x64 -> 64 via im2col + GEMM
+        c = synth.conv3x3_nhwc()
+        bc, ic = qp.pack_s8(d(c["W"]), scales=d(c["s_w"]))
+        Xc, bic = d(c["X"]), d(c["bias"])
+        Yc = torch.empty((1, 56, 56, 64), dtype=torch.int8, device=dev)
+
+        def conv():
+            qp.qconv2d_s8_im2col(Xc, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"],
+                                 bic, 1000, c["s_out"], c["zp_out"], True, out=Yc)
+        for _ in range(10):
+            conv()
+        msc = ev_time(conv, 200)
+        copsn = 2.0 * 3136 * 64 * 576
+        workloads["conv3x3_56x56x64_to_64"] = {
+            "us": round(msc * 1e3, 2), "TOPS": round(copsn / msc / 1e9, 2),
+            "frac_mfma_peak": round(copsn / msc / 1e9 / PEAK_INT8_TOPS, 5),
+            "note": "im2col + GEMM launches; latency-bound at this size"}
+
+        # 130x70x129 per-tensor GEMM (the worked example's shape)
+        s = synth.gemm_affine_per_tensor()
+        bs, is_ = qp.pack_s8(d(s["B"]), scale=s["sB"], zero_point=s["zB"], k_axis=0, n_axis=1)
+        As_, biass = d(s["A"]), d(s["bias"])
+        Ys = torch.empty((130, 70), dtype=torch.int8, device=dev)
+        wss = torch.empty(qp.qgemm_s8s8_requant_ws_size(
+            qp.qtensor(qp.QP_S8, [130, 129], [129, 1]), is_), dtype=torch.uint8, device=dev)
+
+        def small():
+            qp.qgemm_s8s8_requant(As_, s["sA"], s["zA"], bs, is_, biass, 1000, s["s_out"],
+                                  s["zp_out"], False, out=Ys, ws=wss)
+        for _ in range(10):
+            small()
+        mss = ev_time(small, 200)
+        workloads["gemm_130x70x129_per_tensor"] = {
+            "us": round(mss * 1e3, 2), "TOPS": round(2 * 130 * 70 * 129 / mss / 1e9, 4),
+            "note": "A repack + GEMM launches; latency-bound"}
+    out["workloads"] = workloads
+
+    # ------------------------------------------------------------ CPU baseline
+    if not a.no_cpu_baseline:
+        import oracle
+        rows = int(os.environ.get("QP_CPU_SAMPLE_ROWS", "256"))
+        Ah, Wh = g["A"], g["W"]
+        t0 = time.perf_counter()
+        acc = oracle.gemm_affine(Ah[:rows], 0, Wh, 0, None, b_is_nk=True)
+        oracle.requant_matrix(acc, g["sA"], g["s_w"], g["s_out"], g["zp_out"], False)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(2.0 * rows * N * K / cpu_s / 1e12, 6), "unit": "TOPS", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of 8192 rows of the 8192^3 GEMM (O1 integer GEMM + O3 requant, "
+                      "scalar C, one thread), %.1f s" % (rows, cpu_s)}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
