@@ -72,6 +72,27 @@ def main():
         e.synchronize()
         return s.elapsed_time(e) / reps
 
+    def graph_time(fn, calls, replays=20):
+        """Milliseconds per call of `fn`, from a HIP graph holding `calls`
+        back-to-back calls, replayed `replays` times between two events (no
+        host launch overhead between kernels)."""
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(calls):
+                fn()
+        gr.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(replays):
+            gr.replay()
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / (replays * calls)
+
     # ------------------------------------------------------------ primary
     g = synth.gemm_large()
     M = N = K = 8192
@@ -158,21 +179,15 @@ def main():
         def gemv_warm():
             qp.qgemm_a8w4_blockwise_f32(Xg, blob4, info4, bg, -6.0, 6.0, out=Yg, ws=ws4)
 
-        for _ in range(copies):
-            gemv_cold()
-        ms_cold = ev_time(gemv_cold, 4 * copies)
-        for _ in range(10):
-            gemv_warm()
-        ms_warm = ev_time(gemv_warm, 200)
+        ms_cold = graph_time(gemv_cold, copies)
+        ms_warm = graph_time(gemv_warm, 100)
         q, sa, za = qp.qquantize_rows_s8(Xg, q=torch.zeros((1, info4.Kpad), dtype=torch.int8,
                                                              device=dev))
 
         def gemv_pre_cold():
             i = idx[0] = (idx[0] + 1) % copies
             qp.qgemm_a8w4_prequant_f32(q, sa, za, blobs[i], info4, bg, -6.0, 6.0, out=Yg)
-        for _ in range(copies):
-            gemv_pre_cold()
-        ms_pre = ev_time(gemv_pre_cold, 4 * copies)
+        ms_pre = graph_time(gemv_pre_cold, copies)
         gbs = nbytes_alg / ms_cold / 1e6
         workloads["a8w4_gemv_1x4096x4096"] = {
             "quantize_plus_gemv_cold_us": round(ms_cold * 1e3, 3),
@@ -180,7 +195,7 @@ def main():
             "gemv_only_cold_us": round(ms_pre * 1e3, 3),
             "warm_cache_resident_us": round(ms_warm * 1e3, 3),
             "algorithmic_bytes": nbytes_alg, "weight_copies_rotated": copies,
-            "note": "per-launch average over back-to-back launches (events)"}
+            "note": "per-launch average, HIP graph replay of back-to-back launches (events)"}
         del blobs
 
         # A8W4 GEMM, M in {16, 128}, N=11008, K=4096
@@ -198,9 +213,7 @@ def main():
             def gm_cold():
                 k = j[0] = (j[0] + 1) % cps
                 qp.qgemm_a8w4_blockwise_f32(Xm, bl[k], i4, bm, -6.0, 6.0, out=Ym, ws=wsm)
-            for _ in range(cps):
-                gm_cold()
-            msg = ev_time(gm_cold, 3 * cps)
+            msg = graph_time(gm_cold, cps, 10)
             byt = 11008 * 4096 // 2 + 11008 * 128 * 4 + Mg * 4096 * 4 + 11008 * 4 + Mg * 11008 * 4
             mac = Mg * 11008 * 4096
             workloads["a8w4_gemm_%dx11008x4096" % Mg] = {
@@ -219,9 +232,7 @@ def main():
         def conv():
             qp.qconv2d_s8_im2col(Xc, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"],
                                  bic, 1000, c["s_out"], c["zp_out"], True, out=Yc)
-        for _ in range(10):
-            conv()
-        msc = ev_time(conv, 200)
+        msc = graph_time(conv, 50)
         copsn = 2.0 * 3136 * 64 * 576
         workloads["conv3x3_56x56x64_to_64"] = {
             "us": round(msc * 1e3, 2), "TOPS": round(copsn / msc / 1e9, 2),
@@ -239,9 +250,7 @@ def main():
         def small():
             qp.qgemm_s8s8_requant(As_, s["sA"], s["zA"], bs, is_, biass, 1000, s["s_out"],
                                   s["zp_out"], False, out=Ys, ws=wss)
-        for _ in range(10):
-            small()
-        mss = ev_time(small, 200)
+        mss = graph_time(small, 50)
         workloads["gemm_130x70x129_per_tensor"] = {
             "us": round(mss * 1e3, 2), "TOPS": round(2 * 130 * 70 * 129 / mss / 1e9, 4),
             "note": "A repack + GEMM launches; latency-bound"}

@@ -33,279 +33,10 @@
 
 #pragma clang fp contract(off)
 
+#include "gemm_s8_core.hpp"
+
 namespace qp {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-struct GemmArgs {
-  const int8_t* A;
-  int64_t lda;
-  const int8_t* B;  // blob data, [Npad][Kpad]
-  int64_t M, N, K, Kpad, Npad;
-  const int32_t* colsum;
-  const int32_t* zpB;
-  const float* sB;
-  const int32_t* rowsum;  // [M] when the weights have zero points
-  const int32_t* bias;    // [N] or null
-  float sA, sOut;
-  int32_t zA, zp_out, lo, hi;
-  void* C;
-  int64_t ldc;
-  int32_t tiles_m, tiles_n;
-  int32_t group_m;
-};
-
 namespace {
-
-// ---- per-column requantization parameters (device derivation) ------------
-// M_n = sA*sB/s_out in fp64; M_n = f*2^e, f in [0.5,1); m0 = rint(f*2^31),
-// 2^31 -> 2^30 with e+1; shift = 31 - e.  A column whose multiplier is not
-// positive and finite (the zero-scale padding columns) gets m0 = 0.
-__device__ __forceinline__ void derive_mult(float sA, float sB, float sOut, int32_t* m0,
-                                            int32_t* sh) {
-  double num = (double)sA * (double)sB;
-  double mr = num / (double)sOut;
-  if (!(mr > 0.0) || !(mr < INFINITY)) {
-    *m0 = 0;
-    *sh = 63;
-    return;
-  }
-  int e = 0;
-  double f = frexp(mr, &e);
-  int64_t q = (int64_t)rint(f * 2147483648.0);
-  if (q == ((int64_t)1 << 31)) {
-    q = (int64_t)1 << 30;
-    e += 1;
-  }
-  int s = 31 - e;
-  if (s < 0) {  // rejected on the host whenever the scales are known there
-    s = 0;
-    q = 0x7fffffff;
-  }
-  if (s > 63) s = 63;
-  *m0 = (int32_t)q;
-  *sh = s;
-}
-
-// RHE(acc*m0 / 2^sh) + zp, clamped to [lo, hi].
-__device__ __forceinline__ int32_t requant_one(int32_t acc, int32_t m0, int32_t sh, int32_t zp,
-                                               int32_t lo, int32_t hi) {
-  int64_t t = (int64_t)acc * (int64_t)m0;
-  int64_t r;
-  if (sh == 0) {
-    r = t;
-  } else if (sh >= 63) {
-    r = 0;
-  } else {
-    // floor((t + half - 1 + odd) / 2^sh) with odd = bit sh of t
-    int64_t odd = (t >> sh) & 1;
-    int64_t half_m1 = ((int64_t)1 << (sh - 1)) - 1;
-    r = (t + half_m1 + odd) >> sh;
-  }
-  int64_t v = r + zp;
-  v = v < lo ? lo : (v > hi ? hi : v);
-  return (int32_t)v;
-}
-
-// ---- LDS swizzle ----------------------------------------------------------
-// A tile row holds BK bytes as BK/16 chunks of 16 bytes; chunk c of row r is
-// stored at chunk position c ^ swz(r).  The XOR keeps both the 16-row
-// fragment reads and the row-wise tile writes free of bank conflicts for
-// 32 or 64 four-byte banks.
-template <int BK>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 128)
-    return (row ^ (row >> 3)) & 7;
-  else
-    return ((row >> 1) ^ (row >> 3)) & 3;
-}
-
-template <int BM, int BN, int BK, int WM, int WN, bool kOut32, bool kRowSum>
-__global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int CH = BK / 16;          // 16-byte chunks per tile row
-  constexpr int TM = BM / WM;          // wave tile, rows of A
-  constexpr int TN = BN / WN;          // wave tile, rows of B (output channels)
-  constexpr int FM = TM / 16;
-  constexpr int FN = TN / 16;
-  constexpr int A_CHUNKS = BM * CH / NT;
-  constexpr int B_CHUNKS = BN * CH / NT;
-  constexpr int STAGE = (BM + BN) * BK;
-  static_assert(BM * CH % NT == 0 && BN * CH % NT == 0, "tile loads must divide evenly");
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-
-  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // ---- tile index: XCD-aware, then grouped along M ----
-  const int nblk = gridDim.x;
-  int lin = blockIdx.x;
-  if ((nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
-  const int per_group = g.group_m * g.tiles_n;
-  const int grp = lin / per_group;
-  const int first_m = grp * g.group_m;
-  const int gsz = min(g.tiles_m - first_m, g.group_m);
-  const int within = lin - grp * per_group;
-  const int tile_m = first_m + within % gsz;
-  const int tile_n = within / gsz;
-  const int64_t m0 = (int64_t)tile_m * BM;
-  const int64_t n0 = (int64_t)tile_n * BN;
-
-  // ---- per-column epilogue constants ----
-  for (int j = tid; j < BN; j += NT) {
-    const int64_t n = n0 + j;
-    int32_t mm = 0, ss = 63, cc = 0, zb = 0;
-    if (n < g.N) {
-      derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
-      zb = g.zpB[n];
-      uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
-      c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
-      c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
-      cc = (int32_t)c;
-    }
-    col_m0[j] = mm;
-    col_sh[j] = ss;
-    col_c[j] = cc;
-    col_zb[j] = zb;
-  }
-
-  // ---- global -> register -> LDS tile loader ----
-  // Chunk i of this thread: row = row0 + i*RS of the tile, 16-byte chunk c.
-  constexpr int RS = NT / CH;
-  static_assert(NT % CH == 0, "threads must cover whole rows");
-  const int row0 = tid / CH, c0 = tid % CH;
-  const int8_t* a_base = g.A + c0 * 16;
-  const int8_t* b_base = g.B + c0 * 16;
-
-  v4i acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  const int nk = (int)(g.Kpad / BK);
-
-#define QP_GLOAD(kt_)                                                                   \
-  do {                                                                                  \
-    const int64_t koff = (int64_t)(kt_) * BK;                                           \
-    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                               \
-      int64_t gm = m0 + row0 + i * RS;                                                  \
-      gm = gm < g.M ? gm : g.M - 1;                                                     \
-      ra[i] = *reinterpret_cast<const uint4*>(a_base + gm * g.lda + koff);               \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                               \
-      int64_t gn = n0 + row0 + i * RS;                                                  \
-      gn = gn < g.Npad ? gn : g.Npad - 1;                                               \
-      rb[i] = *reinterpret_cast<const uint4*>(b_base + gn * g.Kpad + koff);              \
-    }                                                                                   \
-  } while (0)
-
-#define QP_SSTORE(stage_)                                                               \
-  do {                                                                                  \
-    int8_t* base = smem + (stage_) * STAGE;                                             \
-    _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                               \
-      const int row = row0 + i * RS;                                                    \
-      *reinterpret_cast<uint4*>(base + row * BK + ((c0 ^ swz<BK>(row)) * 16)) = ra[i];   \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                               \
-      const int row = row0 + i * RS;                                                    \
-      *reinterpret_cast<uint4*>(base + BM * BK + row * BK + ((c0 ^ swz<BK>(row)) * 16)) = \
-          rb[i];                                                                        \
-    }                                                                                   \
-  } while (0)
-
-  // fragment read offsets (within a stage)
-  const int frow = lane & 15;
-  const int fchunk = lane >> 4;  // 0..3 within a 64-byte K step
-
-  QP_GLOAD(0);
-  QP_SSTORE(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) QP_GLOAD(kt + 1);
-    const int8_t* sa = smem + cur * STAGE;
-    const int8_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int s = 0; s < BK / 64; ++s) {
-      v4i bf[FN], af[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * TN + i * 16 + frow;
-        const int c = s * 4 + fchunk;
-        bf[i] = *reinterpret_cast<const v4i*>(sb + row * BK + ((c ^ swz<BK>(row)) * 16));
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * TM + j * 16 + frow;
-        const int c = s * 4 + fchunk;
-        af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) QP_SSTORE(cur ^ 1);
-    __syncthreads();
-  }
-#undef QP_GLOAD
-#undef QP_SSTORE
-
-  // ---- epilogue: lane holds channels n = 4*(lane/16)+i of row m = lane%16 ----
-  const bool c_vec = kOut32 ? ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 15) == 0)
-                            : ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 3) == 0);
-#pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int64_t m = m0 + wm * TM + j * 16 + (lane & 15);
-    if (m >= g.M) continue;
-    const int32_t rs = kRowSum ? g.rowsum[m] : 0;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int jn = wn * TN + i * 16 + 4 * (lane >> 4);
-      const int64_t n = n0 + jn;
-      int32_t out[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t a = (uint32_t)acc[i][j][r] + (uint32_t)col_c[jn + r];
-        if (kRowSum) a -= (uint32_t)col_zb[jn + r] * (uint32_t)rs;
-        if (kOut32)
-          out[r] = (int32_t)a;
-        else
-          out[r] = requant_one((int32_t)a, col_m0[jn + r], col_sh[jn + r], g.zp_out, g.lo, g.hi);
-      }
-      if (kOut32) {
-        int32_t* crow = static_cast<int32_t*>(g.C) + m * g.ldc;
-        if (c_vec && n + 3 < g.N) {
-          *reinterpret_cast<v4i*>(crow + n) = v4i{out[0], out[1], out[2], out[3]};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < g.N) crow[n + r] = out[r];
-        }
-      } else {
-        int8_t* crow = static_cast<int8_t*>(g.C) + m * g.ldc;
-        if (c_vec && n + 3 < g.N) {
-          uint32_t w = (uint32_t)(uint8_t)out[0] | ((uint32_t)(uint8_t)out[1] << 8) |
-                       ((uint32_t)(uint8_t)out[2] << 16) | ((uint32_t)(uint8_t)out[3] << 24);
-          *reinterpret_cast<uint32_t*>(crow + n) = w;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < g.N) crow[n + r] = (int8_t)out[r];
-        }
-      }
-    }
-  }
-}
 
 // ---- A preparation: copy to an aligned, K-padded buffer and/or row sums ---
 // One wave per row.  Writes Ap[m][0..Kpad) (zeros beyond K) when `copy`, and
@@ -346,17 +77,19 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool kOut32, bool kRowSum>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, bool kOut32, bool kRowSum,
+          bool kHi>
 qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (int32_t)ceil_div(a.M, BM);
   a.tiles_n = (int32_t)ceil_div(a.N, BN);
   a.group_m = 4;
+  a.xcd_remap = 1;
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks == 0) return QP_OK;
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
-  const size_t lds = 2 * (size_t)(BM + BN) * BK;
-  auto kern = qgemm_s8_kernel<BM, BN, BK, WM, WN, kOut32, kRowSum>;
+  const size_t lds = (size_t)ST * (BM + BN) * BK;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, WM, WN, ST, MF, kOut32, kRowSum, kHi>;
   static bool lds_attr_set = false;  // once per instantiation; repeating it is harmless
   if (!lds_attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -368,15 +101,15 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   return check_launch("qgemm_s8s8 kernel");
 }
 
-template <bool kOut32, bool kRowSum>
+template <bool kOut32, bool kRowSum, bool kHi>
 qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
   const bool k128 = (a.Kpad % 128) == 0;
   const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (k128 && big_tiles >= 256)
-    return launch_cfg<256, 256, 128, 2, 4, kOut32, kRowSum>(a, stream);
+    return launch_cfg<256, 256, 128, 2, 4, 2, 32, kOut32, kRowSum, kHi>(a, stream);
   if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
-    return launch_cfg<128, 128, 128, 2, 2, kOut32, kRowSum>(a, stream);
-  return launch_cfg<64, 64, 64, 2, 2, kOut32, kRowSum>(a, stream);
+    return launch_cfg<128, 128, 128, 2, 2, 2, 32, kOut32, kRowSum, kHi>(a, stream);
+  return launch_cfg<64, 64, 64, 2, 2, 3, 32, kOut32, kRowSum, kHi>(a, stream);
 }
 
 }  // namespace
@@ -438,6 +171,7 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
   a.A = p.copy_a ? Ap : A;
   a.lda = p.copy_a ? b->Kpad : lda;
   a.B = reinterpret_cast<const int8_t*>(blob + b->data_off);
+  a.ldb = b->Kpad;
   a.M = M;
   a.N = b->N;
   a.K = b->K;
@@ -457,8 +191,17 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
   a.C = C;
   a.ldc = ldc;
   if (out32)
-    return p.rowsum ? launch_gemm_sel<true, true>(a, stream) : launch_gemm_sel<true, false>(a, stream);
-  return p.rowsum ? launch_gemm_sel<false, true>(a, stream) : launch_gemm_sel<false, false>(a, stream);
+    return p.rowsum ? launch_gemm_sel<true, true, false>(a, stream)
+                    : launch_gemm_sel<true, false, false>(a, stream);
+  // All shifts >= 32 <=> every multiplier < 1/2 (with margin for the m0
+  // rounding bump); known only when the scales were seen at pack time.
+  const bool hi = b->scale_max > 0.0f &&
+                  ((double)sA * (double)b->scale_max / (double)sOut) * (1.0 + 1e-6) < 0.5;
+  if (hi)
+    return p.rowsum ? launch_gemm_sel<false, true, true>(a, stream)
+                    : launch_gemm_sel<false, false, true>(a, stream);
+  return p.rowsum ? launch_gemm_sel<false, true, false>(a, stream)
+                  : launch_gemm_sel<false, false, false>(a, stream);
 }
 
 qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,

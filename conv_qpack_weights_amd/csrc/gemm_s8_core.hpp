@@ -1,0 +1,377 @@
+// gemm_s8_core.hpp -- the INT8 MFMA GEMM kernel and its epilogue helpers.
+//
+// Included by gemm_s8.hip; see there for the numeric contract.  The kernel:
+//  * workgroup tile BM x BN, K in steps of BK bytes, STAGES-deep LDS ring;
+//  * tiles move HBM/L2 -> LDS with gfx950's direct loads
+//    (global_load_lds_dwordx4): each lane names the 16-byte chunk that lands
+//    at its slot, so the XOR swizzle is applied on the global side and no
+//    VGPRs stage the data;
+//  * each wave computes a TM x TN sub-tile with v_mfma_i32_16x16x64_i8 from
+//    16-byte fragments (one ds_read_b128 each), issued as
+//    (B-fragment, A-fragment) so a lane holds 4 consecutive channels of one
+//    output row;
+//  * one barrier per K step; the prefetch distance is STAGES-1 tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qp {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+struct GemmArgs {
+  const int8_t* A;
+  int64_t lda;
+  const int8_t* B;  // blob data, [Npad][Kpad]
+  int64_t ldb;      // row stride of B in bytes (Kpad for a blob)
+  int64_t M, N, K, Kpad, Npad;
+  const int32_t* colsum;
+  const int32_t* zpB;
+  const float* sB;
+  const int32_t* rowsum;  // [M] when the weights have zero points
+  const int32_t* bias;    // [N] or null
+  float sA, sOut;
+  int32_t zA, zp_out, lo, hi;
+  void* C;
+  int64_t ldc;
+  int32_t tiles_m, tiles_n;
+  int32_t group_m;   // tile rows per raster group
+  int32_t xcd_remap; // 1: give each XCD a contiguous range of the raster order
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | 0x70 | 0xF00);
+}
+
+// M_n = sA*sB/s_out in fp64; M_n = f*2^e, f in [0.5,1); m0 = rint(f*2^31),
+// 2^31 -> 2^30 with e+1; shift = 31 - e.
+// The kernel's rounding step needs 1 <= shift <= 62, so the two edge cases
+// are mapped to equivalent pairs: shift >= 63 (|acc*M| < 1/2 for every
+// acc, result 0) becomes (m0 = 0, shift = 1); shift == 0 (M >= 2^30, every
+// non-zero acc saturates, acc = 0 gives 0) becomes (2^31-1, 1), which
+// saturates the same way.  A column whose multiplier is not positive and
+// finite (the zero-scale padding columns) gets (0, 1).
+__device__ __forceinline__ void derive_mult(float sA, float sB, float sOut, int32_t* m0,
+                                            int32_t* sh) {
+#pragma clang fp contract(off)
+  double num = (double)sA * (double)sB;
+  double mr = num / (double)sOut;
+  if (!(mr > 0.0) || !(mr < __builtin_huge_val())) {
+    *m0 = 0;
+    *sh = 1;
+    return;
+  }
+  int e = 0;
+  double f = __builtin_frexp(mr, &e);
+  int64_t q = (int64_t)__builtin_rint(f * 2147483648.0);
+  if (q == ((int64_t)1 << 31)) {
+    q = (int64_t)1 << 30;
+    e += 1;
+  }
+  int s = 31 - e;
+  if (s <= 0) {  // s < 0 is rejected on the host whenever the scales are known there
+    s = 1;
+    q = 0x7fffffff;
+  } else if (s >= 63) {
+    s = 1;
+    q = 0;
+  }
+  *m0 = (int32_t)q;
+  *sh = s;
+}
+
+// RHE(acc*m0 / 2^sh), 1 <= sh <= 62:
+// floor((t + 2^(sh-1) - 1 + odd) / 2^sh) with odd = bit sh of t; |t| < 2^62.
+__device__ __forceinline__ int64_t rhe_shift64(int32_t acc, int32_t m0, int32_t sh) {
+  const int64_t t = (int64_t)acc * (int64_t)m0;
+  const int64_t odd = (t >> sh) & 1;
+  const int64_t half_m1 = ((int64_t)1 << (sh - 1)) - 1;
+  return (t + half_m1 + odd) >> sh;
+}
+
+// The same rounding when sh >= 32, in 32-bit pieces: u = t + 2^(sh-1) (one
+// 32x32+64 multiply-add); floor(u / 2^sh) is the high word shifted by sh-32;
+// u being a multiple of 2^sh marks an exact tie, which rounds to even.
+__device__ __forceinline__ int32_t rhe_shift_hi(int32_t acc, int32_t m0, int64_t half,
+                                                int32_t s2, uint32_t mask) {
+  const int64_t u = (int64_t)acc * (int64_t)m0 + half;
+  const int32_t hi = (int32_t)(u >> 32);
+  const uint32_t lo = (uint32_t)u;
+  int32_t r = hi >> s2;
+  const bool tie = (lo == 0u) & (((uint32_t)hi & mask) == 0u);
+  return r - (int32_t)(tie & (r & 1));
+}
+
+__device__ __forceinline__ int32_t clamp_i64(int64_t v, int32_t lo, int32_t hi) {
+  v = v < lo ? lo : v;
+  v = v > hi ? hi : v;
+  return (int32_t)v;
+}
+
+__device__ __forceinline__ int32_t clamp_i32(int32_t v, int32_t lo, int32_t hi) {
+  return min(max(v, lo), hi);
+}
+
+// Chunk c of LDS row r sits at chunk position c ^ swz(r): conflict-free
+// 16-row fragment reads and row writes for 32 or 64 four-byte banks.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 128)
+    return (row ^ (row >> 3)) & 7;
+  else
+    return ((row >> 1) ^ (row >> 3)) & 3;
+}
+
+// kShiftHi: every column's shift is >= 32 (all multipliers below 1/2, known
+// on the host from the weight scales), so the rounding runs in 32-bit pieces.
+// MF: MFMA shape, 16 (v_mfma_i32_16x16x64_i8) or 32 (v_mfma_i32_32x32x32_i8).
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF, bool kOut32, bool kRowSum,
+          bool kShiftHi>
+__global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
+  constexpr int NW = WM * WN;
+  constexpr int CH = BK / 16;  // 16-byte chunks per tile row
+  constexpr int TM = BM / WM;
+  constexpr int TN = BN / WN;
+  constexpr int FM = TM / MF;
+  constexpr int FN = TN / MF;
+  constexpr int KSTEP = MF == 16 ? 64 : 32;  // K per MFMA
+  constexpr int NREG = MF == 16 ? 4 : 16;    // accumulator registers per MFMA
+  typedef int accv __attribute__((ext_vector_type(NREG)));
+  constexpr int A_SLOTS = BM * CH;  // 16-byte slots per A tile
+  constexpr int B_SLOTS = BN * CH;
+  constexpr int A_INS = A_SLOTS / (64 * NW);  // DMA instructions per wave per tile
+  constexpr int B_INS = B_SLOTS / (64 * NW);
+  constexpr int IPT = A_INS + B_INS;
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(A_SLOTS % (64 * NW) == 0 && B_SLOTS % (64 * NW) == 0, "tile/wave mismatch");
+  static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be a multiple of the MFMA");
+  static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(STAGES >= 2 && (STAGES - 2) * IPT < 64, "prefetch depth");
+
+  extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
+  __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- tile index: XCD-aware (dispatch round-robins over 8 XCDs), then
+  // grouped along M so concurrent workgroups share A rows and B rows in L2.
+  const int nblk = gridDim.x;
+  int lin = blockIdx.x;
+  if (g.xcd_remap && (nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
+  const int per_group = g.group_m * g.tiles_n;
+  const int grp = lin / per_group;
+  const int first_m = grp * g.group_m;
+  const int gsz = min(g.tiles_m - first_m, g.group_m);
+  const int within = lin - grp * per_group;
+  const int tile_m = first_m + within % gsz;
+  const int tile_n = within / gsz;
+  const int64_t m0 = (int64_t)tile_m * BM;
+  const int64_t n0 = (int64_t)tile_n * BN;
+
+  // ---- per-lane DMA source pointers: instruction j fills slots
+  // [(j*NW + wave)*64, +64); lane -> slot -> (row, swizzled chunk).
+  const int8_t* a_src[A_INS];
+  const int8_t* b_src[B_INS];
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j) {
+    const int s = (j * NW + wave) * 64 + lane;
+    const int row = s / CH, c = (s % CH) ^ swz<BK>(s / CH);
+    int64_t gm = m0 + row;
+    gm = gm < g.M ? gm : g.M - 1;
+    a_src[j] = g.A + gm * g.lda + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) {
+    const int s = (j * NW + wave) * 64 + lane;
+    const int row = s / CH, c = (s % CH) ^ swz<BK>(s / CH);
+    int64_t gn = n0 + row;
+    gn = gn < g.Npad ? gn : g.Npad - 1;
+    b_src[j] = g.B + gn * g.ldb + c * 16;
+  }
+  lds_void_t* lds_base = (lds_void_t*)smem;
+
+  auto issue = [&](int kt, int stage) {
+    const int64_t koff = (int64_t)kt * BK;
+    lds_void_t* sbase = (lds_void_t*)((__attribute__((address_space(3))) int8_t*)lds_base +
+                                      stage * STAGE);
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[j] + koff),
+                                       (lds_void_t*)((__attribute__((address_space(3))) int8_t*)sbase +
+                                                     (j * NW + wave) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[j] + koff),
+                                       (lds_void_t*)((__attribute__((address_space(3))) int8_t*)sbase +
+                                                     BM * BK + (j * NW + wave) * 1024),
+                                       16, 0, 0);
+  };
+
+  const int nk = (int)(g.Kpad / BK);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p, p);
+
+  // ---- per-column epilogue constants (overlaps the first loads) ----
+  for (int j = tid; j < BN; j += NW * 64) {
+    const int64_t n = n0 + j;
+    int32_t mm = 0, ss = 63, cc = 0, zb = 0;
+    if (n < g.N) {
+      derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
+      zb = g.zpB[n];
+      uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
+      c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
+      c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
+      cc = (int32_t)c;
+    }
+    col_m0[j] = mm;
+    col_sh[j] = ss;
+    col_c[j] = cc;
+    col_zb[j] = zb;
+  }
+
+  accv acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = accv{};
+
+  // fragment lane mapping: row = lane % MF, 16-byte chunk = lane / MF
+  const int frow = lane % MF;
+  const int fchunk = lane / MF;
+
+  __syncthreads();  // epilogue constants visible
+  for (int kt = 0; kt < nk; ++kt) {
+    // Tile kt has landed once at most (STAGES-2) younger tiles are in flight.
+    // The barrier is issued bare: every LDS read of the stage refilled below
+    // was consumed by an MFMA before this point, and the explicit vmcnt wait
+    // covers the direct loads, so no full memory fence is needed.
+    if (kt + STAGES - 2 < nk)
+      wait_vmcnt<(STAGES - 2) * IPT>();
+    else
+      wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const int8_t* sa = smem + (kt % STAGES) * STAGE;
+    const int8_t* sb = sa + BM * BK;
+#pragma unroll
+    for (int s = 0; s < BK / KSTEP; ++s) {
+      v4i bf[FN], af[FM];
+      const int c = s * (KSTEP / 16) + fchunk;
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const int row = wn * TN + i * MF + frow;
+        bf[i] = *reinterpret_cast<const v4i*>(sb + row * BK + ((c ^ swz<BK>(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int row = wm * TM + j * MF + frow;
+        af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          if constexpr (MF == 16)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- epilogue ----
+  // 16x16 MFMA: register r of a lane is channel 4*(lane/16)+r of row lane%16.
+  // 32x32 MFMA: register 4q+r is channel 8q+4*(lane/32)+r of row lane%32.
+  // Either way a lane owns runs of 4 consecutive channels of one row.
+  constexpr int QN = NREG / 4;  // runs of 4 channels per MFMA tile
+  const bool c_vec = kOut32 ? ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 15) == 0)
+                            : ((g.ldc & 3) == 0 && ((uintptr_t)g.C & 3) == 0);
+  const bool full = c_vec && (m0 + BM <= g.M) && (n0 + BN <= g.N);
+  int32_t rs[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    int64_t m = m0 + wm * TM + j * MF + (lane % MF);
+    rs[j] = (kRowSum && m < g.M) ? g.rowsum[m] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int jn = wn * TN + i * MF + (MF == 16 ? 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5));
+      const int64_t n = n0 + jn;
+      const v4i cc = *reinterpret_cast<const v4i*>(&col_c[jn]);
+      const v4i mm = *reinterpret_cast<const v4i*>(&col_m0[jn]);
+      const v4i ss = *reinterpret_cast<const v4i*>(&col_sh[jn]);
+      v4i zb = v4i{0, 0, 0, 0};
+      if (kRowSum) zb = *reinterpret_cast<const v4i*>(&col_zb[jn]);
+      int64_t half[4];
+      int32_t s2[4];
+      uint32_t mask[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s2[r] = ss[r] - 32;
+        half[r] = (int64_t)1 << (ss[r] - 1);
+        mask[r] = (1u << (s2[r] & 31)) - 1u;
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + wm * TM + j * MF + (lane % MF);
+        int32_t out[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
+          if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
+          if constexpr (kOut32) {
+            out[r] = (int32_t)a;
+          } else if constexpr (kShiftHi) {
+            out[r] = clamp_i32(rhe_shift_hi((int32_t)a, mm[r], half[r], s2[r], mask[r]) + g.zp_out,
+                               g.lo, g.hi);
+          } else {
+            out[r] = clamp_i64(rhe_shift64((int32_t)a, mm[r], ss[r]) + g.zp_out, g.lo, g.hi);
+          }
+        }
+        if (full) {
+          if constexpr (kOut32) {
+            *reinterpret_cast<v4i*>(static_cast<int32_t*>(g.C) + m * g.ldc + n) =
+                v4i{out[0], out[1], out[2], out[3]};
+          } else {
+            const uint32_t w = ((uint32_t)out[0] & 0xFFu) | (((uint32_t)out[1] & 0xFFu) << 8) |
+                               (((uint32_t)out[2] & 0xFFu) << 16) | ((uint32_t)out[3] << 24);
+            *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(g.C) + m * g.ldc + n) = w;
+          }
+        } else if (m < g.M) {
+          if constexpr (kOut32) {
+            int32_t* crow = static_cast<int32_t*>(g.C) + m * g.ldc;
+            if (c_vec && n + 3 < g.N) {
+              *reinterpret_cast<v4i*>(crow + n) = v4i{out[0], out[1], out[2], out[3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < g.N) crow[n + r] = out[r];
+            }
+          } else {
+            int8_t* crow = static_cast<int8_t*>(g.C) + m * g.ldc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < g.N) crow[n + r] = (int8_t)out[r];
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace qp
