@@ -88,8 +88,11 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
   }
 }
 
-// One workgroup per padded row n; thread r builds run r (32 K -> 16 bytes).
-// Byte 4w+j of a run: low nibble k=8w+j, high nibble k=8w+4+j.
+// One workgroup per padded row n; thread r builds the 32-K run r (group-
+// sized pieces of the row).  Within each 128-K block (64 bytes) byte
+// 16c + 4t + j holds k = 32t + 8c + j (low nibble) and k = 32t + 8c + 4 + j
+// (high nibble), so the 16 bytes at 16c hold the 8-K chunk c of four
+// consecutive 32-K runs: one 16-byte load feeds four MFMA K-steps.
 __global__ __launch_bounds__(256) void pack_s4_kernel(
     const int8_t* __restrict__ w, int64_t N, int64_t K, int64_t Kpad, int64_t group, int64_t sn,
     KMap km, const float* __restrict__ sw, int64_t ldsw, uint8_t* __restrict__ blob,
@@ -99,39 +102,40 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
   const bool live = n < N;
   const int64_t runs = Kpad / 32;
   const int64_t G = Kpad / group;
+  const int64_t Greal = (K + group - 1) / group;
   uint8_t* row = blob + data_off + n * (Kpad / 2);
   int bad = 0;
   for (int64_t r = threadIdx.x; r < runs; r += blockDim.x) {
-    uint32_t words[4];
+    const int64_t b = r / 4, t = r % 4;
     int32_t s = 0;
 #pragma unroll
-    for (int wq = 0; wq < 4; ++wq) {
+    for (int c = 0; c < 4; ++c) {
       uint32_t v = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        int64_t klo = r * 32 + 8 * wq + j, khi = klo + 4;
-        int32_t lo = (live && klo < K) ? w[n * sn + km.off(klo)] : 0;
-        int32_t hi = (live && khi < K) ? w[n * sn + km.off(khi)] : 0;
+        const int64_t klo = r * 32 + 8 * c + j, khi = klo + 4;
+        const int32_t lo = (live && klo < K) ? w[n * sn + km.off(klo)] : 0;
+        const int32_t hi = (live && khi < K) ? w[n * sn + km.off(khi)] : 0;
         bad |= (lo < -8) | (lo > 7) | (hi < -8) | (hi > 7);
         s += lo + hi;
         v |= ((uint32_t)(lo & 0xF) | ((uint32_t)(hi & 0xF) << 4)) << (8 * j);
       }
-      words[wq] = v;
+      *reinterpret_cast<uint32_t*>(row + b * 64 + 16 * c + 4 * t) = v;
     }
-    *reinterpret_cast<uint4*>(row + 16 * r) = make_uint4(words[0], words[1], words[2], words[3]);
     run_sum[r] = s;
   }
   if (bad) atomicOr(reinterpret_cast<int32_t*>(blob + kInvalidFlagOffset), 1);
   __syncthreads();
   float* srow = reinterpret_cast<float*>(blob + scale_off) + n * G;
-  for (int64_t g = threadIdx.x; g < G; g += blockDim.x) srow[g] = live ? sw[n * ldsw + g] : 0.0f;
+  for (int64_t g = threadIdx.x; g < G; g += blockDim.x)
+    srow[g] = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
   if (threadIdx.x == 0) {
     double acc = 0.0;
     const int64_t rpg = group / 32;
     for (int64_t g = 0; g < G; ++g) {
       int64_t gs = 0;
       for (int64_t r = g * rpg; r < (g + 1) * rpg; ++r) gs += run_sum[r];
-      double s = live ? (double)sw[n * ldsw + g] : 0.0;
+      const double s = (live && g < Greal) ? (double)sw[n * ldsw + g] : 0.0;
       acc = acc + s * (double)gs;
     }
     reinterpret_cast<float*>(blob + sum_off)[n] = live ? (float)acc : 0.0f;
@@ -299,7 +303,7 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     if ((st = check_launch("qpack_weights header"))) return st;
     size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / 32);
     hipLaunchKernelGGL(pack_s4_kernel, dim3((unsigned)g.Npad), dim3(256), lds, stream, src, v.N,
-                       v.K, g.Kpad, g.group, v.sn, v.km, w->scales, g.Kpad / g.group, blob,
+                       v.K, g.Kpad, g.group, v.sn, v.km, w->scales, ceil_div(v.K, g.group), blob,
                        g.data_off, g.scale_off, g.sum_off);
     if ((st = check_launch("qpack_weights int4"))) return st;
     g.has_zero_points = 0;

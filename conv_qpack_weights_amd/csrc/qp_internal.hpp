@@ -37,7 +37,8 @@ constexpr int64_t kHeaderBytes = 256;
 constexpr int64_t kRegionAlign = 256;
 constexpr int64_t kPadN = 64;       // Npad multiple
 constexpr int64_t kPadK8 = 64;      // int8 Kpad multiple (one MFMA K-step)
-constexpr int64_t kRunK4 = 32;      // int4: 32 nibbles = 16 bytes per run
+constexpr int64_t kRunK4 = 32;      // int4: a 32-K group run
+constexpr int64_t kBlockK4 = 128;   // int4: 128 K (64 bytes) interleaved per block
 constexpr int kInvalidFlagOffset = 108;
 
 struct alignas(16) BlobHeader {

@@ -26,15 +26,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
                                                             int64_t kfill,
                                                             float* __restrict__ row_scale,
                                                             int32_t* __restrict__ row_zp) {
-  __shared__ float red_min[256 / 64];
-  __shared__ float red_max[256 / 64];
+  __shared__ float red[2 * 4];
   const int64_t m = blockIdx.x;
   const float* xr = x + m * ldx;
   int8_t* qr = q + m * ldq;
+  const bool vec = (((uintptr_t)xr) & 15) == 0;
+  const bool dvec = (((uintptr_t)qr) & 15) == 0;
   float s;
   int32_t z;
-  row_params_block(xr, K, red_min, red_max, &s, &z);
-  quantize_row_block(xr, K, kfill, s, z, qr);
+  quantize_row_wg<256>(xr, K, kfill, vec, dvec, qr, red, &s, &z);
   if (threadIdx.x == 0) {
     row_scale[m] = s;
     row_zp[m] = z;

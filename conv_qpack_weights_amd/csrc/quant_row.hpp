@@ -1,7 +1,10 @@
-// quant_row.hpp -- the per-row dynamic quantization steps as block-level
-// device functions, used by the standalone quantizer and by kernels that
-// quantize their activation row in place.  Every caller must be compiled
-// with FP contraction off so the f32 sequence is the documented one.
+// quant_row.hpp -- the per-row dynamic quantization steps as workgroup-level
+// device functions, used by the standalone quantizer and by the A8W4 GEMV,
+// which quantizes its activation row itself.  Every caller must be compiled
+// with FP contraction off so the f32 sequence is the documented one:
+//   rmin = min(0, min x); rmax = max(0, max x); scale = (rmax - rmin) / 255
+//   (scale == 0 -> scale = 1, zp = 0); zp = clamp(rint(-128 - rmin/scale));
+//   q = clamp(rint(x/scale) + zp, -128, 127)      (IEEE division, RHE rint)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,35 +16,47 @@ namespace qp {
 __device__ __forceinline__ float qp_min(float a, float b) { return b < a ? b : a; }
 __device__ __forceinline__ float qp_max(float a, float b) { return b > a ? b : a; }
 
-// Scale and zero point of one row, computed by the whole workgroup; every
-// thread returns the same (s, z).  `red_*` are LDS scratch of one float per
-// wave.  Requires blockDim.x to be a multiple of 64 and <= 64 * 16.
-__device__ __forceinline__ void row_params_block(const float* __restrict__ xr, int64_t K,
-                                                 float* red_min, float* red_max, float* s_out,
-                                                 int32_t* z_out) {
-  float lo = 0.0f, hi = 0.0f;
-  for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
-    float v = xr[k];
-    lo = qp_min(lo, v);
-    hi = qp_max(hi, v);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = qp_min(lo, __shfl_xor(lo, off, 64));
-    hi = qp_max(hi, __shfl_xor(hi, off, 64));
-  }
-  const int wave = threadIdx.x / 64, nwaves = blockDim.x / 64;
-  if ((threadIdx.x & 63) == 0) {
-    red_min[wave] = lo;
-    red_max[wave] = hi;
-  }
-  __syncthreads();
-  lo = red_min[0];
-  hi = red_max[0];
-  for (int i = 1; i < nwaves; ++i) {
-    lo = qp_min(lo, red_min[i]);
-    hi = qp_max(hi, red_max[i]);
-  }
+// DPP row operations (16-lane rows): quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror.  After the four steps every lane of a row
+// holds the row's reduction.
+template <typename Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  0xB1, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  0x4E, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  0x141, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                  0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Wave-wide reduction in a fixed order: rows reduced by DPP, then the four
+// row results combined as ((r0 op r1) op r2) op r3; wave-uniform result.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = row16_reduce(v, op);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return op(op(op(r0, r1), r2), r3);
+}
+
+struct MinOp {
+  __device__ float operator()(float a, float b) const { return qp_min(a, b); }
+};
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return qp_max(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Scale and zero point from the row extremes (already widened to include 0).
+__device__ __forceinline__ void params_from_range(float lo, float hi, float* s_out,
+                                                  int32_t* z_out) {
   float s = (hi - lo) / 255.0f;
   int32_t z = 0;
   if (s == 0.0f) {
@@ -55,20 +70,104 @@ __device__ __forceinline__ void row_params_block(const float* __restrict__ xr, i
   *z_out = z;
 }
 
-__device__ __forceinline__ int8_t quantize_one(float x, float s, int32_t z) {
-  float r = __builtin_rintf(x / s);
+__device__ __forceinline__ uint32_t quantize_one(float x, float s, int32_t z) {
+  const float r = __builtin_rintf(x / s);
   // |x/s| <= 255 for in-row values, so the conversion is exact.
   int32_t v = (int32_t)r + z;
   v = v < -128 ? -128 : (v > 127 ? 127 : v);
-  return (int8_t)v;
+  return (uint32_t)(uint8_t)(int8_t)v;
 }
 
-// Quantizes xr[0..K) into qr and writes zeros into qr[K..kfill).
-__device__ __forceinline__ void quantize_row_block(const float* __restrict__ xr, int64_t K,
-                                                   int64_t kfill, float s, int32_t z,
-                                                   int8_t* __restrict__ qr) {
-  for (int64_t k = threadIdx.x; k < kfill; k += blockDim.x)
-    qr[k] = k < K ? quantize_one(xr[k], s, z) : (int8_t)0;
+// Workgroup quantization of one row of K floats into `dst` (LDS or global),
+// zero-filling dst[K, kfill).  Thread t owns 16 consecutive values per pass
+// (16-byte loads when `vec`: x 16-byte aligned).  Codes are written 16 bytes
+// at a time when `dst_vec` (dst 16-byte aligned), else byte by byte.  `red`
+// is LDS scratch of 2 floats per wave.  Requires blockDim.x == NT (a
+// multiple of 64).
+// kChunkMajor: dst receives the codes permuted for the A8W4 GEMV -- within
+// each 128-K block the 8-byte piece (t, c) holding k = 32t + 8c .. +8 goes to
+// offset 32c + 8t, so the four pieces one lane needs are 32 contiguous
+// bytes (requires kfill % 128 == 0 and a 16-byte aligned dst).
+template <int NT, bool kChunkMajor = false>
+__device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
+                                                int64_t kfill, bool vec, bool dst_vec,
+                                                int8_t* __restrict__ dst, float* red,
+                                                float* s_out, int32_t* z_out) {
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x;
+  float lo = 0.0f, hi = 0.0f;
+  // pass 1: extremes
+  for (int64_t k0 = (int64_t)t * 16; k0 < K; k0 += NT * 16) {
+    if (vec && k0 + 16 <= K) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+        lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
+        hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
+      }
+    } else {
+      for (int j = 0; j < 16; ++j)
+        if (k0 + j < K) {
+          const float v = x[k0 + j];
+          lo = qp_min(lo, v);
+          hi = qp_max(hi, v);
+        }
+    }
+  }
+  lo = wave_reduce(lo, MinOp{});
+  hi = wave_reduce(hi, MaxOp{});
+  const int wave = t >> 6;
+  if ((t & 63) == 0) {
+    red[wave] = lo;
+    red[NW + wave] = hi;
+  }
+  __syncthreads();
+  lo = red[0];
+  hi = red[NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    lo = qp_min(lo, red[w]);
+    hi = qp_max(hi, red[NW + w]);
+  }
+  float s;
+  int32_t z;
+  params_from_range(lo, hi, &s, &z);
+  // pass 2: codes (the second read of x hits the caches)
+  for (int64_t k0 = (int64_t)t * 16; k0 < kfill; k0 += NT * 16) {
+    uint32_t w[4];
+    if (vec && k0 + 16 <= K) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+        w[q] = quantize_one(v.x, s, z) | (quantize_one(v.y, s, z) << 8) |
+               (quantize_one(v.z, s, z) << 16) | (quantize_one(v.w, s, z) << 24);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = k0 + 4 * q + j;
+          if (k < K) acc |= quantize_one(x[k], s, z) << (8 * j);
+        }
+        w[q] = acc;
+      }
+    }
+    if constexpr (kChunkMajor) {
+      // k0 = 128b + 32t + 16p: pieces c = 2p and 2p+1 of group t
+      const int64_t b = k0 >> 7, t = (k0 >> 5) & 3, p = (k0 >> 4) & 1;
+      int8_t* base = dst + b * 128 + t * 8;
+      *reinterpret_cast<uint2*>(base + (2 * p) * 32) = make_uint2(w[0], w[1]);
+      *reinterpret_cast<uint2*>(base + (2 * p + 1) * 32) = make_uint2(w[2], w[3]);
+    } else if (dst_vec && k0 + 16 <= kfill) {
+      *reinterpret_cast<uint4*>(dst + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int j = 0; j < 16 && k0 + j < kfill; ++j) dst[k0 + j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
+    }
+  }
+  *s_out = s;
+  *z_out = z;
 }
 
 }  // namespace qp

@@ -44,10 +44,11 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.zp_off = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
     g.total_bytes = g.zp_off + round_up(4 * g.Npad, kRegionAlign);
   } else if (format == 2) {
-    QP_REQUIRE(group > 0 && group % kRunK4 == 0, QP_EUNSUPPORTED,
-               "int4 group size must be a positive multiple of 32 (got %lld)", (long long)group);
+    QP_REQUIRE(group > 0 && group % kRunK4 == 0 && (kBlockK4 % group == 0 || group % kBlockK4 == 0),
+               QP_EUNSUPPORTED, "int4 group size must be 32, 64, 128 or a multiple of 128 (got %lld)",
+               (long long)group);
     g.group = group;
-    g.Kpad = round_up(K, group);
+    g.Kpad = round_up(K, group > kBlockK4 ? group : kBlockK4);
     g.data_bytes = g.Npad * g.Kpad / 2;
     g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
     g.sum_off = g.scale_off + round_up(4 * g.Npad * (g.Kpad / group), kRegionAlign);

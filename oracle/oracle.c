@@ -475,10 +475,11 @@ int orc_a8w4_blockwise(int64_t M, int64_t N, int64_t K, int64_t group, const int
  * int8 format:  Npad = roundup(N,64), Kpad = roundup(K,64);
  *   data  [Npad][Kpad] int8, row n holds W[n, 0..K) then zeros;
  *   scale f32[Npad], colsum i32[Npad] = sum_{k<K} W[n,k], zp i32[Npad].
- * int4 format:  Npad = roundup(N,64), Kpad = roundup(K, group) (group a
- *   multiple of 32);  data [Npad][Kpad/2] bytes; within each run of 32 K
- *   (16 bytes), byte 4w+j holds k = 8w+j in its low nibble and k = 8w+4+j in
- *   its high nibble, as 4-bit two's complement; scale f32[Npad][Kpad/group];
+ * int4 format:  Npad = roundup(N,64), Kpad = roundup(K, max(group,128))
+ *   (group 32, 64, 128 or a multiple of 128); data [Npad][Kpad/2] bytes;
+ *   within each block of 128 K (64 bytes), byte 16c+4t+j (c, t, j in 0..3)
+ *   holds k = 32t+8c+j in its low nibble and k = 32t+8c+4+j in its high
+ *   nibble, as 4-bit two's complement; scale f32[Npad][Kpad/group];
  *   wsum f32[Npad] = (float) sum_g (double)sw[n,g] * sum_{k in g} W[n,k],
  *   accumulated in fp64 in increasing g.  All padding is zero.
  * ====================================================================== */
@@ -549,17 +550,21 @@ int orc_pack_s8_ref(int64_t N, int64_t K, const int8_t* Wt, int64_t w_sn, int64_
   return 0;
 }
 
+static int orc_s4_group_ok(int64_t group) {
+  return group > 0 && group % 32 == 0 && (128 % group == 0 || group % 128 == 0);
+}
+
 int64_t orc_packed_s4_bytes(int64_t N, int64_t K, int64_t group) {
-  if (group <= 0 || group % 32) return -1;
-  int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group);
+  if (!orc_s4_group_ok(group)) return -1;
+  int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group > 128 ? group : 128);
   return ORC_HDR + orc_a256(Npad * Kpad / 2) + orc_a256(4 * Npad * (Kpad / group)) +
          orc_a256(4 * Npad);
 }
 
 int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64_t w_sn,
                     int64_t w_sk, const float* sw, int64_t ldsw, uint8_t* blob) {
-  if (N <= 0 || K <= 0 || group <= 0 || group % 32) return ORC_EINVAL;
-  int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group);
+  if (N <= 0 || K <= 0 || !orc_s4_group_ok(group)) return ORC_EINVAL;
+  int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group > 128 ? group : 128);
   int64_t G = Kpad / group;
   int64_t data_bytes = Npad * Kpad / 2;
   int64_t scale_off = ORC_HDR + orc_a256(data_bytes);
@@ -571,17 +576,18 @@ int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64
     for (int64_t k = 0; k < K; ++k) {
       int8_t v = Wt[n * w_sn + k * w_sk];
       if (v < -8 || v > 7) return ORC_EINVAL;
-      int64_t run = k / 32, r = k % 32;
-      int64_t w = r / 8, j = r % 4, high = (r % 8) >= 4;
-      int64_t byte = ORC_HDR + n * (Kpad / 2) + run * 16 + 4 * w + j;
+      int64_t block = k / 128, t = (k % 128) / 32, c = (k % 32) / 8, j = k % 4;
+      int64_t high = (k % 8) >= 4;
+      int64_t byte = ORC_HDR + n * (Kpad / 2) + block * 64 + 16 * c + 4 * t + j;
       uint8_t nib = (uint8_t)(v & 0xF);
       blob[byte] |= high ? (uint8_t)(nib << 4) : nib;
     }
     double ws = 0.0;
+    int64_t Greal = orc_ceil_div(K, group);
     for (int64_t g = 0; g < G; ++g) {
       int64_t gs = 0;
       for (int64_t k = g * group; k < (g + 1) * group && k < K; ++k) gs += Wt[n * w_sn + k * w_sk];
-      float s = (g * group < K) ? sw[n * ldsw + g] : 0.0f;
+      float s = (g < Greal) ? sw[n * ldsw + g] : 0.0f;
       memcpy(blob + scale_off + 4 * (n * G + g), &s, 4);
       ws += (double)s * (double)gs;
     }

@@ -71,6 +71,9 @@ def test_header_parser_reads_the_reference_blob(qp, orc):
     blob4 = orc.pack_s4_ref(W4, np.ones((5, 4), np.float32))
     info4 = qp.qp_packed_info_from_header(blob4[:256].tobytes())
     assert (info4.format, info4.group, info4.Kpad, info4.total_bytes) == (2, 32, 128, blob4.size)
+    blob5 = orc.pack_s4_ref(rng.integers(-8, 8, (2, 200)).astype(np.int8), np.ones((2, 7), np.float32))
+    info5 = qp.qp_packed_info_from_header(blob5[:256].tobytes())
+    assert (info5.Kpad, info5.total_bytes) == (256, blob5.size)
     bad = bytearray(blob[:256].tobytes())
     bad[0] ^= 0xFF
     with pytest.raises(qp.QPackError):
@@ -87,7 +90,7 @@ def test_pack_rejects_bad_descriptors(qp):
     _expect(qp, L.qpack_weights_size(C.byref(d3), 1, 0, C.byref(nb), C.byref(al)), qp.QP_EINVAL)
     d4 = qp.qtensor(qp.QP_S4, [8, 64], [64, 1], scheme=qp.QP_BLOCKWISE, group_size=48)
     _expect(qp, L.qpack_weights_size(C.byref(d4), 1, 0, C.byref(nb), C.byref(al)),
-            qp.QP_EUNSUPPORTED, "multiple of 32")
+            qp.QP_EUNSUPPORTED, "group size")
     dz = qp.qtensor(qp.QP_S4, [8, 64], [64, 1], scheme=qp.QP_BLOCKWISE, group_size=32,
                     zero_point=3)
     _expect(qp, L.qpack_weights_size(C.byref(dz), 1, 0, C.byref(nb), C.byref(al)),

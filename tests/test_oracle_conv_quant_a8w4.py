@@ -266,7 +266,7 @@ def test_o7_s8_blob_decodes_back(orc, N, K):
     assert np.array_equal(orc.pack_s8_ref(np.ascontiguousarray(W.T).T, sc, zp), blob)
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (5, 100), (64, 4096 // 8), (130, 64)])
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 100), (64, 4096 // 8), (130, 64), (3, 300)])
 def test_o7_s4_blob_decodes_back(orc, N, K):
     rng = np.random.default_rng(20)
     W = _rand_i8(rng, (N, K), -8, 7)
@@ -274,16 +274,20 @@ def test_o7_s4_blob_decodes_back(orc, N, K):
     sw = rng.uniform(0.002, 0.02, (N, G)).astype(np.float32)
     blob = orc.pack_s4_ref(W, sw, 32)
     h = _hdr(blob)
-    assert h["format"] == 2 and h["group"] == 32 and h["Kpad"] == G * 32
-    raw = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].reshape(h["Npad"], h["Kpad"] // 32, 4, 4)
+    Kp = (K + 127) // 128 * 128
+    Gp = Kp // 32
+    assert h["format"] == 2 and h["group"] == 32 and h["Kpad"] == Kp
+    # decode with numpy axes: (row, block of 128 K, c, t, j) -> k = 128*block + 32t + 8c + [j | 4+j]
+    raw = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].reshape(h["Npad"], Kp // 128, 4, 4, 4)
     lo = (raw & 0xF).astype(np.int16)
     hi = (raw >> 4).astype(np.int16)
     lo = np.where(lo >= 8, lo - 16, lo)
     hi = np.where(hi >= 8, hi - 16, hi)
-    dec = np.concatenate([lo, hi], axis=3).reshape(h["Npad"], h["Kpad"])   # (run, w, [j | 4+j])
+    dec = np.concatenate([lo, hi], axis=4)              # (row, block, c, t, 8)
+    dec = dec.transpose(0, 1, 3, 2, 4).reshape(h["Npad"], Kp)   # -> (row, block, t, c, 8)
     assert np.array_equal(dec[:N, :K], W) and not dec[N:].any() and not dec[:, K:].any()
-    sc = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"] * G].view(np.float32).reshape(h["Npad"], G)
-    assert np.array_equal(sc[:N], sw) and not sc[N:].any()
+    sc = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"] * Gp].view(np.float32).reshape(h["Npad"], Gp)
+    assert np.array_equal(sc[:N, :G], sw) and not sc[N:].any() and not sc[:, G:].any()
     Wp = np.zeros((N, G * 32), np.int64)
     Wp[:, :K] = W
     gs = Wp.reshape(N, G, 32).sum(2)
