@@ -77,8 +77,7 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST, int MF, bool kOut32, bool kRowSum,
-          bool kHi>
+template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kHi>
 qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (int32_t)ceil_div(a.M, BM);
@@ -88,8 +87,8 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks == 0) return QP_OK;
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
-  const size_t lds = (size_t)ST * (BM + BN) * BK;
-  auto kern = qgemm_s8_kernel<BM, BN, BK, WM, WN, ST, MF, kOut32, kRowSum, kHi>;
+  const size_t lds = (size_t)SA * BM * BK;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi>;
   static bool lds_attr_set = false;  // once per instantiation; repeating it is harmless
   if (!lds_attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -97,7 +96,7 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
       QP_FAIL(QP_EHIP, "qgemm: cannot reserve %zu bytes of LDS", lds);
     lds_attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(WM * WN * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, a);
   return check_launch("qgemm_s8s8 kernel");
 }
 
@@ -106,10 +105,10 @@ qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
   const bool k128 = (a.Kpad % 128) == 0;
   const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (k128 && big_tiles >= 256)
-    return launch_cfg<256, 256, 128, 2, 4, 2, 32, kOut32, kRowSum, kHi>(a, stream);
+    return launch_cfg<256, 256, 128, 4, 4, 32, kOut32, kRowSum, kHi>(a, stream);
   if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
-    return launch_cfg<128, 128, 128, 2, 2, 2, 32, kOut32, kRowSum, kHi>(a, stream);
-  return launch_cfg<64, 64, 64, 2, 2, 3, 32, kOut32, kRowSum, kHi>(a, stream);
+    return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi>(a, stream);
+  return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi>(a, stream);
 }
 
 }  // namespace

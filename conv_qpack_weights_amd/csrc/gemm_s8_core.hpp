@@ -132,37 +132,40 @@ __device__ __forceinline__ int swz(int row) {
 
 // kShiftHi: every column's shift is >= 32 (all multipliers below 1/2, known
 // on the host from the weight scales), so the rounding runs in 32-bit pieces.
-// MF: MFMA shape, 16 (v_mfma_i32_16x16x64_i8) or 32 (v_mfma_i32_32x32x32_i8).
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, int MF, bool kOut32, bool kRowSum,
-          bool kShiftHi>
-__global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
-  constexpr int NW = WM * WN;
-  constexpr int CH = BK / 16;  // 16-byte chunks per tile row
-  constexpr int TM = BM / WM;
-  constexpr int TN = BN / WN;
+//
+// Data movement (per workgroup tile BM x BN, K in steps of BK bytes):
+//  * A (activations, row-major) goes HBM/L2 -> LDS with direct loads into an
+//    SA-deep ring (prefetch distance SA-1 tiles); every wave reads all BM
+//    rows from it.
+//  * B (the packed weights, 32x32 sub-tiles) goes straight into VGPRs in
+//    MFMA operand order, one tile ahead: each wave owns BN/NW columns, so no
+//    B byte is loaded twice and LDS only carries A.
+template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kShiftHi>
+__global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
+  constexpr int CH = BK / 16;  // 16-byte chunks per A tile row
+  constexpr int TM = BM;       // every wave covers all rows of the tile
+  constexpr int TN = BN / NW;
   constexpr int FM = TM / MF;
   constexpr int FN = TN / MF;
   constexpr int KSTEP = MF == 16 ? 64 : 32;  // K per MFMA
   constexpr int NREG = MF == 16 ? 4 : 16;    // accumulator registers per MFMA
+  constexpr int SUB = BK / KSTEP;            // MFMAs along K per tile
+  constexpr int IA = BM * CH / (64 * NW);    // A direct loads per wave per tile
+  constexpr int IB = SUB * FN;               // B fragment loads per wave per tile
+  constexpr int STAGE = BM * BK;
   typedef int accv __attribute__((ext_vector_type(NREG)));
-  constexpr int A_SLOTS = BM * CH;  // 16-byte slots per A tile
-  constexpr int B_SLOTS = BN * CH;
-  constexpr int A_INS = A_SLOTS / (64 * NW);  // DMA instructions per wave per tile
-  constexpr int B_INS = B_SLOTS / (64 * NW);
-  constexpr int IPT = A_INS + B_INS;
-  constexpr int STAGE = (BM + BN) * BK;
-  static_assert(A_SLOTS % (64 * NW) == 0 && B_SLOTS % (64 * NW) == 0, "tile/wave mismatch");
-  static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be a multiple of the MFMA");
+  static_assert(BM * CH % (64 * NW) == 0, "A tile must split evenly over the waves");
+  static_assert(TN % MF == 0 && TM % MF == 0 && BK % KSTEP == 0, "tile shape");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
-  static_assert(STAGES >= 2 && (STAGES - 2) * IPT < 64, "prefetch depth");
+  static_assert(SA >= 2 && (SA - 2) * IA + IB < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave;
 
   // ---- tile index: XCD-aware (dispatch round-robins over 8 XCDs), then
   // grouped along M so concurrent workgroups share A rows and B rows in L2.
@@ -179,50 +182,60 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
   const int64_t m0 = (int64_t)tile_m * BM;
   const int64_t n0 = (int64_t)tile_n * BN;
 
-  // ---- per-lane DMA source pointers: instruction j fills slots
+  // ---- A: per-lane direct-load sources.  Instruction j fills 16-byte slots
   // [(j*NW + wave)*64, +64); lane -> slot -> (row, swizzled chunk).
-  const int8_t* a_src[A_INS];
-  const int8_t* b_src[B_INS];
+  const int8_t* a_src[IA];
 #pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
+  for (int j = 0; j < IA; ++j) {
     const int s = (j * NW + wave) * 64 + lane;
     const int row = s / CH, c = (s % CH) ^ swz<BK>(s / CH);
     int64_t gm = m0 + row;
     gm = gm < g.M ? gm : g.M - 1;
     a_src[j] = g.A + gm * g.lda + c * 16;
   }
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int s = (j * NW + wave) * 64 + lane;
-    const int row = s / CH, c = (s % CH) ^ swz<BK>(s / CH);
-    int64_t gn = n0 + row;
-    gn = gn < g.Npad ? gn : g.Npad - 1;
-    b_src[j] = g.B + gn * g.ldb + c * 16;
-  }
-  lds_void_t* lds_base = (lds_void_t*)smem;
+  auto issue_a = [&](int kt, int stage, int j) {
+    __attribute__((address_space(3))) int8_t* sbase =
+        (__attribute__((address_space(3))) int8_t*)smem + stage * STAGE;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[j] + (int64_t)kt * BK),
+                                     (lds_void_t*)(sbase + (j * NW + wave) * 1024), 16, 0, 0);
+  };
 
-  auto issue = [&](int kt, int stage) {
-    const int64_t koff = (int64_t)kt * BK;
-    lds_void_t* sbase = (lds_void_t*)((__attribute__((address_space(3))) int8_t*)lds_base +
-                                      stage * STAGE);
+  // ---- B: fragment sources in the 32x32 sub-tile layout.  MF = 32: lane
+  // reads row lane%32, 16 bytes at K offset 16*(lane/32) of a 32x32 tile.
+  // MF = 16: 16 rows x 64 K, lane reads row lane%16, K chunk lane/16.
+  const int64_t kblocks = g.Kpad / 32;
+  const int64_t nblocks = g.Npad / 32;
+  const int8_t* b_src[FN];
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[j] + koff),
-                                       (lds_void_t*)((__attribute__((address_space(3))) int8_t*)sbase +
-                                                     (j * NW + wave) * 1024),
-                                       16, 0, 0);
+  for (int i = 0; i < FN; ++i) {
+    const int64_t r0 = n0 + wn * TN + i * MF;  // first channel of the fragment
+    int64_t nb = r0 / 32;
+    nb = nb < nblocks ? nb : nblocks - 1;
+    if constexpr (MF == 32) {
+      b_src[i] = g.B + nb * kblocks * 1024 + (lane & 31) * 32 + (lane >> 5) * 16;
+    } else {
+      const int c = lane >> 4;  // 16-byte chunk of the 64-K step
+      b_src[i] = g.B + (nb * kblocks + (c >> 1)) * 1024 + ((r0 & 31) + (lane & 15)) * 32 +
+                 (c & 1) * 16;
+    }
+  }
+  v4i breg[SUB][FN];
+  auto load_b = [&](int kt, int sub) {
+    // MF=32: K block kt*BK/32 + sub; MF=16: K blocks (kt*BK + 64*sub)/32 + {0,1}
+    const int64_t kb = (int64_t)kt * (BK / 32) + sub * (KSTEP / 32);
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(b_src[j] + koff),
-                                       (lds_void_t*)((__attribute__((address_space(3))) int8_t*)sbase +
-                                                     BM * BK + (j * NW + wave) * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < FN; ++i) breg[sub][i] = *reinterpret_cast<const v4i*>(b_src[i] + kb * 1024);
   };
 
   const int nk = (int)(g.Kpad / BK);
+  // prologue: A(0) .. A(SA-2) into the ring, B(0) into registers
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nk) issue(p, p);
+  for (int p = 0; p < SA - 1; ++p)
+    if (p < nk)
+#pragma unroll
+      for (int j = 0; j < IA; ++j) issue_a(p, p, j);
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) load_b(0, sub);
 
   // ---- per-column epilogue constants (overlaps the first loads) ----
   for (int j = tid; j < BN; j += NW * 64) {
@@ -248,50 +261,106 @@ __global__ __launch_bounds__(WM* WN * 64) void qgemm_s8_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = accv{};
 
-  // fragment lane mapping: row = lane % MF, 16-byte chunk = lane / MF
+  // fragment lane mapping of A: row = lane % MF, 16-byte chunk = lane / MF
   const int frow = lane % MF;
   const int fchunk = lane / MF;
+  v4i af[FM];
+  auto read_a = [&](const int8_t* sa, int sub, int j) {
+    const int c = sub * (KSTEP / 16) + fchunk;
+    const int row = j * MF + frow;
+    af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
+  };
+  // The barrier sits in the middle of each tile: past it, every wave has
+  // finished the previous tile (so its ring slot may be refilled) and the
+  // next tile's A has landed everywhere (so its first fragments can be read
+  // while the current tile's last K-step computes).
+  constexpr int HALF = SUB / 2 > 0 ? SUB / 2 : 1;   // K-steps before the barrier
+  constexpr int SECOND = SUB - HALF > 0 ? SUB - HALF : 1;
+  constexpr int A_PER_SUB = (IA + SECOND - 1) / SECOND;  // direct loads per later K-step
+  // Loads issued after the last direct load of tile kt+1, in steady state:
+  // the B loads that follow it, SA-3 whole iterations, and the B loads of
+  // this tile's first half.
+  constexpr int A_WAIT = FN + (SA - 3) * (IA + IB) + HALF * FN;
+  static_assert(SUB == 1 || SA >= 3, "the refill slot must differ from the two slots being read");
+  static_assert(SUB == 1 || (A_WAIT >= 0 && A_WAIT < 64), "vmcnt range");
 
-  __syncthreads();  // epilogue constants visible
-  for (int kt = 0; kt < nk; ++kt) {
-    // Tile kt has landed once at most (STAGES-2) younger tiles are in flight.
-    // The barrier is issued bare: every LDS read of the stage refilled below
-    // was consumed by an MFMA before this point, and the explicit vmcnt wait
-    // covers the direct loads, so no full memory fence is needed.
-    if (kt + STAGES - 2 < nk)
-      wait_vmcnt<(STAGES - 2) * IPT>();
-    else
-      wait_vmcnt<0>();
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const int8_t* sa = smem + (kt % STAGES) * STAGE;
-    const int8_t* sb = sa + BM * BK;
-#pragma unroll
-    for (int s = 0; s < BK / KSTEP; ++s) {
-      v4i bf[FN], af[FM];
-      const int c = s * (KSTEP / 16) + fchunk;
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * TN + i * MF + frow;
-        bf[i] = *reinterpret_cast<const v4i*>(sb + row * BK + ((c ^ swz<BK>(row)) * 16));
+  wait_vmcnt<0>();
+  __syncthreads();  // A(0) everywhere; epilogue constants visible
+
+  if constexpr (SUB == 1) {
+    // One K-step per tile (small tiles): barrier at the top of each tile.
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt > 0) {
+        wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
       }
+      const int8_t* sa = smem + (kt % SA) * STAGE;
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * TM + j * MF + frow;
-        af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
-      }
+      for (int j = 0; j < FM; ++j) read_a(sa, 0, j);
+      if (kt + SA - 1 < nk)
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
+        for (int j = 0; j < IA; ++j) issue_a(kt + SA - 1, (kt + SA - 1) % SA, j);
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+          if constexpr (MF == 16)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(breg[0][i], af[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[0][i], af[j], acc[i][j], 0, 0, 0);
+        }
+      if (kt + 1 < nk) load_b(kt + 1, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) read_a(smem, 0, j);
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool refill = kt + SA - 1 < nk;
+      const bool has_next = kt + 1 < nk;
+      const int8_t* sa = smem + (kt % SA) * STAGE;
+      const int8_t* sa_next = smem + ((kt + 1) % SA) * STAGE;
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub) {
+        if (sub == HALF) {
+          if (kt >= SA - 2 && kt + SA - 2 < nk)
+            wait_vmcnt<(A_WAIT > 0 ? A_WAIT : 0)>();
+          else
+            wait_vmcnt<0>();
+          asm volatile("s_barrier" ::: "memory");
+        }
+        if (refill && sub >= HALF) {
+          const int part = sub - HALF;
+#pragma unroll
+          for (int d = 0; d < A_PER_SUB; ++d)
+            if (part * A_PER_SUB + d < IA)
+              issue_a(kt + SA - 1, (kt + SA - 1) % SA, part * A_PER_SUB + d);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
-          if constexpr (MF == 16)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[i], af[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < FN; ++i) {
+            if constexpr (MF == 16)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
+          }
+          // af[j] is consumed: refill it with the next K-step's fragment
+          if (sub + 1 < SUB)
+            read_a(sa, sub + 1, j);
+          else if (has_next)
+            read_a(sa_next, 0, j);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // breg[sub] is consumed: fetch the same K-step of the next tile
+        if (has_next) load_b(kt + 1, sub);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
+  constexpr int WM = 1;
+  const int wm = 0;
   // ---- epilogue ----
   // 16x16 MFMA: register r of a lane is channel 4*(lane/16)+r of row lane%16.
   // 32x32 MFMA: register 4q+r is channel 8q+4*(lane/32)+r of row lane%32.

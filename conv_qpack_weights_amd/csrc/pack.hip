@@ -6,9 +6,10 @@
 // MNN "ConvInt8TiledExecutor.cpp" (reorderWeight: OIHW source with K ordered
 // tap-outer / input-channel-inner; packWeightAndQuantInfo: scales stored next
 // to the weights; _computeReorderQuantInfo: weight kernel sums precomputed).
-// The layout itself is the GPU's: one K-contiguous row per output channel, so
-// a GEMM workgroup streams a [BN x BK] tile as BN rows of BK bytes and every
-// MFMA fragment is one 16-byte LDS read.
+// The layout itself is the GPU's: int8 weights in 32x32 (channel x K)
+// sub-tiles so that each MFMA operand a GEMM wave needs is one contiguous
+// kilobyte; int4 weights in 128-K blocks whose 16-byte chunks each feed four
+// MFMA K-steps.
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -41,8 +42,11 @@ __global__ void write_header_kernel(BlobHeader h, uint8_t* blob) {
   if (t < 64) dst[t] = src[t];
 }
 
-// One workgroup per padded row n.  Writes the row's Kpad bytes, its scale,
-// zero point and colsum (sum over the real K only).
+// One workgroup per padded row n.  Writes the row's Kpad bytes into the
+// 32x32 sub-tile layout -- W[n,k] at ((n/32)*(Kpad/32) + k/32)*1024 +
+// (n%32)*32 + k%32, so a GEMM wave fetches a 32-row x 32-K MFMA operand as
+// one contiguous kilobyte -- plus its scale, zero point and colsum (sum over
+// the real K only).
 __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__ w, int64_t N,
                                                       int64_t K, int64_t Kpad, int64_t sn, KMap km,
                                                       const float* __restrict__ scales,
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
   const int t = threadIdx.x;
   const bool live = n < N;
   int32_t part = 0;
-  uint8_t* row = blob + data_off + n * Kpad;
+  uint8_t* tiles = blob + data_off + (n / 32) * (Kpad / 32) * 1024 + (n % 32) * 32;
   for (int64_t k0 = (int64_t)t * 16; k0 < Kpad; k0 += 256 * 16) {
     uint32_t words[4];
 #pragma unroll
@@ -70,7 +74,8 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
       }
       words[q] = v;
     }
-    *reinterpret_cast<uint4*>(row + k0) = make_uint4(words[0], words[1], words[2], words[3]);
+    *reinterpret_cast<uint4*>(tiles + (k0 / 32) * 1024 + (k0 % 32)) =
+        make_uint4(words[0], words[1], words[2], words[3]);
   }
   __shared__ int32_t red[256];
   red[t] = part;

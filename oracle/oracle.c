@@ -473,7 +473,8 @@ int orc_a8w4_blockwise(int64_t M, int64_t N, int64_t K, int64_t group, const int
  *   i64 N, K, Npad, Kpad, group, data_off, data_bytes, scale_off, sum_off,
  *   zp_off, total_bytes; i32 has_zero_points; zero to byte 256.
  * int8 format:  Npad = roundup(N,64), Kpad = roundup(K,64);
- *   data  [Npad][Kpad] int8, row n holds W[n, 0..K) then zeros;
+ *   data: 32x32 sub-tiles, [Npad/32][Kpad/32][32 rows][32 bytes] -- W[n,k]
+ *   at ((n/32)*(Kpad/32) + k/32)*1024 + (n%32)*32 + k%32, zero beyond N, K;
  *   scale f32[Npad], colsum i32[Npad] = sum_{k<K} W[n,k], zp i32[Npad].
  * int4 format:  Npad = roundup(N,64), Kpad = roundup(K, max(group,128))
  *   (group 32, 64, 128 or a multiple of 128); data [Npad][Kpad/2] bytes;
@@ -539,7 +540,8 @@ int orc_pack_s8_ref(int64_t N, int64_t K, const int8_t* Wt, int64_t w_sn, int64_
     int64_t cs = 0;
     for (int64_t k = 0; k < K; ++k) {
       int8_t v = Wt[n * w_sn + k * w_sk];
-      blob[ORC_HDR + n * Kpad + k] = (uint8_t)v;
+      int64_t off = ((n / 32) * (Kpad / 32) + k / 32) * 1024 + (n % 32) * 32 + k % 32;
+      blob[ORC_HDR + off] = (uint8_t)v;
       cs += v;
     }
     float sc = per_channel ? scales[n] : scales[0];

@@ -253,7 +253,10 @@ def test_o7_s8_blob_decodes_back(orc, N, K):
     assert (h["N"], h["K"]) == (N, K)
     assert h["Npad"] % 64 == 0 and h["Kpad"] % 64 == 0 and h["Npad"] >= N and h["Kpad"] >= K
     assert h["total_bytes"] == blob.size == orc.lib().orc_packed_s8_bytes(N, K)
-    data = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].view(np.int8).reshape(h["Npad"], h["Kpad"])
+    # 32x32 sub-tiles: (n block, k block, row in block, byte in block) -> [n, k]
+    data = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].view(np.int8)
+    data = data.reshape(h["Npad"] // 32, h["Kpad"] // 32, 32, 32).transpose(0, 2, 1, 3)
+    data = data.reshape(h["Npad"], h["Kpad"])
     assert np.array_equal(data[:N, :K], W)
     assert not data[N:].any() and not data[:, K:].any()
     scales = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"]].view(np.float32)
