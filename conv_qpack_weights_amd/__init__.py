@@ -85,7 +85,7 @@ SIGNATURES = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libqpack.so is not built (expected at %s); run "
-                          "`python -m conv_qpack_weights_amd.build`" % LIB_PATH)
+                          "`python conv_qpack_weights_amd/build.py`" % LIB_PATH)
     h = C.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(h, name)

@@ -1,9 +1,11 @@
 """Build ``libqpack.so`` (gfx950) in-tree with hipcc.
 
-Run as ``python -m conv_qpack_weights_amd.build``; ``__graft_entry__.build()``
-calls :func:`build`.  Every HIP source is compiled for gfx950 only, with
-packed-FP32 instruction selection disabled and FP contraction handled per
-file (the numeric kernels turn it off).
+Run as ``python conv_qpack_weights_amd/build.py`` (a plain script: importing
+the package needs the library); ``__graft_entry__.build()`` calls :func:`build`.
+Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
+selection disabled and FP contraction handled per file (the numeric kernels
+turn it off).  The link refuses undefined symbols, so a kernel whose host
+stub was not emitted fails here rather than at load time.
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ def build(verbose: bool = True, jobs: int = 4) -> str:
             list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
         out_tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
-                               "-o", out_tmp])
+                               "-o", out_tmp, "-Wl,--no-undefined", "-lamdhip64"])
         os.replace(out_tmp, LIB)
     if verbose:
         print("built", LIB)

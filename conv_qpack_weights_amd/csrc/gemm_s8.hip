@@ -133,7 +133,10 @@ static GemmPlan plan_gemm(int64_t M, int64_t K, int64_t lda, const void* A,
                           const qp_packed_info* b) {
   GemmPlan p;
   p.rowsum = b->has_zero_points != 0;
-  p.copy_a = (K != b->Kpad) || (lda % 16 != 0) || (((uintptr_t)A) % 16 != 0);
+  // The kernel addresses a 256-row A tile with 32-bit offsets from its first
+  // row, so very wide strides are compacted first as well.
+  p.copy_a = (K != b->Kpad) || (lda % 16 != 0) || (((uintptr_t)A) % 16 != 0) ||
+             (lda > (INT64_C(1) << 22));
   p.ws_a = p.copy_a ? round_up(M * b->Kpad, 256) : 0;
   p.ws_rowsum = p.rowsum ? round_up(4 * M, 256) : 0;
   p.ws_total = p.ws_a + p.ws_rowsum;

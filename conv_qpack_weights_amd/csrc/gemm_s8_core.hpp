@@ -130,6 +130,94 @@ __device__ __forceinline__ int swz(int row) {
     return ((row >> 1) ^ (row >> 3)) & 3;
 }
 
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+
+// 16 bytes per lane from base + voff + soff straight into LDS (lane i lands
+// at dst + 16*i), through a buffer resource.  The buffer form is counted by
+// the compiler as a vector-memory load only, which keeps its own waits for
+// other loads exact.  The body exists in the device pass only.
+__device__ __forceinline__ void a_dma16(const int8_t* base, lds_void_t* dst, uint32_t voff,
+                                        uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, 0x7fffffff, 0x00020000), dst,
+      16, voff, soff, 0, 0);
+#endif
+}
+
+// One K tile (BK bytes of K) of the multi-step main loop for a wave:
+// SUB MFMA K-steps over the FM x FN fragment grid.
+//  * A fragments for the next K-step are read from LDS right after the
+//    MFMAs that consume the current ones (the last K-step reads the first
+//    step of the next tile, from `sa_next`);
+//  * B fragments of the next tile are loaded into the register slot the
+//    current K-step has just consumed;
+//  * halfway through, one barrier: past it every wave has left the previous
+//    tile, whose ring slot `dst` the second half refills with direct loads,
+//    and the next tile's A has landed.
+// Every tile runs the same branch-free body.  Near the end of K the caller
+// clamps the source offsets to the last tile: the extra loads land in a
+// ring slot that is no longer read (or in registers that are not used) and
+// keep the number of loads issued per tile fixed, which is what makes the
+// constant wait count A_WAIT exact for every tile.
+template <int MF, int FM, int FN, int SUB, int BK, int IA, int NW, int SA, class AccV>
+__device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
+                                           v4i (&breg)[SUB][FN], const lds_i8* sa,
+                                           const lds_i8* sa_next, lds_i8* dst,
+                                           const int8_t* a_base, const uint32_t* a_voff,
+                                           uint32_t a_koff, const int8_t* const (&b_src)[FN],
+                                           int64_t b_koff, int frow, int fchunk, int wave) {
+  constexpr int KSTEP = MF == 16 ? 64 : 32;
+  constexpr int IB = SUB * FN;
+  constexpr int HALF = SUB / 2;                                      // K-steps before the barrier
+  constexpr int A_PER_SUB = (IA + (SUB - HALF) - 1) / (SUB - HALF);  // direct loads per later step
+  // Loads issued after the last direct load of tile kt+1: the B loads that
+  // follow it, SA-3 whole tiles, and this tile's first half.  (Before the
+  // first tiles everything has been drained, so the wait is then trivially
+  // met.)
+  constexpr int A_WAIT = FN + (SA - 3) * (IA + IB) + HALF * FN;
+  static_assert(SUB >= 2 && SA >= 3, "the refill slot must differ from the two slots being read");
+  static_assert(A_WAIT >= 0 && A_WAIT < 64, "vmcnt range");
+#pragma unroll
+  for (int sub = 0; sub < SUB; ++sub) {
+    if (sub == HALF) {
+      wait_vmcnt<A_WAIT>();
+      asm volatile("s_barrier" ::: "memory");
+    }
+    if (sub >= HALF) {
+      const int part = sub - HALF;
+#pragma unroll
+      for (int d = 0; d < A_PER_SUB; ++d) {
+        const int j = part * A_PER_SUB + d;
+        if (j < IA) a_dma16(a_base, (lds_void_t*)(dst + (j * NW + wave) * 1024), a_voff[j], a_koff);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        if constexpr (MF == 16)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
+      }
+      // af[j] is consumed: refill it with the next K-step's fragment
+      const int row = j * MF + frow;
+      const int c = sub + 1 < SUB ? (sub + 1) * (KSTEP / 16) + fchunk : fchunk;
+      const lds_i8* src = sub + 1 < SUB ? sa : sa_next;
+      af[j] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+          src + row * BK + ((c ^ swz<BK>(row)) * 16));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // breg[sub] is consumed: fetch the same K-step of the next tile
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+      breg[sub][i] = *reinterpret_cast<const v4i*>(b_src[i] + b_koff + sub * (KSTEP / 32) * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // kShiftHi: every column's shift is >= 32 (all multipliers below 1/2, known
 // on the host from the weight scales), so the rounding runs in 32-bit pieces.
 //
@@ -184,20 +272,22 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
 
   // ---- A: per-lane direct-load sources.  Instruction j fills 16-byte slots
   // [(j*NW + wave)*64, +64); lane -> slot -> (row, swizzled chunk).
-  const int8_t* a_src[IA];
+  // Offsets are relative to the tile's first row (the host keeps
+  // BM*lda + Kpad below 2^31).
+  const int8_t* const a_base = g.A + m0 * g.lda;
+  uint32_t a_voff[IA];
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int s = (j * NW + wave) * 64 + lane;
     const int row = s / CH, c = (s % CH) ^ swz<BK>(s / CH);
     int64_t gm = m0 + row;
     gm = gm < g.M ? gm : g.M - 1;
-    a_src[j] = g.A + gm * g.lda + c * 16;
+    a_voff[j] = (uint32_t)((gm - m0) * g.lda + c * 16);
   }
   auto issue_a = [&](int kt, int stage, int j) {
     __attribute__((address_space(3))) int8_t* sbase =
         (__attribute__((address_space(3))) int8_t*)smem + stage * STAGE;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(a_src[j] + (int64_t)kt * BK),
-                                     (lds_void_t*)(sbase + (j * NW + wave) * 1024), 16, 0, 0);
+    a_dma16(a_base, (lds_void_t*)(sbase + (j * NW + wave) * 1024), a_voff[j], (uint32_t)(kt * BK));
   };
 
   // ---- B: fragment sources in the 32x32 sub-tile layout.  MF = 32: lane
@@ -270,20 +360,6 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     const int row = j * MF + frow;
     af[j] = *reinterpret_cast<const v4i*>(sa + row * BK + ((c ^ swz<BK>(row)) * 16));
   };
-  // The barrier sits in the middle of each tile: past it, every wave has
-  // finished the previous tile (so its ring slot may be refilled) and the
-  // next tile's A has landed everywhere (so its first fragments can be read
-  // while the current tile's last K-step computes).
-  constexpr int HALF = SUB / 2 > 0 ? SUB / 2 : 1;   // K-steps before the barrier
-  constexpr int SECOND = SUB - HALF > 0 ? SUB - HALF : 1;
-  constexpr int A_PER_SUB = (IA + SECOND - 1) / SECOND;  // direct loads per later K-step
-  // Loads issued after the last direct load of tile kt+1, in steady state:
-  // the B loads that follow it, SA-3 whole iterations, and the B loads of
-  // this tile's first half.
-  constexpr int A_WAIT = FN + (SA - 3) * (IA + IB) + HALF * FN;
-  static_assert(SUB == 1 || SA >= 3, "the refill slot must differ from the two slots being read");
-  static_assert(SUB == 1 || (A_WAIT >= 0 && A_WAIT < 64), "vmcnt range");
-
   wait_vmcnt<0>();
   __syncthreads();  // A(0) everywhere; epilogue constants visible
 
@@ -312,51 +388,27 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
       if (kt + 1 < nk) load_b(kt + 1, 0);
     }
   } else {
+    // Settle every outstanding scalar load (kernel arguments used only by
+    // the epilogue): with one pending, the compiler cannot count LDS reads
+    // precisely across the loop back edge and waits for all of them.
+    // The first fragments are read in the loop's own order, so that the
+    // counts agree on both edges into the loop.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) read_a(smem, 0, j);
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool refill = kt + SA - 1 < nk;
-      const bool has_next = kt + 1 < nk;
-      const int8_t* sa = smem + (kt % SA) * STAGE;
-      const int8_t* sa_next = smem + ((kt + 1) % SA) * STAGE;
-#pragma unroll
-      for (int sub = 0; sub < SUB; ++sub) {
-        if (sub == HALF) {
-          if (kt >= SA - 2 && kt + SA - 2 < nk)
-            wait_vmcnt<(A_WAIT > 0 ? A_WAIT : 0)>();
-          else
-            wait_vmcnt<0>();
-          asm volatile("s_barrier" ::: "memory");
-        }
-        if (refill && sub >= HALF) {
-          const int part = sub - HALF;
-#pragma unroll
-          for (int d = 0; d < A_PER_SUB; ++d)
-            if (part * A_PER_SUB + d < IA)
-              issue_a(kt + SA - 1, (kt + SA - 1) % SA, part * A_PER_SUB + d);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-#pragma unroll
-          for (int i = 0; i < FN; ++i) {
-            if constexpr (MF == 16)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[sub][i], af[j], acc[i][j], 0, 0, 0);
-          }
-          // af[j] is consumed: refill it with the next K-step's fragment
-          if (sub + 1 < SUB)
-            read_a(sa, sub + 1, j);
-          else if (has_next)
-            read_a(sa_next, 0, j);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // breg[sub] is consumed: fetch the same K-step of the next tile
-        if (has_next) load_b(kt + 1, sub);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < FM; ++j) {
+      read_a(smem, 0, j);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    lds_i8* const ring = (lds_i8*)smem;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ka = min(kt + SA - 1, nk - 1);  // tile refilled into the free slot
+      const int kb = min(kt + 1, nk - 1);       // tile whose B goes into registers
+      gemm_ktile<MF, FM, FN, SUB, BK, IA, NW, SA>(
+          acc, af, breg, ring + (kt % SA) * STAGE, ring + ((kt + 1) % SA) * STAGE,
+          ring + ((kt + SA - 1) % SA) * STAGE, a_base, a_voff, (uint32_t)(ka * BK), b_src,
+          (int64_t)kb * (BK / 32) * 1024, frow, fchunk, wave);
+    }
+    wait_vmcnt<0>();  // the clamped refills must land before the workgroup ends
   }
 
   constexpr int WM = 1;
