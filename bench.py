@@ -45,9 +45,9 @@ def _args():
 def main():
     a = _args()
     if a.gpus != 1:
-        print("bench.py measures one GPU: --gpus %d is not supported (this build has no "
-              "multi-GPU path; see DESIGN.md for how the work would shard)" % a.gpus,
-              file=sys.stderr)
+        print("bench.py measures one GPU: --gpus %d is not supported (there is no "
+              "multi-GPU path; the work would shard along output channels with no "
+              "exchange step)" % a.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -106,8 +106,10 @@ typedef struct {
  *   scheme       qp_qscheme of the weight scales.
  *   N, K         logical output channels and reduction length.
  *   Npad, Kpad   padded extents: Npad = roundup(N, 64);
- *                Kpad = roundup(K, 64) for int8, roundup(K, group) for int4.
- *   group        int4 group size (multiple of 32); 0 for int8.
+ *                Kpad = roundup(K, 64) for int8, roundup(K, max(group, 128))
+ *                for int4.
+ *   group        int4 group size (32, 64, 128 or a multiple of 128); 0 for
+ *                int8.
  *   *_off        byte offsets of the regions inside the blob.
  *   total_bytes  blob size.
  *   has_zero_points  int8: some weight zero point is non-zero.
@@ -145,14 +147,20 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  * qpack_weights -- one-time weight pre-pack into the blob the GEMM kernels
  * read ([MNN] reorderWeight / packWeightAndQuantInfo, [TRACT] pack_tensor_view
  * and PackedI8K4::pack_view).
- * int8 blob: 256-byte header; data int8 [Npad][Kpad] (row n = channel n, K
- *   contiguous, zero-filled beyond N and K: the kernels compute on the
- *   padding, so it must hold defined values, [TRACT] pack_tensor_view);
- *   f32 scale[Npad]; int32 colsum[Npad] = sum_{k<K} w[n,k] over the real K
- *   (the zero-point correction term, [MNN] kernel sums); int32 zp[Npad].
- * int4 blob: header; data [Npad][Kpad/2] bytes -- within each run of 32 K
- *   (16 bytes) byte 4w+j holds k=8w+j in its low nibble and k=8w+4+j in its
- *   high nibble, 4-bit two's complement; f32 scale[Npad][Kpad/group];
+ * int8 blob: 256-byte header; data int8 in 32x32 sub-tiles (32 channels by
+ *   32 K, 1 KiB each, row n%32 at byte 32*(n%32), K contiguous): sub-tile
+ *   (n/32, k/32) starts at ((n/32)*(Kpad/32) + k/32)*1024, so one 64-lane
+ *   16-byte load fills one MFMA weight fragment.  Zero-filled beyond N and
+ *   K: the kernels compute on the padding, so it must hold defined values
+ *   ([TRACT] pack_tensor_view).  Then f32 scale[Npad]; int32 colsum[Npad] =
+ *   sum_{k<K} w[n,k] over the real K (the zero-point correction term,
+ *   [MNN] kernel sums); int32 zp[Npad].
+ * int4 blob: header; data [Npad][Kpad/2] bytes -- each channel's K is cut in
+ *   blocks of 128 (64 bytes); byte 16c+4t+j of a block holds k = 32t+8c+j
+ *   in its low nibble and k = 32t+8c+4+j in its high nibble (t = group of
+ *   32 inside the block, c = 16-byte chunk), 4-bit two's complement, so one
+ *   16-byte chunk carries the same 8 K of four consecutive groups;
+ *   f32 scale[Npad][Kpad/group] (zero for groups past K);
  *   f32 wsum[Npad] = sum_g sw[n,g] * sum_{k in g} w[n,k], accumulated in fp64
  *   (the weight kernel sum that folds the activation zero point,
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
