@@ -26,9 +26,14 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-fno-gpu-rdc", "-Wall", "-Wno-unused-result", "-Wno-unused-variable"]
 
 
+# Per-file code-generation options.  The A8W4 kernels rescale every MFMA
+# result on the VALU right away, so their MFMAs write VGPRs (no AGPR copy).
+EXTRA = {"a8w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def _compile(src: str, obj: str) -> None:
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     subprocess.check_call(cmd)
 
 

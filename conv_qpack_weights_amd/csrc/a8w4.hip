@@ -22,7 +22,9 @@
 // exactly (a power of two) in the epilogue.  One 16-byte load (chunk c of a
 // block) carries the same 8 K of four consecutive groups.
 #include <cstring>
+#include <type_traits>
 
+#include "dev_util.hpp"
 #include "qp_internal.hpp"
 #include "quant_row.hpp"
 
@@ -30,8 +32,6 @@
 
 namespace qp {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t nib_lo16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t nib_hi16(uint32_t w) { return w & 0xF0F0F0F0u; }
@@ -54,11 +54,14 @@ __device__ __forceinline__ float finish(float S16, float sa, int32_t za, float w
   return y;
 }
 
+// The int4 blob (group 32): channel n, 128-K block b at
+// ((n/16)*nblk + b)*1024 + (n%16)*64 bytes; its four group scales at float
+// ((n/16)*nblk + b)*64 + (n%16)*4.
 struct W4 {
-  const uint8_t* data;   // [Npad][Kpad/2]
-  const float* scale;    // [Npad][G]
+  const uint8_t* data;
+  const float* scale;
   const float* wsum;     // [Npad]
-  int64_t N, Npad, Kpad, G;
+  int64_t N, Npad, Kpad, nblk;
 };
 
 // ---- GEMV: one wave per RPW output channels, lanes split K by 16-byte chunks ----
@@ -85,7 +88,6 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   const int wave = threadIdx.x >> 6;
   const int64_t nbase = ((int64_t)blockIdx.x * NW + wave) * RPW;  // < Npad by grid sizing
   const int64_t chunks = w.Kpad / 32;
-  const int64_t rowbytes = w.Kpad / 2;
   constexpr int U = 2;  // chunks per lane per batch
 
   for (int64_t m = 0; m < M; ++m) {
@@ -104,9 +106,12 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
         const int64_t hh = live ? h : chunks - 1;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
-          wv[u][i] = *reinterpret_cast<const uint4*>(w.data + (nbase + i) * rowbytes + hh * 16);
+          const int64_t n = nbase + i;
+          const int64_t tb = (n >> 4) * w.nblk + (hh >> 2);  // tile-block
+          wv[u][i] = *reinterpret_cast<const uint4*>(w.data + tb * 1024 + (n & 15) * 64 +
+                                                     (hh & 3) * 16);
           const float4 s4 =
-              *reinterpret_cast<const float4*>(w.scale + (nbase + i) * w.G + (hh >> 2) * 4);
+              *reinterpret_cast<const float4*>(w.scale + tb * 64 + (n & 15) * 4);
           sv[u][i] = live ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
@@ -165,15 +170,29 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 }
 
 // ---- GEMM: MFMA 16x16x32 per 32-K group, f32 rescale per group ----------
-// A workgroup owns 16 output channels and FM*16 rows of M; its 4 waves split
-// the 128-K blocks of K in four contiguous ranges and their f32 partial sums
-// are added in wave order through LDS.  The MFMA is issued as (weights,
-// activations), so a lane holds channels 4*(lane/16)+i of row lane%16.  Lane
-// (row lane%16, c = lane/16) loads chunk c of a block: the 8-K piece c of
-// four groups, each unpacked to an 8-byte MFMA operand; the activation
-// operand of group t is qa[m][128b + 32t + 8c ..+8].  Loads for the next
-// block are issued before the current block is computed.
-template <int FM>
+// A wave computes FM x FN tiles of 16 rows x 16 channels.  The MFMA is
+// issued as (activations, weights), so lane l holds rows 4*(l/16)+i of
+// channel l%16: one f32 scale per lane, group and channel tile.  Lane
+// (channel l%16, c = l/16) loads chunk c of its tile's 128-K block (the 8-K
+// piece c of four groups, each unpacked to an 8-byte operand); a tile's
+// block is 1 KiB in one piece and its four group scales 256 bytes, so each
+// of these loads is one contiguous, fully used span.
+// The 4 waves of a workgroup are RW row groups x CW channel groups x KS
+// contiguous K ranges.  The workgroup's activation rows go through an
+// R-stage LDS ring filled with direct (buffer ... lds) loads of whole 128-byte
+// row pieces -- shared by the CW channel groups, and not competing with the
+// weight stream for L1 -- stored with chunk p of row r at chunk position
+// p ^ ((r >> 1) & 7) so that the 16-byte fragment reads are conflict-free.
+// With kPerm the activations were written permuted inside each 128-K block
+// (piece (t, c) at 32c + 8t) and a lane's four operands are 32 contiguous
+// bytes; otherwise they are four 8-byte pieces.  One barrier per block: past
+// it every wave has left the previous block (its ring stage may be
+// refilled) and this block's rows have landed.  Weights and scales of the
+// next P blocks are in registers in flight; a block's MFMAs are issued
+// before their results are rescaled, two group slots at a time, into two
+// f32 chains (even and odd slots) per output.  K-range partial sums are
+// added in wave order through LDS.
+template <int FM, int FN, int RW, int CW, int KS, bool kPerm>
 __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict__ qa,
                                                         int64_t lda, const float* __restrict__ sa_g,
                                                         const int32_t* __restrict__ za_g,
@@ -181,94 +200,233 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
                                                         const float* __restrict__ bias, float lo,
                                                         float hi, float* __restrict__ Y,
                                                         int64_t ldy) {
-  __shared__ float red[3][FM][4][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t mbase = (int64_t)blockIdx.y * 16 * FM;
+  static_assert(RW * CW * KS == 4, "four waves");
+  constexpr int P = FM * FN >= 4 ? 3 : 5;   // weight prefetch depth in blocks
+  constexpr int R = 4;                      // activation ring stages
+  constexpr int MT = 16 * FM * RW;          // rows per workgroup
+  constexpr int SLOTS = KS * MT * 8;        // 16-byte pieces per stage
+  constexpr int ND = SLOTS / 256;           // direct loads per thread per stage
+  constexpr int STAGE = SLOTS * 16;         // bytes per stage
+  static_assert(SLOTS % 256 == 0, "a stage must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) int8_t ring[R * STAGE];
+  __shared__ float red[KS > 1 ? (KS - 1) * RW * CW : 1][FM][FN][4][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = wave % KS;
+  const int cw = (wave / KS) % CW;
+  const int rw = wave / (KS * CW);
+  const int slot = rw * CW + cw;
   const int c = lane >> 4;
-  const int64_t rowbytes = w.Kpad / 2;
-  const int8_t* wsrc = reinterpret_cast<const int8_t*>(w.data) + (n0 + (lane & 15)) * rowbytes + 16 * c;
-  const int8_t* arow[FM];
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int64_t m = mbase + f * 16 + (lane & 15);
-    arow[f] = qa + (m < M ? m : M - 1) * lda + 8 * c;
-  }
-  const float* srow = w.scale + (n0 + 4 * c) * w.G;  // + i*G for channel 4c+i
+  const int64_t n0 = ((int64_t)blockIdx.x * CW + cw) * 16 * FN;  // n0 + 16*FN <= Npad
+  const int64_t mw = (int64_t)blockIdx.y * MT;                    // workgroup's first row
   const int64_t nblocks = w.Kpad / 128;
-  const int64_t bpw = (nblocks + 3) / 4;
-  const int64_t b_begin = wave * bpw;
-  const int64_t b_end = b_begin + bpw < nblocks ? b_begin + bpw : nblocks;
+  const int64_t bpw = (nblocks + KS - 1) / KS;  // blocks per K range
+  // every K range runs bpw steps; steps past its end are clamped to its last
+  // block and contribute with zero scales
+  auto range_block = [&](int r, int64_t j) {
+    const int64_t b_begin = r * bpw;
+    int64_t last = (b_begin + bpw < nblocks ? b_begin + bpw : nblocks) - 1;
+    if (last < b_begin) last = nblocks - 1;  // empty range: park on a real block
+    const int64_t b = b_begin + j;
+    return b < last ? b : last;
+  };
+  const int64_t my_end = (ks * bpw + bpw < nblocks ? ks * bpw + bpw : nblocks);
 
-  float acc[FM][4];
+  // ---- weight/scale sources (tile-contiguous blob) ----
+  const int8_t* wsrc[FN];
+  const float* ssrc[FN];
+#pragma unroll
+  for (int q = 0; q < FN; ++q) {
+    const int64_t n = n0 + q * 16 + (lane & 15);
+    wsrc[q] = reinterpret_cast<const int8_t*>(w.data) + (n >> 4) * w.nblk * 1024 +
+              (lane & 15) * 64 + 16 * c;
+    ssrc[q] = w.scale + (n >> 4) * w.nblk * 64 + (lane & 15) * 4;
+  }
+
+  // ---- activation direct loads: thread slot s = tid + 256*i of a stage ->
+  // (K range, row, chunk position); the global chunk is position ^ swizzle.
+  const int8_t* const a_base = qa + mw * lda;
+  uint32_t a_voff[ND];
+  int a_rng[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    const int s = tid + 256 * i;
+    const int r = (s >> 3) % MT;
+    a_rng[i] = (32 * i + 8 * wave) / MT;  // == (s >> 3) / MT: a wave's 8 rows share it
+    const int p = (s & 7) ^ ((r >> 1) & 7);
+    int64_t m = mw + r;
+    m = m < M ? m : M - 1;
+    a_voff[i] = (uint32_t)((m - mw) * lda + 16 * p);
+  }
+  auto issue_stage = [&](int64_t j) {
+    lds_i8* st = (lds_i8*)ring + (int)(j % R) * STAGE;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int64_t b = range_block(a_rng[i], j);
+      dma16_to_lds(a_base, (lds_void_t*)(st + (256 * i + 64 * wave) * 16), a_voff[i],
+                   (uint32_t)(b * 128));
+    }
+  };
+
+  // ---- accumulators ----
+  float acc[2][FM][FN][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int q = 0; q < FN; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][f][q][i] = 0.0f;
+
+  uint4 wr[P][FN];
+  float4 sr[P][FN];
+  auto load_w = [&](int u, int64_t b) {
+#pragma unroll
+    for (int q = 0; q < FN; ++q) {
+      wr[u][q] = *reinterpret_cast<const uint4*>(wsrc[q] + b * 1024);
+      sr[u][q] = *reinterpret_cast<const float4*>(ssrc[q] + 64 * b);
+    }
+  };
+
+  // one block: activation operands from the stage, MFMAs, refill, rescale
+  auto step = [&](int u, int64_t j) {
+    const lds_i8* st = (const lds_i8*)ring + (int)(j % R) * STAGE + ks * MT * 128;
+    uint2 ca[FM][4];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int r = rw * 16 * FM + f * 16 + (lane & 15);
+      const lds_i8* rowp = st + r * 128;
+      const int sw = (r >> 1) & 7;
+      if constexpr (kPerm) {
+        const u32x4 p0 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            rowp + 16 * ((2 * c) ^ sw));
+        const u32x4 p1 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            rowp + 16 * ((2 * c + 1) ^ sw));
+        ca[f][0] = make_uint2(p0.x, p0.y);
+        ca[f][1] = make_uint2(p0.z, p0.w);
+        ca[f][2] = make_uint2(p1.x, p1.y);
+        ca[f][3] = make_uint2(p1.z, p1.w);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {  // bytes 32t + 8c: chunk 2t + c/2, half c%2
+          const u32x2 p = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+              rowp + 16 * ((2 * t + (c >> 1)) ^ sw) + 8 * (c & 1));
+          ca[f][t] = make_uint2(p.x, p.y);
+        }
+      }
+    }
+    uint4 cw4[FN];
+    float4 cs[FN];
+    const bool live = ks * bpw + j < my_end;
+#pragma unroll
+    for (int q = 0; q < FN; ++q) {
+      cw4[q] = wr[u][q];
+      cs[q] = live ? sr[u][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    load_w(u, range_block(ks, j + P));
+#pragma unroll
+    for (int t2 = 0; t2 < 4; t2 += 2) {
+      v4i d[2][FM][FN];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int q = 0; q < FN; ++q) {
+          const uint32_t wd = h == 0 ? (t2 == 0 ? cw4[q].x : cw4[q].z)
+                                     : (t2 == 0 ? cw4[q].y : cw4[q].w);
+          const long bop = (long)(((uint64_t)nib_hi16(wd) << 32) | nib_lo16(wd));
+#pragma unroll
+          for (int f = 0; f < FM; ++f) {
+            const long aop = (long)(((uint64_t)ca[f][t2 + h].y << 32) | ca[f][t2 + h].x);
+            d[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < FN; ++q) {
+          const float sc = h == 0 ? (t2 == 0 ? cs[q].x : cs[q].z) : (t2 == 0 ? cs[q].y : cs[q].w);
+#pragma unroll
+          for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[h][f][q][i] = __builtin_fmaf(sc, (float)d[h][f][q][i], acc[h][f][q][i]);
+        }
+    }
+  };
+
+  // ---- prologue: stages 0..R-2 and weights of blocks 0..P-1, all drained ----
+#pragma unroll
+  for (int j = 0; j < R - 1; ++j) issue_stage(j);
+#pragma unroll
+  for (int u = 0; u < P; ++u) load_w(u, range_block(ks, u));
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): settle the scalar loads too
+
+  // Loads issued after stage j+1's direct loads, in the steady state: the
+  // weights refilled by step j+2-R, and R-2 whole steps (direct loads and a
+  // weight refill each).  Earlier stages were drained in the prologue.
+  constexpr int A_WAIT = 2 * FN + (R - 2) * (ND + 2 * FN);
+  static_assert(A_WAIT < 64, "vmcnt range");
+  // The step loop is unrolled by P so the weight ring index is static.
+  for (int64_t j0 = 0; j0 < bpw; j0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int64_t j = j0 + u;
+      // (past the last step the body still runs, with zero scales, so that
+      // every iteration issues the same loads)
+      wait_vmcnt<A_WAIT>();
+      asm volatile("s_barrier" ::: "memory");
+      issue_stage(j + R - 1);
+      step(u, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<0>();  // the clamped direct loads must land before the workgroup ends
+
+  float out[FM][FN][4];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[f][i] = 0.0f;
-
-  uint4 wd;
-  float4 sc[4];
-  uint2 av[FM][4];
-  auto load = [&](int64_t b) {
-    wd = *reinterpret_cast<const uint4*>(wsrc + b * 64);
+    for (int q = 0; q < FN; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = *reinterpret_cast<const float4*>(srow + i * w.G + 4 * b);
+      for (int i = 0; i < 4; ++i) out[f][q][i] = acc[0][f][q][i] + acc[1][f][q][i];
+  if constexpr (KS > 1) {
+    if (ks > 0) {
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
+      for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        av[f][t] = *reinterpret_cast<const uint2*>(arow[f] + b * 128 + 32 * t);
-  };
-  if (b_begin < b_end) load(b_begin);
-  for (int64_t b = b_begin; b < b_end; ++b) {
-    const uint4 cw = wd;
-    float4 cs[4];
+        for (int q = 0; q < FN; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cs[i] = sc[i];
-    uint2 ca[FM][4];
+          for (int i = 0; i < 4; ++i) red[slot * (KS - 1) + ks - 1][f][q][i][lane] = out[f][q][i];
+    }
+    __syncthreads();
+    if (ks != 0) return;
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) ca[f][t] = av[f][t];
-    if (b + 1 < b_end) load(b + 1);
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+      for (int q = 0; q < FN; ++q)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const long bop = (long)(((uint64_t)nib_hi16(words[t]) << 32) | nib_lo16(words[t]));
-      const float s_t[4] = {t == 0 ? cs[0].x : t == 1 ? cs[0].y : t == 2 ? cs[0].z : cs[0].w,
-                            t == 0 ? cs[1].x : t == 1 ? cs[1].y : t == 2 ? cs[1].z : cs[1].w,
-                            t == 0 ? cs[2].x : t == 1 ? cs[2].y : t == 2 ? cs[2].z : cs[2].w,
-                            t == 0 ? cs[3].x : t == 1 ? cs[3].y : t == 2 ? cs[3].z : cs[3].w};
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const long aop = (long)(((uint64_t)ca[f][t].y << 32) | ca[f][t].x);
-        const v4i d = __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, aop, v4i{0, 0, 0, 0}, 0, 0, 0);
+          for (int r = 0; r < KS - 1; ++r)
+            out[f][q][i] = out[f][q][i] + red[slot * (KS - 1) + r][f][q][i][lane];
+  }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[f][i] = acc[f][i] + s_t[i] * (float)d[i];
+  for (int q = 0; q < FN; ++q) {
+    const int64_t n = n0 + q * 16 + (lane & 15);
+    if (n >= w.N) continue;
+    const float ws = w.wsum[n];
+    const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mw + rw * 16 * FM + f * 16 + 4 * c + i;
+        if (m < M) Y[m * ldy + n] = finish(out[f][q][i], sa_g[m], za_g[m], ws, bn, lo, hi);
       }
-    }
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave - 1][f][i][lane] = acc[f][i];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int64_t m = mbase + f * 16 + (lane & 15);
-    if (m >= M) continue;
-    const float sa = sa_g[m];
-    const int32_t za = za_g[m];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float S = ((acc[f][i] + red[0][f][i][lane]) + red[1][f][i][lane]) + red[2][f][i][lane];
-      const int64_t n = n0 + 4 * c + i;
-      if (n < w.N) Y[m * ldy + n] = finish(S, sa, za, w.wsum[n], bias ? bias[n] : 0.0f, lo, hi);
-    }
   }
 }
 
@@ -276,7 +434,7 @@ W4 w4_of(const qp_packed_info* b, const void* blob) {
   const uint8_t* p = static_cast<const uint8_t*>(blob);
   return W4{p + b->data_off, reinterpret_cast<const float*>(p + b->scale_off),
             reinterpret_cast<const float*>(p + b->sum_off), b->N, b->Npad, b->Kpad,
-            b->Kpad / b->group};
+            b->Kpad / 128};
 }
 
 qp_status validate_w4(const qp_packed_info* b, int64_t K) {
@@ -313,23 +471,38 @@ qp_status launch_gemv(const float* X, int64_t K, const int8_t* qa, int64_t lda,
   return launch_gemv_cfg<512, 2>(X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, fused, stream);
 }
 
-qp_status launch_gemm(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
-                      int64_t M, const W4& w, const float* bias, float lo, float hi, float* Y,
-                      int64_t ldy, hipStream_t stream) {
-  const unsigned bx = (unsigned)ceil_div(w.N, 16);
-  if (M <= 16) {
-    hipLaunchKernelGGL(a8w4_gemm_kernel<1>, dim3(bx, 1), dim3(256), 0, stream, qa, lda, sa, za, M,
-                       w, bias, lo, hi, Y, ldy);
-  } else if (M <= 64) {
-    hipLaunchKernelGGL(a8w4_gemm_kernel<4>, dim3(bx, 1), dim3(256), 0, stream, qa, lda, sa, za, M,
-                       w, bias, lo, hi, Y, ldy);
-  } else {
-    const unsigned by = (unsigned)ceil_div(M, 128);
-    hipLaunchKernelGGL(a8w4_gemm_kernel<8>, dim3(bx, by), dim3(256), 0, stream, qa, lda, sa, za, M,
-                       w, bias, lo, hi, Y, ldy);
-  }
+template <int FM, int FN, int RW, int CW, int KS>
+qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float* sa,
+                          const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
+                          float hi, float* Y, int64_t ldy, hipStream_t stream) {
+  static_assert(64 % (16 * FN * CW) == 0, "channel tiles must tile the 64-channel padding");
+  const unsigned bx = (unsigned)ceil_div(w.N, 16 * FN * CW);
+  const int64_t by = ceil_div(M, 16 * FM * RW);
+  QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w4: M too large");
+  if (perm)
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true>), dim3(bx, (unsigned)by),
+                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  else
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false>), dim3(bx, (unsigned)by),
+                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w4 gemm");
 }
+
+// perm: the activations are permuted inside each 128-K block (as written by
+// the fused quantization); otherwise plain row-major.
+qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
+                      const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
+                      float hi, float* Y, int64_t ldy, hipStream_t stream) {
+  // <FM, FN, RW, CW, KS>: rows per workgroup 16*FM*RW, channels 16*FN*CW.
+  // Small M splits K over the waves (enough waves stream the weights); larger
+  // M shares each staged activation row among four channel groups.
+  if (M <= 16)
+    return launch_gemm_cfg<1, 1, 1, 1, 4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
+                                          stream);
+  if (M <= 32)
+    return launch_gemm_cfg<2, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
+                                          stream);
+  return launch_gemm_cfg<4, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, stream);}
 
 }  // namespace
 }  // namespace qp
@@ -369,9 +542,9 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32(const float* X, int64_t M, int64_t
   int8_t* qa = reinterpret_cast<int8_t*>(p);
   float* sa = reinterpret_cast<float*>(p + round_up(M * w->Kpad, 256));
   int32_t* za = reinterpret_cast<int32_t*>(sa + M);
-  st = launch_quantize_rows(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, stream);
+  st = launch_quantize_rows(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, true, stream);
   if (st) return st;
-  return launch_gemm(qa, w->Kpad, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
+  return launch_gemm(qa, w->Kpad, true, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
 }
 
 extern "C" qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_t lda,
@@ -389,9 +562,10 @@ extern "C" qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_
   if (M == 0) return QP_OK;
   QP_REQUIRE(qa && sa && za && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
   QP_REQUIRE(((uintptr_t)qa % 16) == 0, QP_EALIGN, "a8w4: qa must be 16-byte aligned");
+  QP_REQUIRE(lda <= (INT64_C(1) << 24), QP_EUNSUPPORTED, "a8w4: lda above 2^24 bytes");
   const W4 wv = w4_of(w, packedW_dev);
   if (M <= 4)
     return launch_gemv(nullptr, w->K, qa, lda, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy,
                        false, stream);
-  return launch_gemm(qa, lda, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
+  return launch_gemm(qa, lda, false, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
 }

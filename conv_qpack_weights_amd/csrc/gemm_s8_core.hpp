@@ -17,11 +17,9 @@
 
 #include <cstdint>
 
-namespace qp {
+#include "dev_util.hpp"
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+namespace qp {
 
 struct GemmArgs {
   const int8_t* A;
@@ -43,13 +41,6 @@ struct GemmArgs {
   int32_t xcd_remap; // 1: give each XCD a contiguous range of the raster order
 };
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
-// [15:14], expcnt[6:4], lgkmcnt[11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | 0x70 | 0xF00);
-}
 
 // M_n = sA*sB/s_out in fp64; M_n = f*2^e, f in [0.5,1); m0 = rint(f*2^31),
 // 2^31 -> 2^30 with e+1; shift = 31 - e.
@@ -130,20 +121,6 @@ __device__ __forceinline__ int swz(int row) {
     return ((row >> 1) ^ (row >> 3)) & 3;
 }
 
-typedef __attribute__((address_space(3))) int8_t lds_i8;
-
-// 16 bytes per lane from base + voff + soff straight into LDS (lane i lands
-// at dst + 16*i), through a buffer resource.  The buffer form is counted by
-// the compiler as a vector-memory load only, which keeps its own waits for
-// other loads exact.  The body exists in the device pass only.
-__device__ __forceinline__ void a_dma16(const int8_t* base, lds_void_t* dst, uint32_t voff,
-                                        uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), 0, 0x7fffffff, 0x00020000), dst,
-      16, voff, soff, 0, 0);
-#endif
-}
 
 // One K tile (BK bytes of K) of the multi-step main loop for a wave:
 // SUB MFMA K-steps over the FM x FN fragment grid.
@@ -189,7 +166,7 @@ __device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
 #pragma unroll
       for (int d = 0; d < A_PER_SUB; ++d) {
         const int j = part * A_PER_SUB + d;
-        if (j < IA) a_dma16(a_base, (lds_void_t*)(dst + (j * NW + wave) * 1024), a_voff[j], a_koff);
+        if (j < IA) dma16_to_lds(a_base, (lds_void_t*)(dst + (j * NW + wave) * 1024), a_voff[j], a_koff);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -287,7 +264,7 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   auto issue_a = [&](int kt, int stage, int j) {
     __attribute__((address_space(3))) int8_t* sbase =
         (__attribute__((address_space(3))) int8_t*)smem + stage * STAGE;
-    a_dma16(a_base, (lds_void_t*)(sbase + (j * NW + wave) * 1024), a_voff[j], (uint32_t)(kt * BK));
+    dma16_to_lds(a_base, (lds_void_t*)(sbase + (j * NW + wave) * 1024), a_voff[j], (uint32_t)(kt * BK));
   };
 
   // ---- B: fragment sources in the 32x32 sub-tile layout.  MF = 32: lane

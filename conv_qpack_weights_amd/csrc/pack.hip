@@ -97,7 +97,10 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
 // sized pieces of the row).  Within each 128-K block (64 bytes) byte
 // 16c + 4t + j holds k = 32t + 8c + j (low nibble) and k = 32t + 8c + 4 + j
 // (high nibble), so the 16 bytes at 16c hold the 8-K chunk c of four
-// consecutive 32-K runs: one 16-byte load feeds four MFMA K-steps.
+// consecutive 32-K runs: one 16-byte load feeds four MFMA K-steps.  The 16
+// channels of a tile store each block side by side (1 KiB per tile and
+// block), and their scales likewise in quads of four groups (256 bytes), so
+// one wave reads a tile's block, or its scales, as one contiguous piece.
 __global__ __launch_bounds__(256) void pack_s4_kernel(
     const int8_t* __restrict__ w, int64_t N, int64_t K, int64_t Kpad, int64_t group, int64_t sn,
     KMap km, const float* __restrict__ sw, int64_t ldsw, uint8_t* __restrict__ blob,
@@ -107,8 +110,10 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
   const bool live = n < N;
   const int64_t runs = Kpad / 32;
   const int64_t G = Kpad / group;
+  const int64_t Gq = (G + 3) / 4;
   const int64_t Greal = (K + group - 1) / group;
-  uint8_t* row = blob + data_off + n * (Kpad / 2);
+  const int64_t nblk = Kpad / 128;
+  uint8_t* row = blob + data_off + (n / 16) * nblk * 1024 + (n % 16) * 64;  // + block * 1024
   int bad = 0;
   for (int64_t r = threadIdx.x; r < runs; r += blockDim.x) {
     const int64_t b = r / 4, t = r % 4;
@@ -125,15 +130,15 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
         s += lo + hi;
         v |= ((uint32_t)(lo & 0xF) | ((uint32_t)(hi & 0xF) << 4)) << (8 * j);
       }
-      *reinterpret_cast<uint32_t*>(row + b * 64 + 16 * c + 4 * t) = v;
+      *reinterpret_cast<uint32_t*>(row + b * 1024 + 16 * c + 4 * t) = v;
     }
     run_sum[r] = s;
   }
   if (bad) atomicOr(reinterpret_cast<int32_t*>(blob + kInvalidFlagOffset), 1);
   __syncthreads();
-  float* srow = reinterpret_cast<float*>(blob + scale_off) + n * G;
-  for (int64_t g = threadIdx.x; g < G; g += blockDim.x)
-    srow[g] = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
+  float* srow = reinterpret_cast<float*>(blob + scale_off) + (n / 16) * Gq * 64 + (n % 16) * 4;
+  for (int64_t g = threadIdx.x; g < 4 * Gq; g += blockDim.x)
+    srow[(g / 4) * 64 + g % 4] = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
   if (threadIdx.x == 0) {
     double acc = 0.0;
     const int64_t rpg = group / 32;

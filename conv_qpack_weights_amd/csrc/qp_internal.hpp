@@ -60,9 +60,11 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
                         qp_packed_info* info);
 
 // ---- entry points shared between translation units ------------------------
+// perm: write each row permuted inside 128-K blocks (the A8W4 GEMM operand
+// order; needs kfill % 128 == 0 and 16-byte aligned rows).
 qp_status launch_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, int64_t kfill, float* row_scale, int32_t* row_zp,
-                               hipStream_t stream);
+                               bool perm, hipStream_t stream);
 qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
                         int32_t pt, int32_t pl, int32_t pb, int32_t pr, int64_t* OH, int64_t* OW);
 qp_status launch_im2col(const int8_t* X, int64_t NB, int64_t H, int64_t W, int64_t C,

@@ -19,7 +19,8 @@
 namespace qp {
 namespace {
 
-// One workgroup per row.
+// One workgroup per row.  kPerm writes the A8W4 operand order.
+template <bool kPerm>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restrict__ x,
                                                             int64_t K, int64_t ldx,
                                                             int8_t* __restrict__ q, int64_t ldq,
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
   const bool dvec = (((uintptr_t)qr) & 15) == 0;
   float s;
   int32_t z;
-  quantize_row_wg<256>(xr, K, kfill, vec, dvec, qr, red, &s, &z);
+  quantize_row_wg<256, kPerm>(xr, K, kfill, vec, dvec, qr, red, &s, &z);
   if (threadIdx.x == 0) {
     row_scale[m] = s;
     row_zp[m] = z;
@@ -45,10 +46,14 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
 
 qp_status launch_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, int64_t kfill, float* row_scale, int32_t* row_zp,
-                               hipStream_t stream) {
+                               bool perm, hipStream_t stream) {
   if (M == 0) return QP_OK;
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)M), dim3(256), 0, stream, x, K, ldx, q,
-                     ldq, kfill, row_scale, row_zp);
+  if (perm)
+    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3((unsigned)M), dim3(256), 0, stream, x, K,
+                       ldx, q, ldq, kfill, row_scale, row_zp);
+  else
+    hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3((unsigned)M), dim3(256), 0, stream, x, K,
+                       ldx, q, ldq, kfill, row_scale, row_zp);
   return check_launch("qquantize_rows_s8");
 }
 
@@ -64,5 +69,5 @@ extern "C" qp_status qquantize_rows_s8(const float* x, int64_t M, int64_t K, int
   QP_REQUIRE(ldx >= K && ldq >= K, QP_EINVAL, "qquantize_rows_s8: ldx/ldq smaller than K");
   if (M == 0) return QP_OK;
   QP_REQUIRE(x && q && row_scale && row_zp, QP_EINVAL, "qquantize_rows_s8: null pointer");
-  return launch_quantize_rows(x, M, K, ldx, q, ldq, K, row_scale, row_zp, stream);
+  return launch_quantize_rows(x, M, K, ldx, q, ldq, K, row_scale, row_zp, false, stream);
 }

@@ -96,12 +96,16 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
   constexpr int NW = NT / 64;
   const int t = threadIdx.x;
   float lo = 0.0f, hi = 0.0f;
-  // pass 1: extremes
+  // pass 1: extremes; a thread's first 16 values stay in registers for pass
+  // 2 (rows of up to 16*NT values are read once)
+  float4 first[4];
+  const bool keep = vec && (int64_t)t * 16 + 16 <= K;
   for (int64_t k0 = (int64_t)t * 16; k0 < K; k0 += NT * 16) {
     if (vec && k0 + 16 <= K) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+        if (k0 == (int64_t)t * 16) first[q] = v;
         lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
         hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
       }
@@ -132,13 +136,15 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
   float s;
   int32_t z;
   params_from_range(lo, hi, &s, &z);
-  // pass 2: codes (the second read of x hits the caches)
+  // pass 2: codes (beyond the first 16 per thread, x is read again)
   for (int64_t k0 = (int64_t)t * 16; k0 < kfill; k0 += NT * 16) {
     uint32_t w[4];
     if (vec && k0 + 16 <= K) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+        const float4 v = (keep && k0 == (int64_t)t * 16)
+                             ? first[q]
+                             : *reinterpret_cast<const float4*>(x + k0 + 4 * q);
         w[q] = quantize_one(v.x, s, z) | (quantize_one(v.y, s, z) << 8) |
                (quantize_one(v.z, s, z) << 16) | (quantize_one(v.w, s, z) << 24);
       }

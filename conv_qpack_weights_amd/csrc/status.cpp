@@ -51,7 +51,8 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.Kpad = round_up(K, group > kBlockK4 ? group : kBlockK4);
     g.data_bytes = g.Npad * g.Kpad / 2;
     g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
-    g.sum_off = g.scale_off + round_up(4 * g.Npad * (g.Kpad / group), kRegionAlign);
+    // scales in quads of 4 groups: f32 [Npad/16][ceil(G/4)][16][4]
+    g.sum_off = g.scale_off + round_up(16 * g.Npad * ceil_div(g.Kpad / group, 4), kRegionAlign);
     g.zp_off = 0;
     g.total_bytes = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
   } else {

@@ -477,10 +477,14 @@ int orc_a8w4_blockwise(int64_t M, int64_t N, int64_t K, int64_t group, const int
  *   at ((n/32)*(Kpad/32) + k/32)*1024 + (n%32)*32 + k%32, zero beyond N, K;
  *   scale f32[Npad], colsum i32[Npad] = sum_{k<K} W[n,k], zp i32[Npad].
  * int4 format:  Npad = roundup(N,64), Kpad = roundup(K, max(group,128))
- *   (group 32, 64, 128 or a multiple of 128); data [Npad][Kpad/2] bytes;
- *   within each block of 128 K (64 bytes), byte 16c+4t+j (c, t, j in 0..3)
- *   holds k = 32t+8c+j in its low nibble and k = 32t+8c+4+j in its high
- *   nibble, as 4-bit two's complement; scale f32[Npad][Kpad/group];
+ *   (group 32, 64, 128 or a multiple of 128).  Each channel's K is cut in
+ *   blocks of 128 (64 bytes); the 16 channels of a tile n/16 store block b
+ *   next to each other: channel n, block b at ((n/16)*(Kpad/128) + b)*1024
+ *   + (n%16)*64.  Within a block, byte 16c+4t+j (c, t, j in 0..3) holds
+ *   k = 32t+8c+j in its low nibble and k = 32t+8c+4+j in its high nibble,
+ *   as 4-bit two's complement.  Scales f32 in quads of 4 groups, the 16
+ *   channels of a tile side by side: sw[n,g] at float index
+ *   ((n/16)*Gq + g/4)*64 + (n%16)*4 + g%4, Gq = ceil((Kpad/group)/4).
  *   wsum f32[Npad] = (float) sum_g (double)sw[n,g] * sum_{k in g} W[n,k],
  *   accumulated in fp64 in increasing g.  All padding is zero.
  * ====================================================================== */
@@ -559,8 +563,8 @@ static int orc_s4_group_ok(int64_t group) {
 int64_t orc_packed_s4_bytes(int64_t N, int64_t K, int64_t group) {
   if (!orc_s4_group_ok(group)) return -1;
   int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group > 128 ? group : 128);
-  return ORC_HDR + orc_a256(Npad * Kpad / 2) + orc_a256(4 * Npad * (Kpad / group)) +
-         orc_a256(4 * Npad);
+  int64_t Gq = orc_ceil_div(Kpad / group, 4);
+  return ORC_HDR + orc_a256(Npad * Kpad / 2) + orc_a256(16 * Npad * Gq) + orc_a256(4 * Npad);
 }
 
 int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64_t w_sn,
@@ -568,9 +572,11 @@ int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64
   if (N <= 0 || K <= 0 || !orc_s4_group_ok(group)) return ORC_EINVAL;
   int64_t Npad = orc_round_up(N, 64), Kpad = orc_round_up(K, group > 128 ? group : 128);
   int64_t G = Kpad / group;
+  int64_t Gq = orc_ceil_div(G, 4);      /* scale quads per channel */
+  int64_t nblk = Kpad / 128;            /* 128-K blocks per channel */
   int64_t data_bytes = Npad * Kpad / 2;
   int64_t scale_off = ORC_HDR + orc_a256(data_bytes);
-  int64_t sum_off = scale_off + orc_a256(4 * Npad * G);
+  int64_t sum_off = scale_off + orc_a256(16 * Npad * Gq);
   int64_t total = sum_off + orc_a256(4 * Npad);
   memset(blob, 0, (size_t)total);
   orc_header(blob, 2u, 2u, N, K, Npad, Kpad, group, data_bytes, scale_off, sum_off, 0, total, 0);
@@ -580,7 +586,7 @@ int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64
       if (v < -8 || v > 7) return ORC_EINVAL;
       int64_t block = k / 128, t = (k % 128) / 32, c = (k % 32) / 8, j = k % 4;
       int64_t high = (k % 8) >= 4;
-      int64_t byte = ORC_HDR + n * (Kpad / 2) + block * 64 + 16 * c + 4 * t + j;
+      int64_t byte = ORC_HDR + ((n / 16) * nblk + block) * 1024 + (n % 16) * 64 + 16 * c + 4 * t + j;
       uint8_t nib = (uint8_t)(v & 0xF);
       blob[byte] |= high ? (uint8_t)(nib << 4) : nib;
     }
@@ -590,7 +596,7 @@ int orc_pack_s4_ref(int64_t N, int64_t K, int64_t group, const int8_t* Wt, int64
       int64_t gs = 0;
       for (int64_t k = g * group; k < (g + 1) * group && k < K; ++k) gs += Wt[n * w_sn + k * w_sk];
       float s = (g < Greal) ? sw[n * ldsw + g] : 0.0f;
-      memcpy(blob + scale_off + 4 * (n * G + g), &s, 4);
+      memcpy(blob + scale_off + 4 * (((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4), &s, 4);
       ws += (double)s * (double)gs;
     }
     float wsf = (float)ws;

@@ -59,7 +59,8 @@ def test_a8w4_gemm_workload(qp, orc, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 70, 96), (1, 1, 32), (2, 130, 200), (3, 64, 4096),
-                                   (5, 77, 1000), (17, 100, 256), (40, 33, 64), (1, 4096, 33)])
+                                   (5, 77, 1000), (17, 100, 256), (40, 33, 64), (1, 4096, 33),
+                                   (33, 48, 160), (65, 40, 256), (130, 48, 320)])
 def test_a8w4_small_shapes_and_tails(qp, orc, M, N, K):
     _case(qp, orc, synth.a8w4(synth.BASE_SEED + 7 * M + N + K, M, N, K))
 

@@ -280,8 +280,11 @@ def test_o7_s4_blob_decodes_back(orc, N, K):
     Kp = (K + 127) // 128 * 128
     Gp = Kp // 32
     assert h["format"] == 2 and h["group"] == 32 and h["Kpad"] == Kp
-    # decode with numpy axes: (row, block of 128 K, c, t, j) -> k = 128*block + 32t + 8c + [j | 4+j]
-    raw = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].reshape(h["Npad"], Kp // 128, 4, 4, 4)
+    # decode with numpy axes: (tile of 16 rows, block of 128 K, row in tile, c, t, j)
+    #   -> row 16*tile + r, k = 128*block + 32t + 8c + [j | 4+j]
+    raw = blob[h["data_off"]:h["data_off"] + h["data_bytes"]].reshape(
+        h["Npad"] // 16, Kp // 128, 16, 4, 4, 4).transpose(0, 2, 1, 3, 4, 5)
+    raw = raw.reshape(h["Npad"], Kp // 128, 4, 4, 4)
     lo = (raw & 0xF).astype(np.int16)
     hi = (raw >> 4).astype(np.int16)
     lo = np.where(lo >= 8, lo - 16, lo)
@@ -289,7 +292,9 @@ def test_o7_s4_blob_decodes_back(orc, N, K):
     dec = np.concatenate([lo, hi], axis=4)              # (row, block, c, t, 8)
     dec = dec.transpose(0, 1, 3, 2, 4).reshape(h["Npad"], Kp)   # -> (row, block, t, c, 8)
     assert np.array_equal(dec[:N, :K], W) and not dec[N:].any() and not dec[:, K:].any()
-    sc = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"] * Gp].view(np.float32).reshape(h["Npad"], Gp)
+    # scales: (tile of 16 rows, quad of 4 groups, row in tile, group in quad)
+    sc = blob[h["scale_off"]:h["scale_off"] + 4 * h["Npad"] * Gp].view(np.float32)
+    sc = sc.reshape(h["Npad"] // 16, Gp // 4, 16, 4).transpose(0, 2, 1, 3).reshape(h["Npad"], Gp)
     assert np.array_equal(sc[:N, :G], sw) and not sc[N:].any() and not sc[:, G:].any()
     Wp = np.zeros((N, G * 32), np.int64)
     Wp[:, :K] = W
