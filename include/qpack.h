@@ -155,12 +155,16 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  *   ([TRACT] pack_tensor_view).  Then f32 scale[Npad]; int32 colsum[Npad] =
  *   sum_{k<K} w[n,k] over the real K (the zero-point correction term,
  *   [MNN] kernel sums); int32 zp[Npad].
- * int4 blob: header; data [Npad][Kpad/2] bytes -- each channel's K is cut in
- *   blocks of 128 (64 bytes); byte 16c+4t+j of a block holds k = 32t+8c+j
- *   in its low nibble and k = 32t+8c+4+j in its high nibble (t = group of
- *   32 inside the block, c = 16-byte chunk), 4-bit two's complement, so one
- *   16-byte chunk carries the same 8 K of four consecutive groups;
- *   f32 scale[Npad][Kpad/group] (zero for groups past K);
+ * int4 blob: header; data Npad*Kpad/2 bytes -- each channel's K is cut in
+ *   blocks of 128 (64 bytes) and the 16 channels of a tile store each block
+ *   side by side: channel n, block b at ((n/16)*(Kpad/128) + b)*1024 +
+ *   (n%16)*64.  Byte 16c+4t+j of a block holds k = 32t+8c+j in its low
+ *   nibble and k = 32t+8c+4+j in its high nibble (t = group of 32 inside the
+ *   block, c = 16-byte chunk), 4-bit two's complement, so one 16-byte chunk
+ *   carries the same 8 K of four consecutive groups.  Scales f32 in quads
+ *   of four groups with the tile's 16 channels side by side: sw[n][g] at
+ *   float ((n/16)*ceil(G/4) + g/4)*64 + (n%16)*4 + g%4, G = Kpad/group
+ *   (zero for groups past K);
  *   f32 wsum[Npad] = sum_g sw[n,g] * sum_{k in g} w[n,k], accumulated in fp64
  *   (the weight kernel sum that folds the activation zero point,
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
