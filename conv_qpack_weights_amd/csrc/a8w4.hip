@@ -64,15 +64,19 @@ struct W4 {
   int64_t N, Npad, Kpad, nblk;
 };
 
-// ---- GEMV: one wave per RPW output channels, lanes split K by 16-byte chunks ----
-// Chunk h of a row is the 8-K piece c = h%4 of the four groups 4(h/4)..+3.
-// All of a lane's weight chunks and scales are requested first; while they
-// are in flight the workgroup quantizes the activation row (kFused, M = 1:
-// the same device steps as qquantize_rows_s8) into LDS, permuted so that
-// the 32 activation bytes of a chunk are contiguous; otherwise it reads the
-// quantized rows from memory.  Lane partial sums are reduced with DPP in a
-// fixed order.
-template <int NT, int RPW, bool kFused>
+// ---- GEMV: a workgroup per 16-channel tile, waves split the 128-K blocks ----
+// Lane l handles channel l/4 of the tile and 16-byte chunk c = l%4 of each
+// of its wave's blocks (the 8-K piece c of four groups), so one wave load
+// instruction reads one tile-block: 1 KiB in one piece.  Its four group
+// scales are 16 bytes shared by the four lanes of the channel.  All of a
+// wave's weight and scale loads are issued first; while they are in flight
+// the workgroup quantizes the activation row (kFused, M = 1: the same device
+// steps as qquantize_rows_s8) into LDS, permuted so that the 32 activation
+// bytes of a chunk are contiguous; otherwise it reads the quantized rows
+// from memory (row-major).  Partial sums are reduced across the four lanes
+// of a channel with DPP and then across the waves through LDS, in a fixed
+// order.  Rows m > 0 reuse the weights held in registers.
+template <int NT, bool kFused>
 __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__ X, int64_t K,
                                                        const int8_t* __restrict__ qa_g,
                                                        int64_t lda, const float* __restrict__ sa_g,
@@ -82,90 +86,122 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
                                                        float hi, float* __restrict__ Y,
                                                        int64_t ldy) {
   constexpr int NW = NT / 64;
+  constexpr int BB = 4;      // blocks a wave holds in registers per batch
+  constexpr int MR = 4;      // rows per call (M = 1 fused, M <= 4 prequantized)
   extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];
   __shared__ float red[2 * NW];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t nbase = ((int64_t)blockIdx.x * NW + wave) * RPW;  // < Npad by grid sizing
-  const int64_t chunks = w.Kpad / 32;
-  constexpr int U = 2;  // chunks per lane per batch
+  __shared__ float part_w[NW][16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ch = lane >> 2, c = lane & 3;
+  const int64_t tile = blockIdx.x;
+  const int64_t nb = w.nblk;
+  const uint8_t* wbase = w.data + tile * nb * 1024 + lane * 16;
+  const float* sbase = w.scale + tile * nb * 64 + ch * 4;
+  // per-channel epilogue operands, fetched up front (off the critical path)
+  const int64_t n_out = tile * 16 + (tid & 15);
+  float wsum_c = 0.0f, bias_c = 0.0f;
+  if (tid < 16) {
+    wsum_c = w.wsum[n_out];
+    bias_c = (bias && n_out < w.N) ? bias[n_out] : 0.0f;
+  }
 
-  for (int64_t m = 0; m < M; ++m) {
-    float part[RPW];
+  float part[MR];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) part[i] = 0.0f;
-    float sa = 0.0f;
-    int32_t za = 0;
-    for (int64_t h0 = 0; h0 < chunks; h0 += 64 * U) {
-      uint4 wv[U][RPW];
-      float4 sv[U][RPW];
+  for (int m = 0; m < MR; ++m) part[m] = 0.0f;
+  float sa = 0.0f;
+  int32_t za = 0;
+  const bool xvec = (((uintptr_t)X) & 15) == 0;
+  RowFirst xfirst;
+  float sa_m[MR];
+  int32_t za_m[MR];
+  if constexpr (kFused) {
+    xfirst = quantize_row_first<NT>(X, K, xvec);  // before the weights
+  } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t h = h0 + u * 64 + lane;
-        const bool live = h < chunks;
-        const int64_t hh = live ? h : chunks - 1;
+    for (int m = 0; m < MR; ++m) {
+      sa_m[m] = m < M ? sa_g[m] : 0.0f;
+      za_m[m] = m < M ? za_g[m] : 0;
+    }
+  }
+  // Batches are uniform over the workgroup (every wave runs all of them);
+  // block j*NW*BB + u*NW + wave, past the end clamped with zero scales.
+  const int64_t nbatch = (nb + (int64_t)NW * BB - 1) / ((int64_t)NW * BB);
+  for (int64_t j = 0; j < nbatch; ++j) {
+    uint4 wv[BB];
+    float4 sv[BB];
+    int64_t blk[BB];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          const int64_t n = nbase + i;
-          const int64_t tb = (n >> 4) * w.nblk + (hh >> 2);  // tile-block
-          wv[u][i] = *reinterpret_cast<const uint4*>(w.data + tb * 1024 + (n & 15) * 64 +
-                                                     (hh & 3) * 16);
-          const float4 s4 =
-              *reinterpret_cast<const float4*>(w.scale + tb * 64 + (n & 15) * 4);
-          sv[u][i] = live ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    for (int u = 0; u < BB; ++u) {
+      const int64_t b = (j * BB + u) * NW + wave;
+      blk[u] = b < nb ? b : nb - 1;
+      wv[u] = *reinterpret_cast<const uint4*>(wbase + blk[u] * 1024);
+      const float4 s4 = *reinterpret_cast<const float4*>(sbase + blk[u] * 64);
+      sv[u] = b < nb ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (kFused) {
+      if (j == 0) {  // quantize the row while the first loads are in flight
+        quantize_row_wg<NT, true>(X, K, w.Kpad, xvec, true, qa_lds, red, &sa, &za, &xfirst);
+        __syncthreads();
       }
-      if (h0 == 0) {
-        if constexpr (kFused) {
-          const float* xr = X + m * K;
-          quantize_row_wg<NT, true>(xr, K, w.Kpad, (((uintptr_t)xr) & 15) == 0, true, qa_lds,
-                                    red, &sa, &za);
-          __syncthreads();
-        } else {
-          sa = sa_g[m];
-          za = za_g[m];
-        }
-      }
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t h = h0 + u * 64 + lane;
-        const int64_t hh = h < chunks ? h : chunks - 1;
-        uint2 a[4];
-        if constexpr (kFused) {
-          const int8_t* ab = qa_lds + (hh >> 2) * 128 + (hh & 3) * 32;
-          const uint4 p0 = *reinterpret_cast<const uint4*>(ab);
-          const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 16);
-          a[0] = make_uint2(p0.x, p0.y);
-          a[1] = make_uint2(p0.z, p0.w);
-          a[2] = make_uint2(p1.x, p1.y);
-          a[3] = make_uint2(p1.z, p1.w);
-        } else {
-          const int8_t* ab = qa_g + m * lda + (hh >> 2) * 128 + (hh & 3) * 8;
+    for (int m = 0; m < MR; ++m) {
+      if (m < M) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint2*>(ab + 32 * t);
-        }
+        for (int u = 0; u < BB; ++u) {
+          uint2 a[4];
+          if constexpr (kFused) {
+            const int8_t* ab = qa_lds + blk[u] * 128 + c * 32;
+            const uint4 p0 = *reinterpret_cast<const uint4*>(ab);
+            const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 16);
+            a[0] = make_uint2(p0.x, p0.y);
+            a[1] = make_uint2(p0.z, p0.w);
+            a[2] = make_uint2(p1.x, p1.y);
+            a[3] = make_uint2(p1.z, p1.w);
+          } else {
+            const int8_t* ab = qa_g + m * lda + blk[u] * 128 + c * 8;
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          const uint4 wq = wv[u][i];
+            for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint2*>(ab + 32 * t);
+          }
+          const uint4 wq = wv[u];
           const float d0 = (float)word_dot16(wq.x, a[0].x, a[0].y);
           const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
           const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
           const float d3 = (float)word_dot16(wq.w, a[3].x, a[3].y);
-          part[i] = part[i] + sv[u][i].x * d0;
-          part[i] = part[i] + sv[u][i].y * d1;
-          part[i] = part[i] + sv[u][i].z * d2;
-          part[i] = part[i] + sv[u][i].w * d3;
+          part[m] = part[m] + sv[u].x * d0;
+          part[m] = part[m] + sv[u].y * d1;
+          part[m] = part[m] + sv[u].z * d2;
+          part[m] = part[m] + sv[u].w * d3;
         }
       }
     }
+  }
+  for (int64_t m = 0; m < M && m < MR; ++m) {
+    float p = part[m];
+    // the four lanes of a channel: quad_perm [1,0,3,2] then [2,3,0,1]
+    p = p + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p),
+                                                                  0xB1, 0xF, 0xF, false));
+    p = p + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p),
+                                                                  0x4E, 0xF, 0xF, false));
+    if (c == 0) part_w[wave][ch] = p;
+    __syncthreads();
+    if (tid < 16) {
+      float S = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const float S = wave_reduce(part[i], AddOp{});
-      const int64_t n = nbase + i;
-      if (lane == i && n < w.N)
-        Y[m * ldy + n] = finish(S, sa, za, w.wsum[n], bias ? bias[n] : 0.0f, lo, hi);
+      for (int v = 0; v < NW; ++v) S = S + part_w[v][tid];
+      if constexpr (!kFused) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+          if (r == m) {
+            sa = sa_m[r];
+            za = za_m[r];
+          }
+      }
+      if (n_out < w.N) Y[m * ldy + n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
     }
-    if constexpr (kFused) __syncthreads();
+    __syncthreads();
   }
 }
 
@@ -446,21 +482,19 @@ qp_status validate_w4(const qp_packed_info* b, int64_t K) {
   return QP_OK;
 }
 
-template <int NT, int RPW>
+template <int NT>
 qp_status launch_gemv_cfg(const float* X, int64_t K, const int8_t* qa, int64_t lda,
                           const float* sa, const int32_t* za, int64_t M, const W4& w,
                           const float* bias, float lo, float hi, float* Y, int64_t ldy,
                           bool fused, hipStream_t stream) {
-  constexpr int rows_per_block = (NT / 64) * RPW;
-  static_assert(64 % rows_per_block == 0, "blocks must tile the 64-row padding");
-  const unsigned blocks = (unsigned)ceil_div(w.N, rows_per_block);
+  const unsigned blocks = (unsigned)(w.Npad / 16);
   const size_t lds = fused ? (size_t)w.Kpad : 0;
   if (fused)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, RPW, true>), dim3(blocks), dim3(NT), lds, stream, X,
-                       K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true>), dim3(blocks), dim3(NT), lds, stream, X, K,
+                       qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   else
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, RPW, false>), dim3(blocks), dim3(NT), lds, stream, X,
-                       K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false>), dim3(blocks), dim3(NT), lds, stream, X, K,
+                       qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w4 gemv");
 }
 
@@ -468,7 +502,8 @@ qp_status launch_gemv(const float* X, int64_t K, const int8_t* qa, int64_t lda,
                       const float* sa, const int32_t* za, int64_t M, const W4& w,
                       const float* bias, float lo, float hi, float* Y, int64_t ldy, bool fused,
                       hipStream_t stream) {
-  return launch_gemv_cfg<512, 2>(X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, fused, stream);
+  QP_REQUIRE(M <= 4, QP_EUNSUPPORTED, "a8w4 gemv: at most 4 rows");
+  return launch_gemv_cfg<512>(X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, fused, stream);
 }
 
 template <int FM, int FN, int RW, int CW, int KS>

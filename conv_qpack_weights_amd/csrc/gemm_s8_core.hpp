@@ -404,43 +404,124 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     int64_t m = m0 + wm * TM + j * MF + (lane % MF);
     rs[j] = (kRowSum && m < g.M) ? g.rowsum[m] : 0;
   }
+  // The clamp bounds in a VGPR let the clamp be one v_med3 (one scalar
+  // operand per instruction).
+  int32_t lo_v = g.lo;
+  asm volatile("" : "+v"(lo_v));
+
+  // Output values of fragment row j, channel run (i, q) of this lane.
+  auto outputs = [&](int i, int q, int j, const v4i& cc, const v4i& mm, const v4i& ss,
+                     const v4i& zb, const int64_t (&half)[4], const int32_t (&s2)[4],
+                     const uint32_t (&mask)[4], int32_t (&out)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
+      if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
+      if constexpr (kOut32) {
+        out[r] = (int32_t)a;
+      } else if constexpr (kShiftHi) {
+        out[r] = clamp_i32(rhe_shift_hi((int32_t)a, mm[r], half[r], s2[r], mask[r]) + g.zp_out,
+                           lo_v, g.hi);
+      } else {
+        out[r] = clamp_i64(rhe_shift64((int32_t)a, mm[r], ss[r]) + g.zp_out, lo_v, g.hi);
+      }
+    }
+  };
+  // Per-run column constants.
+  auto column = [&](int i, int q, int* jn_out, v4i* cc, v4i* mm, v4i* ss, v4i* zb,
+                    int64_t (&half)[4], int32_t (&s2)[4], uint32_t (&mask)[4]) {
+    const int jn = wn * TN + i * MF + (MF == 16 ? 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5));
+    *jn_out = jn;
+    *cc = *reinterpret_cast<const v4i*>(&col_c[jn]);
+    *mm = *reinterpret_cast<const v4i*>(&col_m0[jn]);
+    *ss = *reinterpret_cast<const v4i*>(&col_sh[jn]);
+    *zb = v4i{0, 0, 0, 0};
+    if (kRowSum) *zb = *reinterpret_cast<const v4i*>(&col_zb[jn]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s2[r] = (*ss)[r] - 32;
+      half[r] = (int64_t)1 << ((*ss)[r] - 1);
+      mask[r] = (1u << (s2[r] & 31)) - 1u;
+    }
+  };
+
+  // Full tiles with 16-byte aligned output rows go through LDS (the A ring
+  // is free now): each wave writes its values there, then the workgroup
+  // stores whole output rows with 16-byte stores, instead of each lane
+  // writing 4 (int8) or 16 (int32) bytes into 32 different rows.  int32
+  // tiles go 64 rows at a time.  Chunk c (16 bytes) of staged row r sits at
+  // chunk position c ^ swizzle(r), which keeps the lane writes within two
+  // ways of bank conflict and the row reads conflict-free.
+  constexpr int ES = kOut32 ? 4 : 1;             // output element bytes
+  constexpr int RB = BN * ES;                    // staged row bytes
+  constexpr int CPR = RB / 16;                   // 16-byte chunks per row
+  constexpr int PR = kOut32 ? 64 : BM;           // rows per pass
+  constexpr bool kStaged = MF == 32 && (CPR == 8 || CPR >= 16) && PR * RB <= SA * STAGE &&
+                           (PR * CPR) % (NW * 64) == 0 && PR % 64 == 0;
+  const bool staged = kStaged && full && ((g.ldc * ES) % 16 == 0) && (((uintptr_t)g.C & 15) == 0);
+  if (staged) {
+    auto swz_row = [](int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); };
+    int8_t* stg = smem;
+    __syncthreads();  // every wave has left the A ring
+#pragma unroll
+    for (int p = 0; p < BM / PR; ++p) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          int jn;
+          v4i cc, mm, ss, zb;
+          int64_t half[4];
+          int32_t s2[4];
+          uint32_t mask[4];
+          column(i, q, &jn, &cc, &mm, &ss, &zb, half, s2, mask);
+#pragma unroll
+          for (int j = p * (PR / MF); j < (p + 1) * (PR / MF); ++j) {
+            int32_t out[4];
+            outputs(i, q, j, cc, mm, ss, zb, half, s2, mask, out);
+            const int r = j * MF + (lane % MF) - p * PR;  // row inside the pass
+            const int byte = jn * ES;                     // column byte in the row
+            int8_t* dst = stg + r * RB + 16 * ((byte >> 4) ^ swz_row(r)) + (byte & 15);
+            if constexpr (kOut32) {
+              *reinterpret_cast<v4i*>(dst) = v4i{out[0], out[1], out[2], out[3]};
+            } else {
+              *reinterpret_cast<uint32_t*>(dst) =
+                  ((uint32_t)out[0] & 0xFFu) | (((uint32_t)out[1] & 0xFFu) << 8) |
+                  (((uint32_t)out[2] & 0xFFu) << 16) | ((uint32_t)out[3] << 24);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      int8_t* crow0 = static_cast<int8_t*>(g.C) + ((m0 + p * PR) * g.ldc + n0) * ES;
+#pragma unroll
+      for (int it = 0; it < PR * CPR / (NW * 64); ++it) {
+        const int id = it * NW * 64 + tid;
+        const int r = id / CPR, ch = id % CPR;
+        const v4i v = *reinterpret_cast<const v4i*>(stg + r * RB + 16 * (ch ^ swz_row(r)));
+        *reinterpret_cast<v4i*>(crow0 + (int64_t)r * g.ldc * ES + 16 * ch) = v;
+      }
+      if (p + 1 < BM / PR) __syncthreads();
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
-      const int jn = wn * TN + i * MF + (MF == 16 ? 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5));
-      const int64_t n = n0 + jn;
-      const v4i cc = *reinterpret_cast<const v4i*>(&col_c[jn]);
-      const v4i mm = *reinterpret_cast<const v4i*>(&col_m0[jn]);
-      const v4i ss = *reinterpret_cast<const v4i*>(&col_sh[jn]);
-      v4i zb = v4i{0, 0, 0, 0};
-      if (kRowSum) zb = *reinterpret_cast<const v4i*>(&col_zb[jn]);
+      int jn;
+      v4i cc, mm, ss, zb;
       int64_t half[4];
       int32_t s2[4];
       uint32_t mask[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s2[r] = ss[r] - 32;
-        half[r] = (int64_t)1 << (ss[r] - 1);
-        mask[r] = (1u << (s2[r] & 31)) - 1u;
-      }
+      column(i, q, &jn, &cc, &mm, &ss, &zb, half, s2, mask);
+      const int64_t n = n0 + jn;
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int64_t m = m0 + wm * TM + j * MF + (lane % MF);
         int32_t out[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
-          if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
-          if constexpr (kOut32) {
-            out[r] = (int32_t)a;
-          } else if constexpr (kShiftHi) {
-            out[r] = clamp_i32(rhe_shift_hi((int32_t)a, mm[r], half[r], s2[r], mask[r]) + g.zp_out,
-                               g.lo, g.hi);
-          } else {
-            out[r] = clamp_i64(rhe_shift64((int32_t)a, mm[r], ss[r]) + g.zp_out, g.lo, g.hi);
-          }
-        }
+        outputs(i, q, j, cc, mm, ss, zb, half, s2, mask, out);
         if (full) {
           if constexpr (kOut32) {
             *reinterpret_cast<v4i*>(static_cast<int32_t*>(g.C) + m * g.ldc + n) =

@@ -88,11 +88,29 @@ __device__ __forceinline__ uint32_t quantize_one(float x, float s, int32_t z) {
 // each 128-K block the 8-byte piece (t, c) holding k = 32t + 8c .. +8 goes to
 // offset 32c + 8t, so the four pieces one lane needs are 32 contiguous
 // bytes (requires kfill % 128 == 0 and a 16-byte aligned dst).
+// The thread's first 16 values, loaded ahead (quantize_row_first) so that a
+// caller can put the row's loads in flight before other traffic.
+struct RowFirst {
+  float4 v[4];
+};
+template <int NT>
+__device__ __forceinline__ RowFirst quantize_row_first(const float* __restrict__ x, int64_t K,
+                                                       bool vec) {
+  RowFirst f;
+  const int64_t k0 = (int64_t)threadIdx.x * 16;
+  if (vec && k0 + 16 <= K) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f.v[q] = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+  }
+  return f;
+}
+
 template <int NT, bool kChunkMajor = false>
 __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
                                                 int64_t kfill, bool vec, bool dst_vec,
                                                 int8_t* __restrict__ dst, float* red,
-                                                float* s_out, int32_t* z_out) {
+                                                float* s_out, int32_t* z_out,
+                                                const RowFirst* pre = nullptr) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x;
   float lo = 0.0f, hi = 0.0f;
@@ -104,7 +122,9 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
     if (vec && k0 + 16 <= K) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+        const float4 v = (pre && k0 == (int64_t)t * 16)
+                             ? pre->v[q]
+                             : *reinterpret_cast<const float4*>(x + k0 + 4 * q);
         if (k0 == (int64_t)t * 16) first[q] = v;
         lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
         hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
