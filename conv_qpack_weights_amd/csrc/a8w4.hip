@@ -117,7 +117,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   float sa_m[MR];
   int32_t za_m[MR];
   if constexpr (kFused) {
-    xfirst = quantize_row_first<NT>(X, K, xvec);  // before the weights
+    xfirst = quantize_row_first<NT, 8>(X, K, xvec);  // before the weights
   } else {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
     }
     if constexpr (kFused) {
       if (j == 0) {  // quantize the row while the first loads are in flight
-        quantize_row_wg<NT, true>(X, K, w.Kpad, xvec, true, qa_lds, red, &sa, &za, &xfirst);
+        quantize_row_wg<NT, true, 8>(X, K, w.Kpad, xvec, true, qa_lds, red, &sa, &za, &xfirst);
         __syncthreads();
       }
     }

@@ -88,49 +88,53 @@ __device__ __forceinline__ uint32_t quantize_one(float x, float s, int32_t z) {
 // each 128-K block the 8-byte piece (t, c) holding k = 32t + 8c .. +8 goes to
 // offset 32c + 8t, so the four pieces one lane needs are 32 contiguous
 // bytes (requires kfill % 128 == 0 and a 16-byte aligned dst).
-// The thread's first 16 values, loaded ahead (quantize_row_first) so that a
+// The thread's first E values, loaded ahead (quantize_row_first) so that a
 // caller can put the row's loads in flight before other traffic.
 struct RowFirst {
   float4 v[4];
 };
-template <int NT>
+template <int NT, int E = 16>
 __device__ __forceinline__ RowFirst quantize_row_first(const float* __restrict__ x, int64_t K,
                                                        bool vec) {
   RowFirst f;
-  const int64_t k0 = (int64_t)threadIdx.x * 16;
-  if (vec && k0 + 16 <= K) {
+  const int64_t k0 = (int64_t)threadIdx.x * E;
+  if (vec && k0 + E <= K) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f.v[q] = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+    for (int q = 0; q < E / 4; ++q) f.v[q] = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
   }
   return f;
 }
 
-template <int NT, bool kChunkMajor = false>
+// E: values per thread per pass (16, or 8 to spread a short row over more
+// threads).
+template <int NT, bool kChunkMajor = false, int E = 16>
 __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
                                                 int64_t kfill, bool vec, bool dst_vec,
                                                 int8_t* __restrict__ dst, float* red,
                                                 float* s_out, int32_t* z_out,
                                                 const RowFirst* pre = nullptr) {
+  static_assert(E == 16 || E == 8, "8 or 16 values per thread");
   constexpr int NW = NT / 64;
+  constexpr int Q = E / 4;
   const int t = threadIdx.x;
   float lo = 0.0f, hi = 0.0f;
-  // pass 1: extremes; a thread's first 16 values stay in registers for pass
-  // 2 (rows of up to 16*NT values are read once)
-  float4 first[4];
-  const bool keep = vec && (int64_t)t * 16 + 16 <= K;
-  for (int64_t k0 = (int64_t)t * 16; k0 < K; k0 += NT * 16) {
-    if (vec && k0 + 16 <= K) {
+  // pass 1: extremes; a thread's first E values stay in registers for pass
+  // 2 (rows of up to E*NT values are read once)
+  float4 first[Q];
+  const bool keep = vec && (int64_t)t * E + E <= K;
+  for (int64_t k0 = (int64_t)t * E; k0 < K; k0 += NT * E) {
+    if (vec && k0 + E <= K) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = (pre && k0 == (int64_t)t * 16)
+      for (int q = 0; q < Q; ++q) {
+        const float4 v = (pre && k0 == (int64_t)t * E)
                              ? pre->v[q]
                              : *reinterpret_cast<const float4*>(x + k0 + 4 * q);
-        if (k0 == (int64_t)t * 16) first[q] = v;
+        if (k0 == (int64_t)t * E) first[q] = v;
         lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
         hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
       }
     } else {
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < E; ++j)
         if (k0 + j < K) {
           const float v = x[k0 + j];
           lo = qp_min(lo, v);
@@ -156,13 +160,13 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
   float s;
   int32_t z;
   params_from_range(lo, hi, &s, &z);
-  // pass 2: codes (beyond the first 16 per thread, x is read again)
-  for (int64_t k0 = (int64_t)t * 16; k0 < kfill; k0 += NT * 16) {
-    uint32_t w[4];
-    if (vec && k0 + 16 <= K) {
+  // pass 2: codes (beyond the first E per thread, x is read again)
+  for (int64_t k0 = (int64_t)t * E; k0 < kfill; k0 += NT * E) {
+    uint32_t w[Q];
+    if (vec && k0 + E <= K) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = (keep && k0 == (int64_t)t * 16)
+      for (int q = 0; q < Q; ++q) {
+        const float4 v = (keep && k0 == (int64_t)t * E)
                              ? first[q]
                              : *reinterpret_cast<const float4*>(x + k0 + 4 * q);
         w[q] = quantize_one(v.x, s, z) | (quantize_one(v.y, s, z) << 8) |
@@ -170,7 +174,7 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < Q; ++q) {
         uint32_t acc = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -181,15 +185,20 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
       }
     }
     if constexpr (kChunkMajor) {
-      // k0 = 128b + 32t + 16p: pieces c = 2p and 2p+1 of group t
-      const int64_t b = k0 >> 7, t = (k0 >> 5) & 3, p = (k0 >> 4) & 1;
-      int8_t* base = dst + b * 128 + t * 8;
-      *reinterpret_cast<uint2*>(base + (2 * p) * 32) = make_uint2(w[0], w[1]);
-      *reinterpret_cast<uint2*>(base + (2 * p + 1) * 32) = make_uint2(w[2], w[3]);
-    } else if (dst_vec && k0 + 16 <= kfill) {
-      *reinterpret_cast<uint4*>(dst + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+      // the 8-byte piece holding k = 128b + 32g + 8c .. +8 goes to 128b + 32c + 8g
+#pragma unroll
+      for (int h = 0; h < Q / 2; ++h) {
+        const int64_t kk = k0 + 8 * h;
+        const int64_t b = kk >> 7, g = (kk >> 5) & 3, cc = (kk >> 3) & 3;
+        *reinterpret_cast<uint2*>(dst + b * 128 + cc * 32 + g * 8) = make_uint2(w[2 * h], w[2 * h + 1]);
+      }
+    } else if (dst_vec && k0 + E <= kfill) {
+      if constexpr (E == 16)
+        *reinterpret_cast<uint4*>(dst + k0) = make_uint4(w[0], w[1], w[2], w[3]);
+      else
+        *reinterpret_cast<uint2*>(dst + k0) = make_uint2(w[0], w[1]);
     } else {
-      for (int j = 0; j < 16 && k0 + j < kfill; ++j) dst[k0 + j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
+      for (int j = 0; j < E && k0 + j < kfill; ++j) dst[k0 + j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
     }
   }
   *s_out = s;
