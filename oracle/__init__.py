@@ -69,6 +69,7 @@ _SIGS = {
                              _I64, _I64, _P]),
     "orc_quantize_row_s8": (None, [_P, _I64, _P, C.POINTER(_F), C.POINTER(_I32)]),
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
+    "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
     "orc_a8w4_blockwise": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64,
                                      _P, _F, _F, _P, _I64]),
     "orc_packed_s8_bytes": (_I64, [_I64, _I64]),
@@ -267,6 +268,18 @@ def quantize_rows_s8(X):
     zp = np.zeros(M, dtype=np.int32)
     lib().orc_quantize_rows_s8(M, K, _ptr(X), K, _ptr(q), K, _ptr(sc), _ptr(zp))
     return q, sc, zp
+
+
+def quantize_rows_s8_sym(X):
+    """O5s: symmetric per-row quantization; returns (q, scale)."""
+    X = _arr(X, np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    M, K = X.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    sc = np.zeros(M, dtype=np.float32)
+    lib().orc_quantize_rows_s8_sym(M, K, _ptr(X), K, _ptr(q), K, _ptr(sc))
+    return q, sc
 
 
 # ---------------------------------------------------------------- O6

@@ -421,6 +421,36 @@ void orc_quantize_rows_s8(int64_t M, int64_t K, const float* X, int64_t ldx, int
 }
 
 /* ========================================================================
+ * O5s -- dynamic per-row symmetric quantization to int8.
+ * [MNN] BatchSymDynamicQuant: per row the largest magnitude (MNNAbsMax), a
+ * scale from it (MNNQuantScale), then the codes (MNNDynamicQuant) with the
+ * input zero point set to 0; the helpers' bodies are not on the page.
+ * Reading, in the same f32 style as O5 (division by the dequantization
+ * scale, round half to even):
+ *   amax = max |x|;  scale = amax / 127;   all-zero row: scale = 1
+ *   q = clamp(rint(x/scale), -127, 127)    (zero point 0)
+ * ====================================================================== */
+void orc_quantize_row_s8_sym(const float* x, int64_t K, int8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int64_t k = 0; k < K; ++k) {
+    float a = fabsf(x[k]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 127.0f;
+  if (s == 0.0f) s = 1.0f;
+  for (int64_t k = 0; k < K; ++k) {
+    float r = rintf(x[k] / s);
+    q[k] = (int8_t)orc_clamp64((int64_t)r, -127, 127);
+  }
+  *scale = s;
+}
+
+void orc_quantize_rows_s8_sym(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q,
+                              int64_t ldq, float* scale) {
+  for (int64_t m = 0; m < M; ++m) orc_quantize_row_s8_sym(X + m * ldx, K, Q + m * ldq, &scale[m]);
+}
+
+/* ========================================================================
  * O6 -- int8 activations times int4 weights with one f32 scale per group of
  * `group` consecutive K ([KLEIDI]: f32 output with clamp, dynamically
  * quantized int8 activations, signed int4 weights in blocks of 32, and no

@@ -78,6 +78,9 @@ int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int
 
 /* ---- O5: dynamic per-row asymmetric int8 quantization (f32) ------------- */
 void orc_quantize_row_s8(const float* x, int64_t K, int8_t* q, float* scale, int32_t* zp);
+void orc_quantize_row_s8_sym(const float* x, int64_t K, int8_t* q, float* scale);
+void orc_quantize_rows_s8_sym(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q,
+                              int64_t ldq, float* scale);
 void orc_quantize_rows_s8(int64_t M, int64_t K, const float* X, int64_t ldx, int8_t* Q,
                           int64_t ldq, float* scale, int32_t* zp);
 

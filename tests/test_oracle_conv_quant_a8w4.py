@@ -145,6 +145,67 @@ def test_o5_brute_force_grid(orc):
             assert qv == want
 
 
+# ------------------------------------------------------------------ O5s
+def test_o5s_special_rows(orc):
+    """All-zero row: scale 1, codes 0.  The largest magnitude maps to +-127."""
+    q, s = orc.quantize_rows_s8_sym(np.zeros((1, 7), np.float32))
+    assert s[0] == 1.0 and not q.any()
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 3, (5, 33)).astype(np.float32)
+    q, s = orc.quantize_rows_s8_sym(x)
+    for r in range(5):
+        i = int(np.argmax(np.abs(x[r])))
+        assert q[r, i] == (127 if x[r, i] > 0 else -127)
+        assert s[r] == np.float32(np.abs(x[r]).max()) / np.float32(127)
+    assert q.min() >= -127 and q.max() <= 127
+
+
+def test_o5s_odd_symmetry_monotone_and_error_bound(orc):
+    rng = np.random.default_rng(42)
+    x = rng.uniform(-5, 5, (3, 101)).astype(np.float32)
+    q, s = orc.quantize_rows_s8_sym(x)
+    qn, sn = orc.quantize_rows_s8_sym(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    for r in range(3):
+        order = np.argsort(x[r], kind="stable")
+        assert (np.diff(q[r][order].astype(int)) >= 0).all()
+        err = np.abs(q[r].astype(np.float64) * float(s[r]) - x[r].astype(np.float64))
+        assert (err <= 0.5 * float(s[r]) * (1 + 1e-5)).all()
+
+
+def test_o5s_exact_ties_round_to_even(orc):
+    """amax = 127/128 gives scale = 2^-7 exactly, so x = (j + 1/2) * 2^-7 is an
+    exact tie of x/scale: it must round to the even neighbour."""
+    j = np.array([0, 1, 2, 3, 4, 125, -1, -2, -3, -126], np.float64)
+    x = np.concatenate([[127.0 / 128.0], (j + 0.5) / 128.0]).astype(np.float32)
+    q, s = orc.quantize_rows_s8_sym(x)
+    assert s[0] == np.float32(2.0 ** -7)
+    # ties: 0.5->0, 1.5->2, 2.5->2, 3.5->4, 4.5->4, 125.5->126, -0.5->0, -1.5->-2,
+    # -2.5->-2, -125.5->-126
+    want = [127] + [0, 2, 2, 4, 4, 126, 0, -2, -2, -126]
+    assert q[0].tolist() == want
+
+
+def test_o5s_brute_force_grid(orc):
+    """Rows over a value grid: codes equal the exact rational rounding of
+    x/scale (with the oracle's f32 scale) away from f32-rounding distance of
+    a tie, and the scale is the f32 quotient max|x| / 127."""
+    vals = np.array([-3.0, -1.25, -0.5, 0.0, 0.75, 1.0, 2.5, 7.0], np.float32)
+    import itertools
+    for row in itertools.product(vals, repeat=3):
+        x = np.array(row, np.float32)
+        q, s = orc.quantize_rows_s8_sym(x)
+        amax = np.float32(np.abs(x).max())
+        assert s[0] == (np.float32(amax / np.float32(127)) if amax > 0 else 1.0)
+        sf = Fraction(float(s[0]))
+        for xv, qv in zip(x, q[0]):
+            ex = Fraction(float(xv)) / sf
+            frac = ex - math.floor(ex)
+            if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 16):
+                continue
+            assert qv == max(-127, min(127, round(ex)))
+
+
 # ------------------------------------------------------------------ O6
 def test_o6_single_group_closed_form(orc):
     rng = np.random.default_rng(16)
