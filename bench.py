@@ -298,6 +298,36 @@ def main():
                 "frac_mfma_peak": round(2 * mac / msg / 1e9 / PEAK_INT8_TOPS, 5)}
             del bl
 
+        # dynamic per-row activation quantization (asymmetric and symmetric),
+        # the A8W4 GEMM's activation shape: M=128, K=4096
+        xq = d(synth.a8w4_gemm(128)["X"])
+        qq = torch.empty((128, 4096), dtype=torch.int8, device=dev)
+        sq = torch.empty(128, dtype=torch.float32, device=dev)
+        zq = torch.empty(128, dtype=torch.int32, device=dev)
+        msa = graph_time(lambda: qp.qquantize_rows_s8(xq, q=qq, row_scale=sq, row_zp=zq), 50)
+        mss_ = graph_time(lambda: qp.qquantize_rows_s8_sym(xq, q=qq, row_scale=sq), 50)
+        qbytes = 128 * 4096 * 5 + 128 * 8
+        for name, ms_ in (("quantize_rows_s8_128x4096", msa), ("quantize_rows_s8_sym_128x4096", mss_)):
+            workloads[name] = {"us": round(ms_ * 1e3, 2),
+                               "GBps": round(qbytes / ms_ / 1e6, 1),
+                               "frac_hbm_peak": round(qbytes / ms_ / 1e6 / PEAK_HBM_GBS, 4)}
+
+        # one-time weight packs (load-time steps): the 8192^2 int8 and the
+        # 11008x4096 int4 weights
+        Wp = d(g["W"])
+        swp = d(g["s_w"])
+        msp8 = ev_time(lambda: qp.pack_s8(Wp, scales=swp), 3)
+        gg4 = synth.a8w4_gemm(16)
+        W4d, sw4d = d(gg4["W"]), d(gg4["sw"])
+        msp4 = ev_time(lambda: qp.pack_s4(W4d, sw4d), 3)
+        workloads["pack_s8_8192x8192"] = {
+            "ms": round(msp8, 3), "GBps": round(2 * 8192 * 8192 / msp8 / 1e6, 1),
+            "note": "includes the blob allocation and the scale read-back sync"}
+        workloads["pack_s4_11008x4096"] = {
+            "ms": round(msp4, 3), "GBps": round((11008 * 4096 * 1.5) / msp4 / 1e6, 1),
+            "note": "includes the blob allocation"}
+        del Wp, W4d
+
         # 3x3 conv 56x56x64 -> 64 via im2col + GEMM
         c = synth.conv3x3_nhwc()
         bc, ic = qp.pack_s8(d(c["W"]), scales=d(c["s_w"]))

@@ -65,6 +65,7 @@ SIGNATURES = {
     "qpack_weights": (C.c_int, [_QT, _P, _I32, _I32, _P, C.c_size_t, _PI, _P]),
     "qp_packed_info_from_header": (C.c_int, [_P, _PI]),
     "qquantize_rows_s8": (C.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "qquantize_rows_s8_sym": (C.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "qgemm_s8s8_requant_ws_size": (C.c_int, [_QT, _PI, _SZ]),
     "qgemm_s8s8_requant": (C.c_int, [_QT, _P, _PI, _P, _P, _I64, _QT, _I32, _P, _P, C.c_size_t,
                                      _P]),
@@ -207,6 +208,17 @@ def qquantize_rows_s8(x: torch.Tensor, q=None, row_scale=None, row_zp=None):
                                   _ptr(row_scale), _ptr(row_zp), _stream(x.device)),
            "qquantize_rows_s8")
     return q, row_scale, row_zp
+
+
+def qquantize_rows_s8_sym(x: torch.Tensor, q=None, row_scale=None):
+    assert x.dim() == 2 and x.dtype == torch.float32 and x.stride(1) == 1
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device) if q is None else q
+    row_scale = torch.empty(M, dtype=torch.float32, device=x.device) if row_scale is None else row_scale
+    _check(_lib.qquantize_rows_s8_sym(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0),
+                                      _ptr(row_scale), _stream(x.device)),
+           "qquantize_rows_s8_sym")
+    return q, row_scale
 
 
 # ---------------------------------------------------------------- int8 GEMM

@@ -19,8 +19,9 @@
 namespace qp {
 namespace {
 
-// One workgroup per row.  kPerm writes the A8W4 operand order.
-template <bool kPerm>
+// One workgroup per row.  kPerm writes the A8W4 operand order; kSym is the
+// symmetric variant.
+template <bool kPerm, bool kSym = false>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restrict__ x,
                                                             int64_t K, int64_t ldx,
                                                             int8_t* __restrict__ q, int64_t ldq,
@@ -35,10 +36,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
   const bool dvec = (((uintptr_t)qr) & 15) == 0;
   float s;
   int32_t z;
-  quantize_row_wg<256, kPerm>(xr, K, kfill, vec, dvec, qr, red, &s, &z);
+  quantize_row_wg<256, kPerm, 16, kSym>(xr, K, kfill, vec, dvec, qr, red, &s, &z);
   if (threadIdx.x == 0) {
     row_scale[m] = s;
-    row_zp[m] = z;
+    if (row_zp) row_zp[m] = z;
   }
 }
 
@@ -70,4 +71,19 @@ extern "C" qp_status qquantize_rows_s8(const float* x, int64_t M, int64_t K, int
   if (M == 0) return QP_OK;
   QP_REQUIRE(x && q && row_scale && row_zp, QP_EINVAL, "qquantize_rows_s8: null pointer");
   return launch_quantize_rows(x, M, K, ldx, q, ldq, K, row_scale, row_zp, false, stream);
+}
+
+extern "C" qp_status qquantize_rows_s8_sym(const float* x, int64_t M, int64_t K, int64_t ldx,
+                                           int8_t* q, int64_t ldq, float* row_scale,
+                                           hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  QP_REQUIRE(M >= 0 && K >= 0, QP_EINVAL, "qquantize_rows_s8_sym: negative extent");
+  QP_REQUIRE(M <= 0x7fffffff, QP_EUNSUPPORTED, "qquantize_rows_s8_sym: M too large");
+  QP_REQUIRE(ldx >= K && ldq >= K, QP_EINVAL, "qquantize_rows_s8_sym: ldx/ldq smaller than K");
+  if (M == 0) return QP_OK;
+  QP_REQUIRE(x && q && row_scale, QP_EINVAL, "qquantize_rows_s8_sym: null pointer");
+  hipLaunchKernelGGL((quantize_rows_kernel<false, true>), dim3((unsigned)M), dim3(256), 0, stream,
+                     x, K, ldx, q, ldq, K, row_scale, (int32_t*)nullptr);
+  return check_launch("qquantize_rows_s8_sym");
 }

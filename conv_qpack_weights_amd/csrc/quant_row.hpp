@@ -70,6 +70,7 @@ __device__ __forceinline__ void params_from_range(float lo, float hi, float* s_o
   *z_out = z;
 }
 
+// (symmetric rows never reach -128: |x/s| <= 127 up to one rounding)
 __device__ __forceinline__ uint32_t quantize_one(float x, float s, int32_t z) {
   const float r = __builtin_rintf(x / s);
   // |x/s| <= 255 for in-row values, so the conversion is exact.
@@ -106,8 +107,9 @@ __device__ __forceinline__ RowFirst quantize_row_first(const float* __restrict__
 }
 
 // E: values per thread per pass (16, or 8 to spread a short row over more
-// threads).
-template <int NT, bool kChunkMajor = false, int E = 16>
+// threads).  kSym: symmetric variant -- scale = max|x| / 127 (1 for an
+// all-zero row), zero point 0, codes clamp(rint(x/scale), -127, 127).
+template <int NT, bool kChunkMajor = false, int E = 16, bool kSym = false>
 __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
                                                 int64_t kfill, bool vec, bool dst_vec,
                                                 int8_t* __restrict__ dst, float* red,
@@ -130,15 +132,25 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
                              ? pre->v[q]
                              : *reinterpret_cast<const float4*>(x + k0 + 4 * q);
         if (k0 == (int64_t)t * E) first[q] = v;
-        lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
-        hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
+        if constexpr (kSym) {
+          hi = qp_max(qp_max(qp_max(qp_max(hi, __builtin_fabsf(v.x)), __builtin_fabsf(v.y)),
+                             __builtin_fabsf(v.z)),
+                      __builtin_fabsf(v.w));
+        } else {
+          lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
+          hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
+        }
       }
     } else {
       for (int j = 0; j < E; ++j)
         if (k0 + j < K) {
           const float v = x[k0 + j];
-          lo = qp_min(lo, v);
-          hi = qp_max(hi, v);
+          if constexpr (kSym) {
+            hi = qp_max(hi, __builtin_fabsf(v));
+          } else {
+            lo = qp_min(lo, v);
+            hi = qp_max(hi, v);
+          }
         }
     }
   }
@@ -159,7 +171,13 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
   }
   float s;
   int32_t z;
-  params_from_range(lo, hi, &s, &z);
+  if constexpr (kSym) {
+    s = hi / 127.0f;
+    if (s == 0.0f) s = 1.0f;
+    z = 0;
+  } else {
+    params_from_range(lo, hi, &s, &z);
+  }
   // pass 2: codes (beyond the first E per thread, x is read again)
   for (int64_t k0 = (int64_t)t * E; k0 < kfill; k0 += NT * E) {
     uint32_t w[Q];

@@ -199,6 +199,20 @@ qp_status qquantize_rows_s8(const float* x, int64_t M, int64_t K, int64_t ldx, i
                             int64_t ldq, float* row_scale, int32_t* row_zp, hipStream_t stream);
 
 /*
+ * qquantize_rows_s8_sym -- dynamic per-row symmetric int8 quantization
+ * ([MNN] BatchSymDynamicQuant: largest magnitude per row, a scale from it,
+ * zero point 0; the page does not print the helpers' arithmetic).  Per row,
+ * f32, round half to even, no contraction:
+ *   amax = max |x|; scale = amax / 127 (an all-zero row gives scale 1);
+ *   q = clamp(rint(x/scale), -127, 127).
+ *   x  device f32 [M][ldx];  q  device int8 [M][ldq] (ldq >= K);
+ *   row_scale  device f32 [M].  The zero point is 0 for every row.
+ * Inputs must be finite.
+ */
+qp_status qquantize_rows_s8_sym(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                int64_t ldq, float* row_scale, hipStream_t stream);
+
+/*
  * qgemm_s8s8_requant -- C = requant(A x B + bias), INT8 affine operands
  * ([NPU] sections 1-5; [MNN] tileSplitFunction's post-treat parameters).
  *   acc[m,n] = sum_{k<K} (A[m,k]-zA)(B[k,n]-zB[n]) + bias[n]   (exact INT32,

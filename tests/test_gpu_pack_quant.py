@@ -132,6 +132,25 @@ def test_quantize_rows_bit_exact(qp, orc, case):
     _first_diff(_host(q), wq, "row codes")
 
 
+def _sym_rows_cases():
+    rng = np.random.default_rng(19)
+    return [synth.a8w4_gemm(16)["X"],
+            rng.standard_normal((3, 4099)).astype(np.float32) * 7,
+            np.zeros((2, 64), np.float32),
+            np.array([[127.0 / 128.0] + [(j + 0.5) / 128.0 for j in range(-127, 127)]],
+                     np.float32),
+            (rng.standard_normal((1, 1)) * 3).astype(np.float32)]
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_quantize_rows_sym_bit_exact(qp, orc, case):
+    X = _sym_rows_cases()[case]
+    q, s = qp.qquantize_rows_s8_sym(_dev(X))
+    wq, ws = orc.quantize_rows_s8_sym(X)
+    _first_diff(_host(s), ws, "sym row scale")
+    _first_diff(_host(q), wq, "sym row codes")
+
+
 def test_quantize_rows_strided_input(qp, orc):
     import torch
     rng = np.random.default_rng(10)
