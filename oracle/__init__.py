@@ -70,6 +70,7 @@ _SIGS = {
     "orc_quantize_row_s8": (None, [_P, _I64, _P, C.POINTER(_F), C.POINTER(_I32)]),
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
+    "orc_dequant_matrix_f32": (C.c_int, [_I64, _I64, _P, _F, _P, _P, _F, _F, _P]),
     "orc_a8w4_blockwise": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64,
                                      _P, _F, _F, _P, _I64]),
     "orc_packed_s8_bytes": (_I64, [_I64, _I64]),
@@ -224,6 +225,20 @@ def requant_matrix(acc, s_a, s_b, s_out, zp_out, relu):
                                   int(zp_out), int(bool(relu)), _ptr(out), C.byref(nd))
     _check(rc, "orc_requant_matrix")
     return out, nd.value
+
+
+# ---------------------------------------------------------------- O8
+def dequant_matrix_f32(acc, s_a, s_b, bias, lo, hi):
+    """O8: Y = f32(clamp(sA*sB[n]*acc + bias[n], lo, hi)), in fp64."""
+    acc = _arr(acc, np.int64)
+    M, N = acc.shape
+    sb = _arr(np.broadcast_to(np.asarray(s_b, dtype=np.float32), (N,)), np.float32)
+    bv = None if bias is None else _arr(bias, np.float32)
+    Y = np.zeros((M, N), dtype=np.float32)
+    rc = lib().orc_dequant_matrix_f32(M, N, _ptr(acc), float(s_a), _ptr(sb), _ptr(bv),
+                                      float(lo), float(hi), _ptr(Y))
+    _check(rc, "orc_dequant_matrix_f32")
+    return Y
 
 
 # ---------------------------------------------------------------- O4

@@ -299,6 +299,30 @@ int orc_requant_matrix(int64_t M, int64_t N, const int64_t* acc, float s_a, cons
 }
 
 /* ========================================================================
+ * O8 -- f32 output of the INT8 GEMM (dequantize, f32 bias, clamp).
+ * [MNN] tileSplitFunction: when the destination is not int8 the post
+ * parameters carry a float bias and f32 min/max thresholds (the Relu/Relu6
+ * post parameters) instead of the integer requantization.  Reading: the
+ * exact int32 accumulator of O1 (zero points corrected, no integer bias) is
+ * dequantized with sA*sB[n], the f32 bias is added, then clamped:
+ *   Y[m,n] = (float) clamp(sA*sB[n]*acc[m,n] + bias[n], lo, hi)
+ * formed in fp64 and rounded to f32 once.
+ * ====================================================================== */
+int orc_dequant_matrix_f32(int64_t M, int64_t N, const int64_t* acc, float s_a,
+                           const float* s_b, const float* bias, float lo, float hi, float* Y) {
+  if (M < 0 || N < 0 || !(lo <= hi)) return ORC_EINVAL;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double y = (double)s_a * (double)s_b[n] * (double)acc[m * N + n];
+      if (bias) y += (double)bias[n];
+      if (y < (double)lo) y = (double)lo;
+      if (y > (double)hi) y = (double)hi;
+      Y[m * N + n] = (float)y;
+    }
+  return 0;
+}
+
+/* ========================================================================
  * O4 -- convolution, written as direct loops (no im2col) so that it checks
  * the im2col route rather than repeating it.  [MNN] tileSplitFunction: the
  * int8 im2col fills out-of-image taps with the INPUT zero point, so a padded

@@ -246,3 +246,59 @@ def test_fp64_matmul_formulation_equals_o1(orc):
     K = 129
     acc = gemm_affine_f64(np.full((1, K), -128, np.int8), 127, np.full((1, K), 127, np.int8), -128)
     assert acc[0, 0] == -K * 65025
+
+
+# ------------------------------------------------------------------ O8
+def _f32_ulp(x):
+    x = np.float32(abs(x))
+    return float(np.nextafter(x, np.float32(np.inf)) - x)
+
+
+def test_o8_closed_form_constant_operands(orc):
+    # A == a, B == b everywhere: every accumulator is K*(a-zA)*(b-zB), and with
+    # power-of-two scales and small integers the whole f32 result is exact.
+    M, K, N = 3, 96, 5
+    a, zA, zB = 7, -3, np.array([0, 1, -2, 5, 9], np.int32)
+    A = np.full((M, K), a, np.int8)
+    B = np.full((K, N), -4, np.int8)
+    acc = orc.gemm_affine(A, zA, B, zB, None)
+    sB = np.array([0.5, 0.25, 2.0, 1.0, 0.125], np.float32)
+    bias = np.array([1.5, -2.0, 0.0, 3.25, -0.5], np.float32)
+    y = orc.dequant_matrix_f32(acc, 0.25, sB, bias, -1e30, 1e30)
+    for n in range(N):
+        want = 0.25 * float(sB[n]) * K * (a - zA) * (-4 - int(zB[n])) + float(bias[n])
+        assert (y[:, n] == np.float32(want)).all(), n
+
+
+def test_o8_rounds_once_to_nearest_f32(orc):
+    # Against the exact rational value: the fp64 intermediate keeps the result
+    # within half an f32 ulp (plus a negligible fp64 term), never a full ulp.
+    rng = np.random.default_rng(81)
+    acc = rng.integers(-(2 ** 31) + 1, 2 ** 31 - 1, size=(4, 64)).astype(np.int64)
+    sB = rng.uniform(1e-4, 1e-2, 64).astype(np.float32)
+    bias = rng.uniform(-50, 50, 64).astype(np.float32)
+    sA = np.float32(0.0123)
+    y = orc.dequant_matrix_f32(acc, sA, sB, bias, -np.inf, np.inf)
+    for m in range(4):
+        for n in range(64):
+            exact = (Fraction(float(sA)) * Fraction(float(sB[n])) * int(acc[m, n])
+                     + Fraction(float(bias[n])))
+            err = abs(Fraction(float(y[m, n])) - exact)
+            assert err <= Fraction(_f32_ulp(float(exact))) * Fraction(1, 2) * (1 + Fraction(1, 1 << 20))
+
+
+def test_o8_relu6_clamp_and_no_bias(orc):
+    acc = np.array([[-100, 0, 3, 12, 13, 1000]], np.int64)
+    y = orc.dequant_matrix_f32(acc, 0.5, 1.0, None, 0.0, 6.0)
+    assert y.tolist() == [[0.0, 0.0, 1.5, 6.0, 6.0, 6.0]]
+    # lo == hi forces every output to that value; lo > hi is rejected
+    assert (orc.dequant_matrix_f32(acc, 0.5, 1.0, None, 2.0, 2.0) == 2.0).all()
+    with pytest.raises(Exception):
+        orc.dequant_matrix_f32(acc, 0.5, 1.0, None, 3.0, 2.0)
+
+
+def test_o8_scale_and_bias_are_per_column(orc):
+    acc = np.array([[10, 10, 10], [-4, 6, 8]], np.int64)
+    y = orc.dequant_matrix_f32(acc, 1.0, np.array([1.0, 0.5, 0.25], np.float32),
+                               np.array([0.0, 1.0, -1.0], np.float32), -1e9, 1e9)
+    assert y.tolist() == [[10.0, 6.0, 1.5], [-4.0, 4.0, 1.0]]
