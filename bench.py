@@ -235,6 +235,21 @@ def main():
             "frac_mfma_peak": round(ops / ms32 / 1e9 / PEAK_INT8_TOPS, 4)}
         del C32
 
+        # f32-output variant: dequantize, f32 bias, relu6 clamp
+        Y32 = torch.empty((8192, 8192), dtype=torch.float32, device=dev)
+        bias_f = torch.linspace(-1.0, 1.0, 8192, device=dev)
+
+        def stepf():
+            qp.qgemm_s8s8_dequant_f32(A, g["sA"], g["zA"], blob, info, bias_f, 0.0, 6.0,
+                                      out=Y32, ws=ws)
+        for _ in range(3):
+            stepf()
+        msf = ev_time(stepf, 20)
+        workloads["int8_gemm_8192_f32_out_relu6"] = {
+            "ms": round(msf, 4), "TOPS": round(ops / msf / 1e9, 1),
+            "frac_mfma_peak": round(ops / msf / 1e9 / PEAK_INT8_TOPS, 4)}
+        del Y32
+
         # A8W4 GEMV, M=1, K=N=4096: cold (rotating weight copies) and warm
         gv = synth.a8w4_gemv()
         Wd, swd = d(gv["W"]), d(gv["sw"])

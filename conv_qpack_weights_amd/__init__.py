@@ -69,6 +69,8 @@ SIGNATURES = {
     "qgemm_s8s8_requant_ws_size": (C.c_int, [_QT, _PI, _SZ]),
     "qgemm_s8s8_requant": (C.c_int, [_QT, _P, _PI, _P, _P, _I64, _QT, _I32, _P, _P, C.c_size_t,
                                      _P]),
+    "qgemm_s8s8_dequant_f32": (C.c_int, [_QT, _P, _PI, _P, _P, _F, _F, _P, _I64, _P,
+                                         C.c_size_t, _P]),
     "qgemm_a8w4_blockwise_f32_ws_size": (C.c_int, [_I64, _PI, _SZ]),
     "qgemm_a8w4_blockwise_f32": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P, _I64,
                                            _P, C.c_size_t, _P]),
@@ -247,6 +249,25 @@ def qgemm_s8s8_requant(A: torch.Tensor, sA: float, zA: int, blob: torch.Tensor, 
                                    _ptr(bias), int(max_abs_bias), C.byref(o_desc), int(bool(relu)),
                                    _ptr(out), _ptr(ws), ws.numel(), _stream(A.device)),
            "qgemm_s8s8_requant")
+    return out
+
+
+def qgemm_s8s8_dequant_f32(A: torch.Tensor, sA: float, zA: int, blob: torch.Tensor,
+                           info: PackedInfo, bias=None, clamp_lo=-float("inf"),
+                           clamp_hi=float("inf"), out=None, ws=None):
+    """Y[M,N] = clamp(sA*sB[n]*(A-zA)@(B-zB) + bias, lo, hi) in f32."""
+    assert A.dtype == torch.int8 and A.dim() == 2 and A.stride(1) == 1
+    M, K = A.shape
+    a_desc = qtensor(QP_S8, [M, K], [A.stride(0), 1], scale=sA, zero_point=zA)
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=A.device)
+    assert out.dtype == torch.float32 and out.stride(1) == 1
+    if ws is None:
+        ws = _alloc_bytes(qgemm_s8s8_requant_ws_size(a_desc, info), A.device)
+    _check(_lib.qgemm_s8s8_dequant_f32(C.byref(a_desc), _ptr(A), C.byref(info), _ptr(blob),
+                                       _ptr(bias), clamp_lo, clamp_hi, _ptr(out), out.stride(0),
+                                       _ptr(ws), ws.numel(), _stream(A.device)),
+           "qgemm_s8s8_dequant_f32")
     return out
 
 

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kHi>
+template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kHi,
+          bool kF32>
 qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (int32_t)ceil_div(a.M, BM);
@@ -88,7 +89,7 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   if (blocks == 0) return QP_OK;
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
   const size_t lds = (size_t)SA * BM * BK;
-  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi>;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32>;
   static bool lds_attr_set = false;  // once per instantiation; repeating it is harmless
   if (!lds_attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -100,15 +101,15 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   return check_launch("qgemm_s8s8 kernel");
 }
 
-template <bool kOut32, bool kRowSum, bool kHi>
+template <bool kOut32, bool kRowSum, bool kHi, bool kF32 = false>
 qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
   const bool k128 = (a.Kpad % 128) == 0;
   const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (k128 && big_tiles >= 256)
-    return launch_cfg<256, 256, 128, 4, 4, 32, kOut32, kRowSum, kHi>(a, stream);
+    return launch_cfg<256, 256, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
   if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
-    return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi>(a, stream);
-  return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi>(a, stream);
+    return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
+  return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi, kF32>(a, stream);
 }
 
 }  // namespace
@@ -146,7 +147,8 @@ static GemmPlan plan_gemm(int64_t M, int64_t K, int64_t lda, const void* A,
 qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t zA,
                       const qp_packed_info* b, const void* packedB, const int32_t* bias,
                       float sOut, int32_t zp_out, bool out32, int32_t relu, void* C, int64_t ldc,
-                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream) {
+                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream,
+                      const GemmF32Out* f32) {
   const uint8_t* blob = static_cast<const uint8_t*>(packedB);
   GemmPlan p = plan_gemm(M, b->K, lda, A, b);
   if (a_is_padded) {
@@ -192,6 +194,13 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
   a.hi = 127;
   a.C = C;
   a.ldc = ldc;
+  if (f32) {
+    a.bias_f = f32->bias;
+    a.clo = f32->lo;
+    a.chi = f32->hi;
+    return p.rowsum ? launch_gemm_sel<true, true, false, true>(a, stream)
+                    : launch_gemm_sel<true, false, false, true>(a, stream);
+  }
   if (out32)
     return p.rowsum ? launch_gemm_sel<true, true, false>(a, stream)
                     : launch_gemm_sel<true, false, false>(a, stream);
@@ -287,5 +296,40 @@ extern "C" qp_status qgemm_s8s8_requant(const qp_qtensor* a, const int8_t* A,
              "qgemm: output must be row-major with ldc >= N");
   QP_REQUIRE(M == 0 || (A && packedB_dev && C), QP_EINVAL, "qgemm: null data pointer");
   return run_gemm_s8(A, M, lda, a->scale, a->zero_point, b, packedB_dev, bias_dev, out->scale,
-                     out->zero_point, out32, relu, C, out->stride[0], ws, ws_bytes, false, stream);
+                     out->zero_point, out32, relu, C, out->stride[0], ws, ws_bytes, false, stream,
+                     nullptr);
+}
+
+extern "C" qp_status qgemm_s8s8_dequant_f32(const qp_qtensor* a, const int8_t* A,
+                                            const qp_packed_info* b, const void* packedB_dev,
+                                            const float* bias_dev, float clamp_lo,
+                                            float clamp_hi, float* Y, int64_t ldy, void* ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  QP_REQUIRE(a && b, QP_EINVAL, "qgemm_f32: null descriptor");
+  QP_REQUIRE(a->dtype == QP_S8 && a->rank == 2, QP_EINVAL, "qgemm_f32: A must be rank-2 QP_S8");
+  QP_REQUIRE(a->scheme == QP_PER_TENSOR, QP_EUNSUPPORTED, "qgemm_f32: A must be per-tensor");
+  QP_REQUIRE(a->stride[1] == 1, QP_EUNSUPPORTED,
+             "qgemm_f32: A must be K-contiguous (stride[1] == 1)");
+  QP_REQUIRE(a->rounding == QP_ROUND_HALF_EVEN, QP_EUNSUPPORTED,
+             "qgemm_f32: only round-half-to-even is implemented");
+  const int64_t M = a->shape[0], K = a->shape[1], lda = a->stride[0];
+  QP_REQUIRE(M >= 0 && K > 0 && lda >= K, QP_EINVAL, "qgemm_f32: bad A shape/stride");
+  QP_REQUIRE(b->format == 1, QP_EINVAL, "qgemm_f32: weights must be an int8 blob");
+  QP_REQUIRE(K == b->K, QP_EINVAL, "qgemm_f32: activation K=%lld but the weights have K=%lld",
+             (long long)K, (long long)b->K);
+  QP_REQUIRE(a->zero_point >= -128 && a->zero_point <= 127, QP_EINVAL,
+             "qgemm_f32: activation zero point outside int8");
+  QP_REQUIRE(std::isfinite(a->scale) && a->scale > 0, QP_EINVAL,
+             "qgemm_f32: activation scale must be > 0");
+  QP_REQUIRE(K <= INT64_C(2147483647) / 65025, QP_EOVERFLOW,
+             "qgemm_f32: K*65025 = %lld exceeds INT32", (long long)(K * 65025));
+  QP_REQUIRE(!(clamp_lo > clamp_hi) && !std::isnan(clamp_lo) && !std::isnan(clamp_hi), QP_EINVAL,
+             "qgemm_f32: clamp bounds must satisfy lo <= hi");
+  QP_REQUIRE(ldy >= b->N, QP_EINVAL, "qgemm_f32: ldy smaller than N");
+  QP_REQUIRE(M == 0 || (A && packedB_dev && Y), QP_EINVAL, "qgemm_f32: null data pointer");
+  const GemmF32Out f32{bias_dev, clamp_lo, clamp_hi};
+  return run_gemm_s8(A, M, lda, a->scale, a->zero_point, b, packedB_dev, nullptr, 1.0f, 0, true, 0,
+                     Y, ldy, ws, ws_bytes, false, stream, &f32);
 }

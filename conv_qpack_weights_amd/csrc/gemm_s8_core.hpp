@@ -39,6 +39,8 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
   int32_t group_m;   // tile rows per raster group
   int32_t xcd_remap; // 1: give each XCD a contiguous range of the raster order
+  const float* bias_f;  // f32 output: [N] or null, added after dequantization
+  float clo, chi;       // f32 output: clamp bounds
 };
 
 
@@ -205,7 +207,9 @@ __device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
 //  * B (the packed weights, 32x32 sub-tiles) goes straight into VGPRs in
 //    MFMA operand order, one tile ahead: each wave owns BN/NW columns, so no
 //    B byte is loaded twice and LDS only carries A.
-template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kShiftHi>
+// kF32 (with kOut32): f32 output y = clamp(sA*sB[n]*acc + bias_f[n], clo, chi).
+template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kShiftHi,
+          bool kF32 = false>
 __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   constexpr int CH = BK / 16;  // 16-byte chunks per A tile row
   constexpr int TM = BM;       // every wave covers all rows of the tile
@@ -222,6 +226,7 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   static_assert(BM * CH % (64 * NW) == 0, "A tile must split evenly over the waves");
   static_assert(TN % MF == 0 && TM % MF == 0 && BK % KSTEP == 0, "tile shape");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(!kF32 || kOut32, "f32 output uses the 4-byte store paths");
   static_assert(SA >= 2 && (SA - 2) * IA + IB < 64, "vmcnt range");
 
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
@@ -309,7 +314,13 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     const int64_t n = n0 + j;
     int32_t mm = 0, ss = 63, cc = 0, zb = 0;
     if (n < g.N) {
-      derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
+      if constexpr (kF32) {
+        // f32 output: the columns hold the dequantization scale and the bias
+        mm = __builtin_bit_cast(int32_t, (float)((double)g.sA * (double)g.sB[n]));
+        ss = __builtin_bit_cast(int32_t, g.bias_f ? g.bias_f[n] : 0.0f);
+      } else {
+        derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
+      }
       zb = g.zpB[n];
       uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
       c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
@@ -417,7 +428,15 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     for (int r = 0; r < 4; ++r) {
       uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
       if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
-      if constexpr (kOut32) {
+      if constexpr (kF32) {
+        // (bit_cast of a vector element would read element 0: copy it out first)
+        const int32_t mr = mm[r], sr = ss[r];
+        float y = __builtin_fmaf(__builtin_bit_cast(float, mr), (float)(int32_t)a,
+                                 __builtin_bit_cast(float, sr));
+        y = y < g.clo ? g.clo : y;
+        y = y > g.chi ? g.chi : y;
+        out[r] = __builtin_bit_cast(int32_t, y);
+      } else if constexpr (kOut32) {
         out[r] = (int32_t)a;
       } else if constexpr (kShiftHi) {
         out[r] = clamp_i32(rhe_shift_hi((int32_t)a, mm[r], half[r], s2[r], mask[r]) + g.zp_out,
@@ -439,9 +458,15 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     if (kRowSum) *zb = *reinterpret_cast<const v4i*>(&col_zb[jn]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s2[r] = (*ss)[r] - 32;
-      half[r] = (int64_t)1 << ((*ss)[r] - 1);
-      mask[r] = (1u << (s2[r] & 31)) - 1u;
+      if constexpr (kF32) {  // (the shift slots hold the f32 bias)
+        s2[r] = 0;
+        half[r] = 0;
+        mask[r] = 0;
+      } else {
+        s2[r] = (*ss)[r] - 32;
+        half[r] = (int64_t)1 << ((*ss)[r] - 1);
+        mask[r] = (1u << (s2[r] & 31)) - 1u;
+      }
     }
   };
 

@@ -74,9 +74,15 @@ qp_status launch_im2col(const int8_t* X, int64_t NB, int64_t H, int64_t W, int64
 qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
                         const int32_t* bias, int64_t max_abs_bias, const qp_qtensor* out,
                         bool* out32);
+// f32 output of the INT8 GEMM: y = clamp(sA*sB[n]*acc + bias[n], lo, hi).
+struct GemmF32Out {
+  const float* bias;  // device f32 [N] or null
+  float lo, hi;
+};
 qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t zA,
                       const qp_packed_info* b, const void* packedB, const int32_t* bias,
                       float sOut, int32_t zp_out, bool out32, int32_t relu, void* C, int64_t ldc,
-                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream);
+                      void* ws, size_t ws_bytes, bool a_is_padded, hipStream_t stream,
+                      const GemmF32Out* f32 = nullptr);
 
 }  // namespace qp

@@ -247,6 +247,29 @@ qp_status qgemm_s8s8_requant(const qp_qtensor* a, const int8_t* A, const qp_pack
                              void* C, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qgemm_s8s8_dequant_f32 -- Y = clamp(sA*sB[n]*acc + bias[n], lo, hi) in f32
+ * ([NPU] sections 1-4 for the exact accumulator; [MNN] tileSplitFunction's
+ * post parameters for a float destination: float bias added after the
+ * dequantization, then the f32 min/max thresholds, e.g. 0/6 for Relu6).
+ *   acc[m,n] = sum_{k<K} (A[m,k]-zA)(B[k,n]-zB[n])   (exact INT32)
+ *   y        = fmaf(f32(sA*sB[n]), f32(acc), bias[n]), then clamped.
+ *   a        QP_S8 [M,K], stride (lda, 1), per-tensor scale and zero point.
+ *   b, packedB_dev  an int8 blob from qpack_weights (K must match).
+ *   bias_dev f32 [N] in output units, or NULL (no bias).
+ *   clamp_lo, clamp_hi  f32 bounds, lo <= hi (use -FLT_MAX/FLT_MAX or
+ *            +-inf for no clamp).
+ *   Y        device f32 [M][ldy], ldy >= N.
+ *   ws, ws_bytes  workspace sized by qgemm_s8s8_requant_ws_size (same plan).
+ * The result is within a few f32 ulps of the exactly rounded value.
+ * Errors: QP_EOVERFLOW when K*65025 > 2^31-1; QP_EINVAL on bad shapes,
+ *   NaN or reversed bounds.
+ */
+qp_status qgemm_s8s8_dequant_f32(const qp_qtensor* a, const int8_t* A, const qp_packed_info* b,
+                                 const void* packedB_dev, const float* bias_dev, float clamp_lo,
+                                 float clamp_hi, float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
  * qgemm_a8w4_blockwise_f32 -- Y = clamp(deq(qa) x deq(W)^T + bias, lo, hi)
  * with dynamically quantized int8 activations and int4 group weights
  * ([KLEIDI] matmul_clamp_f32_qai8dxp_qsi4c32p: f32 out, clamp, per-row int8
