@@ -64,9 +64,9 @@ _SIGS = {
     "orc_ideal_rhe": (_I64, [_I64, _D]),
     "orc_requant_matrix": (C.c_int, [_I64, _I64, _P, _F, _P, _F, _I32, _I32, _P, C.POINTER(_I64)]),
     "orc_conv2d_direct": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I32, _I64, _I64, _I64, _P, _I64,
-                                    _I64, _I64, _I64, _I64, _I64, _P, _P]),
+                                    _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P]),
     "orc_im2col": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I32, _I64, _I64, _I64, _I64, _I64, _I64,
-                             _I64, _I64, _P]),
+                             _I64, _I64, _I64, _I64, _P]),
     "orc_quantize_row_s8": (None, [_P, _I64, _P, C.POINTER(_F), C.POINTER(_I32)]),
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
@@ -242,32 +242,36 @@ def dequant_matrix_f32(acc, s_a, s_b, bias, lo, hi):
 
 
 # ---------------------------------------------------------------- O4
-def conv2d_direct(X, zp_in, Wt, stride=(1, 1), pad=(0, 0, 0, 0), bias=None):
+def conv_out_dims(H, W, KH, KW, stride=(1, 1), pad=(0, 0, 0, 0), dilation=(1, 1)):
+    OH = (H + pad[0] + pad[2] - (dilation[0] * (KH - 1) + 1)) // stride[0] + 1
+    OW = (W + pad[1] + pad[3] - (dilation[1] * (KW - 1) + 1)) // stride[1] + 1
+    return OH, OW
+
+
+def conv2d_direct(X, zp_in, Wt, stride=(1, 1), pad=(0, 0, 0, 0), bias=None, dilation=(1, 1)):
     """X: int8 NHWC; Wt: int8 OIHW; pad = (top, left, bottom, right)."""
     X = _arr(X, np.int8)
     Wt = _arr(Wt, np.int8)
     NB, H, W, Cc = X.shape
     OC, IC, KH, KW = Wt.shape
     assert IC == Cc
-    OH = (H + pad[0] + pad[2] - KH) // stride[0] + 1
-    OW = (W + pad[1] + pad[3] - KW) // stride[1] + 1
+    OH, OW = conv_out_dims(H, W, KH, KW, stride, pad, dilation)
     out = np.zeros((NB, OH, OW, OC), dtype=np.int64)
     biasv = None if bias is None else _arr(bias, np.int32)
     rc = lib().orc_conv2d_direct(NB, H, W, Cc, _ptr(X), int(zp_in), OC, KH, KW, _ptr(Wt),
                                  stride[0], stride[1], pad[0], pad[1], pad[2], pad[3],
-                                 _ptr(biasv), _ptr(out))
+                                 dilation[0], dilation[1], _ptr(biasv), _ptr(out))
     _check(rc, "orc_conv2d_direct")
     return out
 
 
-def im2col(X, pad_value, KH, KW, stride=(1, 1), pad=(0, 0, 0, 0)):
+def im2col(X, pad_value, KH, KW, stride=(1, 1), pad=(0, 0, 0, 0), dilation=(1, 1)):
     X = _arr(X, np.int8)
     NB, H, W, Cc = X.shape
-    OH = (H + pad[0] + pad[2] - KH) // stride[0] + 1
-    OW = (W + pad[1] + pad[3] - KW) // stride[1] + 1
+    OH, OW = conv_out_dims(H, W, KH, KW, stride, pad, dilation)
     col = np.zeros((NB * OH * OW, KH * KW * Cc), dtype=np.int8)
     rc = lib().orc_im2col(NB, H, W, Cc, _ptr(X), int(pad_value), KH, KW, stride[0], stride[1],
-                          pad[0], pad[1], pad[2], pad[3], _ptr(col))
+                          pad[0], pad[1], pad[2], pad[3], dilation[0], dilation[1], _ptr(col))
     _check(rc, "orc_im2col")
     return col
 

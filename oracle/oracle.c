@@ -328,14 +328,18 @@ int orc_dequant_matrix_f32(int64_t M, int64_t N, const int64_t* acc, float s_a,
  * int8 im2col fills out-of-image taps with the INPUT zero point, so a padded
  * tap stands for real zero.  [MNN] reorderWeight: source weights are
  * [oc, ic, kh*kw] (OIHW).  The convolution zero-point-corrects the input
- * only; the weights are symmetric (zero point 0).
+ * only; the weights are symmetric (zero point 0).  Dilation (the pages show
+ * none; reading: the usual definition) places tap (ky, kx) at input offset
+ * (ky*dil_h, kx*dil_w); dilation 1 is the plain convolution.
  * ====================================================================== */
 static int orc_conv_out_dims(int64_t H, int64_t W, int64_t KH, int64_t KW, int64_t sh,
                              int64_t sw, int64_t pt, int64_t pl, int64_t pb, int64_t pr,
-                             int64_t* OH, int64_t* OW) {
-  if (sh <= 0 || sw <= 0 || KH <= 0 || KW <= 0 || pt < 0 || pl < 0 || pb < 0 || pr < 0)
+                             int64_t dh, int64_t dw, int64_t* OH, int64_t* OW) {
+  if (sh <= 0 || sw <= 0 || KH <= 0 || KW <= 0 || pt < 0 || pl < 0 || pb < 0 || pr < 0 ||
+      dh <= 0 || dw <= 0)
     return ORC_EINVAL;
-  int64_t hh = H + pt + pb - KH, ww = W + pl + pr - KW;
+  /* a dilated kernel spans d*(k-1)+1 input pixels */
+  int64_t hh = H + pt + pb - (dh * (KH - 1) + 1), ww = W + pl + pr - (dw * (KW - 1) + 1);
   if (hh < 0 || ww < 0) return ORC_EINVAL;
   *OH = hh / sh + 1;
   *OW = ww / sw + 1;
@@ -345,10 +349,11 @@ static int orc_conv_out_dims(int64_t H, int64_t W, int64_t KH, int64_t KW, int64
 int orc_conv2d_direct(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X,
                       int32_t zp_in, int64_t OC, int64_t KH, int64_t KW, const int8_t* Wt,
                       int64_t stride_h, int64_t stride_w, int64_t pad_t, int64_t pad_l,
-                      int64_t pad_b, int64_t pad_r, const int32_t* bias, int64_t* acc) {
+                      int64_t pad_b, int64_t pad_r, int64_t dil_h, int64_t dil_w,
+                      const int32_t* bias, int64_t* acc) {
   int64_t OH, OW;
-  int rc = orc_conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r,
-                             &OH, &OW);
+  int rc = orc_conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, dil_h,
+                             dil_w, &OH, &OW);
   if (rc) return rc;
   rc = 0;
   for (int64_t b = 0; b < NB; ++b)
@@ -358,8 +363,8 @@ int orc_conv2d_direct(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t*
           int64_t s = 0;
           for (int64_t ky = 0; ky < KH; ++ky)
             for (int64_t kx = 0; kx < KW; ++kx) {
-              int64_t iy = oy * stride_h + ky - pad_t;
-              int64_t ix = ox * stride_w + kx - pad_l;
+              int64_t iy = oy * stride_h + ky * dil_h - pad_t;
+              int64_t ix = ox * stride_w + kx * dil_w - pad_l;
               int inside = iy >= 0 && iy < H && ix >= 0 && ix < W;
               for (int64_t ic = 0; ic < C; ++ic) {
                 int64_t xv = inside ? X[((b * H + iy) * W + ix) * C + ic] : zp_in;
@@ -378,10 +383,11 @@ int orc_conv2d_direct(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t*
  * input channel inner, the K order of [MNN] reorderWeight. */
 int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int32_t pad_value,
                int64_t KH, int64_t KW, int64_t stride_h, int64_t stride_w, int64_t pad_t,
-               int64_t pad_l, int64_t pad_b, int64_t pad_r, int8_t* col) {
+               int64_t pad_l, int64_t pad_b, int64_t pad_r, int64_t dil_h, int64_t dil_w,
+               int8_t* col) {
   int64_t OH, OW;
-  int rc = orc_conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r,
-                             &OH, &OW);
+  int rc = orc_conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, dil_h,
+                             dil_w, &OH, &OW);
   if (rc) return rc;
   int64_t Kc = KH * KW * C;
   for (int64_t b = 0; b < NB; ++b)
@@ -391,8 +397,8 @@ int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int
         for (int64_t ky = 0; ky < KH; ++ky)
           for (int64_t kx = 0; kx < KW; ++kx)
             for (int64_t ic = 0; ic < C; ++ic) {
-              int64_t iy = oy * stride_h + ky - pad_t;
-              int64_t ix = ox * stride_w + kx - pad_l;
+              int64_t iy = oy * stride_h + ky * dil_h - pad_t;
+              int64_t ix = ox * stride_w + kx * dil_w - pad_l;
               int inside = iy >= 0 && iy < H && ix >= 0 && ix < W;
               col[m * Kc + (ky * KW + kx) * C + ic] =
                   inside ? X[((b * H + iy) * W + ix) * C + ic] : (int8_t)pad_value;

@@ -75,10 +75,12 @@ int orc_requant_matrix(int64_t M, int64_t N, const int64_t* acc, float s_a,
 int orc_conv2d_direct(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X,
                       int32_t zp_in, int64_t OC, int64_t KH, int64_t KW, const int8_t* Wt,
                       int64_t stride_h, int64_t stride_w, int64_t pad_t, int64_t pad_l,
-                      int64_t pad_b, int64_t pad_r, const int32_t* bias, int64_t* acc);
+                      int64_t pad_b, int64_t pad_r, int64_t dil_h, int64_t dil_w,
+                      const int32_t* bias, int64_t* acc);
 int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int32_t pad_value,
                int64_t KH, int64_t KW, int64_t stride_h, int64_t stride_w, int64_t pad_t,
-               int64_t pad_l, int64_t pad_b, int64_t pad_r, int8_t* col);
+               int64_t pad_l, int64_t pad_b, int64_t pad_r, int64_t dil_h, int64_t dil_w,
+               int8_t* col);
 
 /* ---- O5: dynamic per-row asymmetric int8 quantization (f32) ------------- */
 void orc_quantize_row_s8(const float* x, int64_t K, int8_t* q, float* scale, int32_t* zp);

@@ -27,6 +27,7 @@ def _rand_i8(rng, shape, lo=-128, hi=127):
     dict(NB=1, H=7, W=6, C=5, OC=4, KH=3, KW=3, stride=(1, 1), pad=(1, 1, 1, 1)),
     dict(NB=2, H=9, W=8, C=3, OC=6, KH=3, KW=2, stride=(2, 1), pad=(0, 1, 2, 0)),
     dict(NB=1, H=5, W=5, C=8, OC=3, KH=1, KW=1, stride=(1, 1), pad=(0, 0, 0, 0)),
+    dict(NB=2, H=11, W=10, C=4, OC=5, KH=3, KW=3, stride=(1, 2), pad=(2, 1, 2, 3), dil=(2, 3)),
 ])
 def test_o4_direct_equals_im2col_gemm(orc, case):
     rng = np.random.default_rng(11)
@@ -34,8 +35,9 @@ def test_o4_direct_equals_im2col_gemm(orc, case):
     Wt = _rand_i8(rng, (case["OC"], case["C"], case["KH"], case["KW"]), -127, 127)
     bias = rng.integers(-1000, 1001, case["OC"]).astype(np.int32)
     zp = 7
-    direct = orc.conv2d_direct(X, zp, Wt, case["stride"], case["pad"], bias)
-    col = orc.im2col(X, zp, case["KH"], case["KW"], case["stride"], case["pad"])
+    dil = case.get("dil", (1, 1))
+    direct = orc.conv2d_direct(X, zp, Wt, case["stride"], case["pad"], bias, dil)
+    col = orc.im2col(X, zp, case["KH"], case["KW"], case["stride"], case["pad"], dil)
     Bnk = Wt.transpose(0, 2, 3, 1).reshape(case["OC"], -1)   # K order (ky, kx, ic)
     acc = orc.gemm_affine(col, zp, Bnk, 0, bias, b_is_nk=True)
     assert np.array_equal(direct.reshape(-1, case["OC"]), acc)
@@ -77,6 +79,34 @@ def test_o4_pad_value_only_matters_on_the_border(orc):
     assert np.array_equal(a_good[1:-1, 1:-1], a_bad[1:-1, 1:-1])
     assert not np.array_equal(a_good[0], a_bad[0])
     assert np.array_equal(a_good, orc.conv2d_direct(X, zp, Wt, (1, 1), (1, 1, 1, 1))[0])
+
+
+@pytest.mark.parametrize("dil,stride,pad", [((2, 2), (1, 1), (2, 2, 2, 2)),
+                                             ((3, 1), (2, 1), (1, 0, 3, 2)),
+                                             ((1, 4), (1, 3), (0, 4, 0, 4))])
+def test_o4_dilation_is_a_zero_inserted_kernel(orc, dil, stride, pad):
+    """A kernel dilated by d equals the undilated kernel of size d*(k-1)+1
+    that holds the taps at multiples of d and zeros between (symmetric
+    weights: a zero weight adds nothing, whatever the input)."""
+    rng = np.random.default_rng(15)
+    X = _rand_i8(rng, (2, 12, 13, 3))
+    Wt = _rand_i8(rng, (4, 3, 3, 2), -127, 127)
+    bias = rng.integers(-1000, 1001, 4).astype(np.int32)
+    big = np.zeros((4, 3, dil[0] * 2 + 1, dil[1] * 1 + 1), np.int8)
+    big[:, :, ::dil[0], ::dil[1]] = Wt
+    got = orc.conv2d_direct(X, -9, Wt, stride, pad, bias, dil)
+    want = orc.conv2d_direct(X, -9, big, stride, pad, bias)
+    assert got.shape == want.shape and np.array_equal(got, want)
+    OH, OW = orc.conv_out_dims(12, 13, 3, 2, stride, pad, dil)
+    assert got.shape == (2, OH, OW, 4)
+
+
+def test_o4_dilation_rejects_kernels_larger_than_the_input(orc):
+    X = np.zeros((1, 4, 4, 1), np.int8)
+    Wt = np.ones((1, 1, 3, 3), np.int8)
+    orc.conv2d_direct(X, 0, Wt, dilation=(1, 1))
+    with pytest.raises(Exception):
+        orc.conv2d_direct(X, 0, Wt, dilation=(2, 2))   # spans 5 > 4 rows
 
 
 # ------------------------------------------------------------------ O5
