@@ -349,15 +349,50 @@ def main():
         Xc, bic = d(c["X"]), d(c["bias"])
         Yc = torch.empty((1, 56, 56, 64), dtype=torch.int8, device=dev)
 
+        wsc = torch.empty(3136 * 576 + 4096, dtype=torch.uint8, device=dev)
+
         def conv():
             qp.qconv2d_s8_im2col(Xc, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"],
-                                 bic, 1000, c["s_out"], c["zp_out"], True, out=Yc)
+                                 bic, 1000, c["s_out"], c["zp_out"], True, out=Yc, ws=wsc)
+
+        def conv_implicit():
+            qp.qconv2d_s8(Xc, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"], (1, 1),
+                          bic, 1000, c["s_out"], c["zp_out"], True, out=Yc, ws=wsc)
         msc = graph_time(conv, 50)
+        msci = graph_time(conv_implicit, 50)
         copsn = 2.0 * 3136 * 64 * 576
         workloads["conv3x3_56x56x64_to_64"] = {
             "us": round(msc * 1e3, 2), "TOPS": round(copsn / msc / 1e9, 2),
             "frac_mfma_peak": round(copsn / msc / 1e9 / PEAK_INT8_TOPS, 5),
             "note": "im2col + GEMM launches; latency-bound at this size"}
+        workloads["conv3x3_56x56x64_to_64_implicit"] = {
+            "us": round(msci * 1e3, 2), "TOPS": round(copsn / msci / 1e9, 2),
+            "frac_mfma_peak": round(copsn / msci / 1e9 / PEAK_INT8_TOPS, 5),
+            "note": "one implicit-GEMM launch (no im2col matrix); latency-bound at this size"}
+        # the same layer at batch 32: throughput of both routes
+        cb = synth.conv3x3_nhwc(NB=32)
+        Xb = d(cb["X"])
+        Yb = torch.empty((32, 56, 56, 64), dtype=torch.int8, device=dev)
+        wsb = torch.empty(32 * 3136 * 576 + 65536, dtype=torch.uint8, device=dev)
+
+        def conv_b_explicit():
+            qp.qconv2d_s8_im2col(Xb, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"],
+                                 bic, 1000, c["s_out"], c["zp_out"], True, out=Yb, ws=wsb)
+
+        def conv_b_implicit():
+            qp.qconv2d_s8(Xb, c["s_in"], c["zp_in"], bc, ic, 3, 3, c["stride"], c["pad"], (1, 1),
+                          bic, 1000, c["s_out"], c["zp_out"], True, out=Yb, ws=wsb)
+        for f in (conv_b_explicit, conv_b_implicit):
+            f()
+        mse = ev_time(conv_b_explicit, 20)
+        msi = ev_time(conv_b_implicit, 20)
+        copsb = 32 * copsn
+        workloads["conv3x3_b32_56x56x64_to_64"] = {
+            "explicit_us": round(mse * 1e3, 2), "implicit_us": round(msi * 1e3, 2),
+            "TOPS_explicit": round(copsb / mse / 1e9, 1),
+            "TOPS_implicit": round(copsb / msi / 1e9, 1),
+            "frac_mfma_peak_implicit": round(copsb / msi / 1e9 / PEAK_INT8_TOPS, 4)}
+        del Xb, Yb, wsb
 
         # 130x70x129 per-tensor GEMM (the worked example's shape)
         s = synth.gemm_affine_per_tensor()

@@ -82,6 +82,10 @@ SIGNATURES = {
                                             _I32, _SZ]),
     "qconv2d_s8_im2col": (C.c_int, [_QT, _P, _PI, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                     _I32, _P, _I64, _QT, _I32, _P, _P, C.c_size_t, _P]),
+    "qconv2d_s8_ws_size": (C.c_int, [_QT, _PI, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                     _I32, _I32, _SZ]),
+    "qconv2d_s8": (C.c_int, [_QT, _P, _PI, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                             _I32, _I32, _P, _I64, _QT, _I32, _P, _P, C.c_size_t, _P]),
 }
 
 
@@ -346,4 +350,33 @@ def qconv2d_s8_im2col(X: torch.Tensor, s_in: float, zp_in: int, blob: torch.Tens
                                   _ptr(bias), int(max_abs_bias), C.byref(y_desc), int(bool(relu)),
                                   _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)),
            "qconv2d_s8_im2col")
+    return out
+
+
+def qconv2d_s8(X: torch.Tensor, s_in: float, zp_in: int, blob: torch.Tensor, info: PackedInfo,
+               KH: int, KW: int, stride=(1, 1), pad=(0, 0, 0, 0), dilation=(1, 1), bias=None,
+               max_abs_bias=0, s_out=1.0, zp_out=0, relu=False, out_dtype="s8", out=None,
+               ws=None):
+    """General INT8 NHWC convolution: implicit GEMM when C % 16 == 0, the GEMM
+    itself for a 1x1/stride-1/unpadded kernel, explicit im2col otherwise."""
+    NB, H, W, Cc = X.shape
+    OH = (H + pad[0] + pad[2] - (dilation[0] * (KH - 1) + 1)) // stride[0] + 1
+    OW = (W + pad[1] + pad[3] - (dilation[1] * (KW - 1) + 1)) // stride[1] + 1
+    x_desc = qtensor(QP_S8, [NB, H, W, Cc], scale=s_in, zero_point=zp_in)
+    tdt = torch.int8 if out_dtype == "s8" else torch.int32
+    if out is None:
+        out = torch.empty((NB, OH, OW, info.N), dtype=tdt, device=X.device)
+    y_desc = qtensor(QP_S8 if out_dtype == "s8" else QP_S32, [NB, OH, OW, info.N], scale=s_out,
+                     zero_point=zp_out)
+    geom = (KH, KW, stride[0], stride[1], pad[0], pad[1], pad[2], pad[3], dilation[0],
+            dilation[1])
+    if ws is None:
+        n = C.c_size_t()
+        _check(_lib.qconv2d_s8_ws_size(C.byref(x_desc), C.byref(info), *geom, C.byref(n)),
+               "qconv2d_s8_ws_size")
+        ws = _alloc_bytes(n.value, X.device)
+    _check(_lib.qconv2d_s8(C.byref(x_desc), _ptr(X), C.byref(info), _ptr(blob), *geom,
+                           _ptr(bias), int(max_abs_bias), C.byref(y_desc), int(bool(relu)),
+                           _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)),
+           "qconv2d_s8")
     return out

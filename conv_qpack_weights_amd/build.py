@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqpack.so")
 SOURCES = ["status.cpp", "pack.hip", "quant.hip", "im2col.hip", "gemm_s8.hip", "conv.hip",
-           "a8w4.hip"]
+           "conv_implicit.hip", "a8w4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -27,8 +27,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 
 # Per-file code-generation options.  The A8W4 kernels rescale every MFMA
-# result on the VALU right away, so their MFMAs write VGPRs (no AGPR copy).
-EXTRA = {"a8w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# result on the VALU right away, and the implicit-GEMM convolution keeps
+# few accumulators, so their MFMAs write VGPRs (no AGPR copies).
+EXTRA = {"a8w4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+         "conv_implicit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _compile(src: str, obj: str) -> None:

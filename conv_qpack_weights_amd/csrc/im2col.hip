@@ -16,7 +16,7 @@ namespace {
 
 struct ConvGeom {
   int64_t NB, H, W, C, OH, OW, K;
-  int32_t KH, KW, sh, sw, pt, pl;
+  int32_t KH, KW, sh, sw, pt, pl, dh, dw;
 };
 
 // Each thread writes one 16-byte chunk of one im2col row.
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void im2col_kernel(const int8_t* __restrict__ 
     if (k0 < g.K) {
       const int64_t tap = k0 / g.C, ic = k0 - tap * g.C;
       const int64_t ky = tap / g.KW, kx = tap - ky * g.KW;
-      const int64_t iy = oy * g.sh + ky - g.pt, ix = ox * g.sw + kx - g.pl;
+      const int64_t iy = oy * g.sh + ky * g.dh - g.pt, ix = ox * g.sw + kx * g.dw - g.pl;
       if (iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
         v = *reinterpret_cast<const uint4*>(X + ((b * g.H + iy) * g.W + ix) * g.C + ic);
       else
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void im2col_kernel(const int8_t* __restrict__ 
         if (k < g.K) {
           const int64_t tap = k / g.C, ic = k - tap * g.C;
           const int64_t ky = tap / g.KW, kx = tap - ky * g.KW;
-          const int64_t iy = oy * g.sh + ky - g.pt, ix = ox * g.sw + kx - g.pl;
+          const int64_t iy = oy * g.sh + ky * g.dh - g.pt, ix = ox * g.sw + kx * g.dw - g.pl;
           int8_t val = (int8_t)pad_value;
           if (iy >= 0 && iy < g.H && ix >= 0 && ix < g.W)
             val = X[((b * g.H + iy) * g.W + ix) * g.C + ic];
@@ -76,12 +76,15 @@ __global__ __launch_bounds__(256) void im2col_kernel(const int8_t* __restrict__ 
 }  // namespace
 
 qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
-                        int32_t pt, int32_t pl, int32_t pb, int32_t pr, int64_t* OH,
-                        int64_t* OW) {
+                        int32_t pt, int32_t pl, int32_t pb, int32_t pr, int32_t dh, int32_t dw,
+                        int64_t* OH, int64_t* OW) {
   QP_REQUIRE(KH > 0 && KW > 0 && sh > 0 && sw > 0, QP_EINVAL,
              "conv: kernel and stride must be positive");
+  QP_REQUIRE(dh > 0 && dw > 0, QP_EINVAL, "conv: dilation must be positive");
   QP_REQUIRE(pt >= 0 && pl >= 0 && pb >= 0 && pr >= 0, QP_EINVAL, "conv: negative padding");
-  int64_t hh = H + pt + pb - KH, ww = W + pl + pr - KW;
+  // a dilated kernel spans d*(k-1)+1 input pixels
+  int64_t hh = H + pt + pb - ((int64_t)dh * (KH - 1) + 1);
+  int64_t ww = W + pl + pr - ((int64_t)dw * (KW - 1) + 1);
   QP_REQUIRE(hh >= 0 && ww >= 0, QP_EINVAL, "conv: kernel larger than the padded input");
   *OH = hh / sh + 1;
   *OW = ww / sw + 1;
@@ -90,9 +93,9 @@ qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh
 
 qp_status launch_im2col(const int8_t* X, int64_t NB, int64_t H, int64_t W, int64_t C,
                         int32_t pad_value, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
-                        int32_t pt, int32_t pl, int64_t OH, int64_t OW, int8_t* col,
-                        int64_t ldcol, hipStream_t stream) {
-  ConvGeom g{NB, H, W, C, OH, OW, (int64_t)KH * KW * C, KH, KW, sh, sw, pt, pl};
+                        int32_t pt, int32_t pl, int32_t dh, int32_t dw, int64_t OH, int64_t OW,
+                        int8_t* col, int64_t ldcol, hipStream_t stream) {
+  ConvGeom g{NB, H, W, C, OH, OW, (int64_t)KH * KW * C, KH, KW, sh, sw, pt, pl, dh, dw};
   const int64_t rows = NB * OH * OW;
   const int64_t chunks = ldcol / 16;
   const int64_t total = rows * chunks;
@@ -119,14 +122,14 @@ extern "C" qp_status qim2col_s8(const int8_t* X, int64_t NB, int64_t H, int64_t 
   QP_REQUIRE(NB > 0 && H > 0 && W > 0 && C > 0, QP_EINVAL, "qim2col_s8: empty input");
   QP_REQUIRE(pad_value >= -128 && pad_value <= 127, QP_EINVAL, "qim2col_s8: pad value not int8");
   int64_t OH, OW;
-  qp_status st = conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, &OH,
-                               &OW);
+  qp_status st = conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, 1, 1,
+                               &OH, &OW);
   if (st) return st;
   const int64_t K = (int64_t)KH * KW * C;
   QP_REQUIRE(ldcol >= K && ldcol % 16 == 0, QP_EINVAL,
              "qim2col_s8: ldcol must be >= K and a multiple of 16");
   QP_REQUIRE(X && col, QP_EINVAL, "qim2col_s8: null pointer");
   QP_REQUIRE((uintptr_t)col % 16 == 0, QP_EALIGN, "qim2col_s8: col must be 16-byte aligned");
-  return launch_im2col(X, NB, H, W, C, pad_value, KH, KW, stride_h, stride_w, pad_t, pad_l, OH, OW,
-                       col, ldcol, stream);
+  return launch_im2col(X, NB, H, W, C, pad_value, KH, KW, stride_h, stride_w, pad_t, pad_l, 1, 1,
+                       OH, OW, col, ldcol, stream);
 }

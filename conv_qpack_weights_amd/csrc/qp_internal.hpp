@@ -66,11 +66,23 @@ qp_status launch_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx
                                int64_t ldq, int64_t kfill, float* row_scale, int32_t* row_zp,
                                bool perm, hipStream_t stream);
 qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
-                        int32_t pt, int32_t pl, int32_t pb, int32_t pr, int64_t* OH, int64_t* OW);
+                        int32_t pt, int32_t pl, int32_t pb, int32_t pr, int32_t dh, int32_t dw,
+                        int64_t* OH, int64_t* OW);
 qp_status launch_im2col(const int8_t* X, int64_t NB, int64_t H, int64_t W, int64_t C,
                         int32_t pad_value, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
-                        int32_t pt, int32_t pl, int64_t OH, int64_t OW, int8_t* col,
-                        int64_t ldcol, hipStream_t stream);
+                        int32_t pt, int32_t pl, int32_t dh, int32_t dw, int64_t OH, int64_t OW,
+                        int8_t* col, int64_t ldcol, hipStream_t stream);
+// Implicit-GEMM convolution (the im2col gather inside the operand loads).
+// Needs C % 16 == 0, a 16-byte aligned X of fewer than 2^31 bytes and
+// K*65025 + max|bias| within int32 (checked by the caller).
+struct ConvShape {
+  int64_t NB, H, W, C, OH, OW;
+  int32_t KH, KW, sh, sw, pt, pl, dh, dw;
+};
+qp_status launch_conv_implicit(const int8_t* X, const ConvShape& cs, float sA, int32_t zA,
+                               const qp_packed_info* w, const void* packedW,
+                               const int32_t* bias, float sOut, int32_t zp_out, bool out32,
+                               int32_t relu, void* Y, hipStream_t stream);
 qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
                         const int32_t* bias, int64_t max_abs_bias, const qp_qtensor* out,
                         bool* out32);

@@ -333,6 +333,35 @@ qp_status qconv2d_s8_im2col(const qp_qtensor* x, const int8_t* X, const qp_packe
                             const qp_qtensor* y, int32_t relu, void* Y, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/*
+ * qconv2d_s8 -- the general INT8 NHWC convolution, with dilation.
+ *   acc[b,oy,ox,oc] = sum_{ky,kx,ic} (xp(oy*sh + ky*dh - pt, ox*sw + kx*dw - pl, ic) - zx)
+ *                                    * (w[oc,ic,ky,kx] - zw[oc]) + bias[oc],
+ *   xp = x inside the image and zx outside ([MNN] tileSplitFunction: padded
+ *   taps hold the input zero point); then the requantizing (or raw int32)
+ *   epilogue of qgemm_s8s8_requant.  OH = (H + pt + pb - (dh*(KH-1)+1))/sh + 1,
+ *   likewise OW.  Routes:
+ *   - 1x1 kernel, stride 1, no padding: the GEMM on x viewed as [NB*H*W, C]
+ *     ([MNN] DenseConvInt8TiledExecutor::onResize "fastway");
+ *   - C % 16 == 0 (and x under 2^31 bytes): implicit GEMM, the im2col gather
+ *     inside the operand loads, one launch, no workspace; x must then be
+ *     16-byte aligned (QP_EALIGN otherwise);
+ *   - otherwise the explicit im2col into the workspace, then the GEMM.
+ *   Arguments as qconv2d_s8_im2col, plus dil_h, dil_w >= 1.
+ *   ws       device workspace of qconv2d_s8_ws_size bytes (0 for the
+ *            implicit route; then ws may be NULL).
+ */
+qp_status qconv2d_s8_ws_size(const qp_qtensor* x, const qp_packed_info* w, int32_t KH,
+                             int32_t KW, int32_t stride_h, int32_t stride_w, int32_t pad_t,
+                             int32_t pad_l, int32_t pad_b, int32_t pad_r, int32_t dil_h,
+                             int32_t dil_w, size_t* bytes);
+qp_status qconv2d_s8(const qp_qtensor* x, const int8_t* X, const qp_packed_info* w,
+                     const void* packedW_dev, int32_t KH, int32_t KW, int32_t stride_h,
+                     int32_t stride_w, int32_t pad_t, int32_t pad_l, int32_t pad_b,
+                     int32_t pad_r, int32_t dil_h, int32_t dil_w, const int32_t* bias_dev,
+                     int64_t max_abs_bias, const qp_qtensor* y, int32_t relu, void* Y, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
