@@ -227,6 +227,26 @@ def requant_matrix(acc, s_a, s_b, s_out, zp_out, relu):
     return out, nd.value
 
 
+# ---------------------------------------------------------------- O9
+def dequant_weights_s8(W_nk, s, z):
+    """O9 (int8): f32 sB[n]*(q[n,k] - zB[n]), one IEEE f32 product per value
+    ([TRACT] extract_at_mn_f32 returns packed values as floats; the scale
+    and zero point are those stored beside the weights)."""
+    W = np.asarray(W_nk).astype(np.int32)
+    N = W.shape[0]
+    sv = np.broadcast_to(np.asarray(s, np.float32), (N,))
+    zv = np.broadcast_to(np.asarray(z, np.int32), (N,))
+    return sv[:, None] * (W - zv[:, None]).astype(np.float32)
+
+
+def dequant_weights_s4(W_nk, sw, group=32):
+    """O9 (int4): f32 sw[n, k // group]*q[n,k], one IEEE f32 product per value."""
+    W = np.asarray(W_nk).astype(np.float32)
+    sw = np.asarray(sw, np.float32)
+    g = np.arange(W.shape[1]) // group
+    return sw[:, g] * W
+
+
 # ---------------------------------------------------------------- O8
 def dequant_matrix_f32(acc, s_a, s_b, bias, lo, hi):
     """O8: Y = f32(clamp(sA*sB[n]*acc + bias[n], lo, hi)), in fp64."""

@@ -394,3 +394,25 @@ def test_o7_s4_blob_decodes_back(orc, N, K):
     want = np.array([math.fsum(float(a) * float(b) for a, b in zip(sw[n], gs[n])) for n in range(N)],
                     np.float64).astype(np.float32)
     assert np.array_equal(ws[:N], want) and not ws[N:].any()
+
+
+# ------------------------------------------------------------------ O9
+def test_o9_dequant_is_the_correctly_rounded_product(orc):
+    """Each value is s*(q - z) rounded once to f32: the fp64 product of a
+    24-bit scale and a 9-bit integer is exact, so casting it to f32 is the
+    correctly rounded result."""
+    rng = np.random.default_rng(91)
+    W = _rand_i8(rng, (7, 45))
+    s = rng.uniform(1e-4, 1e-1, 7).astype(np.float32)
+    z = rng.integers(-128, 128, 7).astype(np.int32)
+    got = orc.dequant_weights_s8(W, s, z)
+    want = (s.astype(np.float64)[:, None] * (W.astype(np.int64) - z[:, None])).astype(np.float32)
+    assert got.dtype == np.float32 and np.array_equal(got, want)
+    # scale per channel, not per k: a transposed scale vector changes row 0
+    assert not np.array_equal(got[0], orc.dequant_weights_s8(W, s[::-1], z)[0])
+    W4 = _rand_i8(rng, (5, 100), -8, 7)
+    sw = rng.uniform(1e-3, 1e-2, (5, 4)).astype(np.float32)
+    got4 = orc.dequant_weights_s4(W4, sw, 32)
+    for n in range(5):
+        for k in range(100):
+            assert got4[n, k] == np.float32(float(sw[n, k // 32]) * int(W4[n, k]))
