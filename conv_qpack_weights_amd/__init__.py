@@ -64,6 +64,7 @@ SIGNATURES = {
     "qpack_weights_size": (C.c_int, [_QT, _I32, _I32, _SZ, _SZ]),
     "qpack_weights": (C.c_int, [_QT, _P, _I32, _I32, _P, C.c_size_t, _PI, _P]),
     "qp_packed_info_from_header": (C.c_int, [_P, _PI]),
+    "qunpack_weights": (C.c_int, [_PI, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P]),
     "qquantize_rows_s8": (C.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P]),
     "qquantize_rows_s8_sym": (C.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "qgemm_s8s8_requant_ws_size": (C.c_int, [_QT, _PI, _SZ]),
@@ -201,6 +202,45 @@ def qp_packed_info_from_header(header: bytes) -> PackedInfo:
     buf = C.create_string_buffer(bytes(header), 256)
     _check(_lib.qp_packed_info_from_header(buf, C.byref(info)), "qp_packed_info_from_header")
     return info
+
+
+def qunpack_weights(blob: torch.Tensor, info: PackedInfo, n_begin=0, n_count=None,
+                    values=True, scales=True, dequant=False):
+    """Channels [n_begin, n_begin+n_count) of a blob as logical int8 values
+    [n, K], their scales (int8 blob: [n]; int4: [n, groups]), zero points
+    (int8 blob) and optionally the dequantized f32 weights [n, K]."""
+    n_count = info.N - n_begin if n_count is None else n_count
+    dev = blob.device
+    K = info.K
+    groups = 1 if info.format == 1 else (K + info.group - 1) // info.group
+    w = torch.empty((n_count, K), dtype=torch.int8, device=dev) if values else None
+    sc = None
+    if scales:
+        sc = torch.empty((n_count,) if info.format == 1 else (n_count, groups),
+                         dtype=torch.float32, device=dev)
+    zp = torch.empty(n_count, dtype=torch.int32, device=dev) if (scales and info.format == 1) \
+        else None
+    dq = torch.empty((n_count, K), dtype=torch.float32, device=dev) if dequant else None
+    _check(_lib.qunpack_weights(C.byref(info), _ptr(blob), n_begin, n_count, _ptr(w), K, _ptr(sc),
+                                groups, _ptr(zp), _ptr(dq), K, _stream(dev)), "qunpack_weights")
+    return w, sc, zp, dq
+
+
+def blob_to_bytes(blob: torch.Tensor) -> bytes:
+    """The blob as bytes (it describes itself: header, then the regions)."""
+    return blob.cpu().numpy().tobytes()
+
+
+def blob_from_bytes(data: bytes, device="cuda"):
+    """A blob restored from bytes onto `device`, with its info decoded (and
+    validated) from the header."""
+    info = qp_packed_info_from_header(data[:256])
+    if len(data) < info.total_bytes:
+        raise QPackError(QP_ESIZE, "blob bytes: %d, header says %d"
+                         % (len(data), info.total_bytes))
+    blob = _alloc_bytes(info.total_bytes, device)
+    blob.copy_(torch.frombuffer(bytearray(data[:info.total_bytes]), dtype=torch.uint8))
+    return blob, info
 
 
 # ---------------------------------------------------------------- quantizer

@@ -184,6 +184,26 @@ qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32_t k_axis, 
 qp_status qp_packed_info_from_header(const void* header_host, qp_packed_info* info);
 
 /*
+ * qunpack_weights -- logical weights of channels [n_begin, n_begin+n_count)
+ * read back out of a blob ([TRACT] PackedFormat::extract_at_mn_f32: one
+ * M/N row's K values taken out of the packed panels, optionally as floats).
+ * For inspection and for checking a blob restored from bytes.
+ *   w_out      int8 [n_count][ldw] (ldw >= K): the logical values (int4
+ *              blobs: [-8, 7]); NULL to skip.
+ *   scales_out int8 blob: f32 [n_count]; int4 blob: f32 [n_count][lds]
+ *              (lds >= ceil(K/group)); NULL to skip.
+ *   zp_out     int8 blob: int32 [n_count] (zeros when symmetric); must be
+ *              NULL for int4 blobs.
+ *   deq_out    f32 [n_count][ldd] (ldd >= K): sB[n]*(q - zB[n]) for int8,
+ *              sw[n, k/group]*q for int4, one f32 rounding; NULL to skip.
+ * Padding (K..Kpad, N..Npad) is never written.  Asynchronous on `stream`.
+ */
+qp_status qunpack_weights(const qp_packed_info* info, const void* packed_dev, int64_t n_begin,
+                          int64_t n_count, int8_t* w_out, int64_t ldw, float* scales_out,
+                          int64_t lds, int32_t* zp_out, float* deq_out, int64_t ldd,
+                          hipStream_t stream);
+
+/*
  * qquantize_rows_s8 -- dynamic per-row asymmetric int8 quantization of f32
  * activations ([MNN] BatchAsyDynamicQuant; the [KLEIDI] "qai8dx" format).
  * Per row, as one f32 sequence (round half to even, no contraction):
