@@ -70,6 +70,7 @@ _SIGS = {
     "orc_quantize_row_s8": (None, [_P, _I64, _P, C.POINTER(_F), C.POINTER(_I32)]),
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
+    "orc_round_bf16_array": (None, [_I64, _P, _P]),
     "orc_dequant_matrix_f32": (C.c_int, [_I64, _I64, _P, _F, _P, _P, _F, _F, _P]),
     "orc_a8w4_blockwise": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64,
                                      _P, _F, _F, _P, _I64]),
@@ -225,6 +226,15 @@ def requant_matrix(acc, s_a, s_b, s_out, zp_out, relu):
                                   int(zp_out), int(bool(relu)), _ptr(out), C.byref(nd))
     _check(rc, "orc_requant_matrix")
     return out, nd.value
+
+
+# ---------------------------------------------------------------- O6b
+def round_bf16(x):
+    """O6b: f32 values rounded to the nearest bf16 (ties to even), as f32."""
+    x = _arr(np.asarray(x, np.float32), np.float32)
+    y = np.zeros_like(x)
+    lib().orc_round_bf16_array(x.size, _ptr(x), _ptr(y))
+    return y
 
 
 # ---------------------------------------------------------------- O9

@@ -481,6 +481,27 @@ void orc_quantize_rows_s8_sym(int64_t M, int64_t K, const float* X, int64_t ldx,
 }
 
 /* ========================================================================
+ * O6b -- group scales stored as bf16.  [KLEIDI] review of the wrapper: the
+ * KleidiAI kernel keeps the int4 group scales as bf16 to save space (the
+ * wrapper converts the f32 scales before packing).  The conversion itself is
+ * not printed; reading: round to the nearest bf16 (8 significant bits), ties
+ * to even, the IEEE default.  Written from the significand: x = f*2^e with
+ * f in [0.5, 1); keep rint(f*2^8)/2^8 (rint rounds half to even).  Finite,
+ * normal inputs only (scales are positive and far from the denormal range).
+ * ====================================================================== */
+float orc_round_bf16(float x) {
+  if (x == 0.0f || !isfinite(x)) return x;
+  int e = 0;
+  double f = frexp((double)x, &e);      /* exact: f has x's 24 bits */
+  double r = rint(ldexp(f, 8));         /* 8 significant bits, ties to even */
+  return (float)ldexp(r, e - 8);        /* r*2^(e-8) is a bf16 value, exact in f32 */
+}
+
+void orc_round_bf16_array(int64_t n, const float* x, float* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_round_bf16(x[i]);
+}
+
+/* ========================================================================
  * O6 -- int8 activations times int4 weights with one f32 scale per group of
  * `group` consecutive K ([KLEIDI]: f32 output with clamp, dynamically
  * quantized int8 activations, signed int4 weights in blocks of 32, and no

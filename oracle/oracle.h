@@ -39,6 +39,10 @@ int orc_gemm_affine_points(int64_t npts, const int64_t* ms, const int64_t* ns, i
                            const int8_t* B, int64_t b_sk, int64_t b_sn, const int32_t* zB,
                            const int32_t* bias, int64_t* acc);
 
+/* ---- O6b: bf16 rounding of group scales ----------------------------------- */
+float orc_round_bf16(float x);
+void orc_round_bf16_array(int64_t n, const float* x, float* y);
+
 /* ---- O8: f32 output of the INT8 GEMM ------------------------------------- */
 int orc_dequant_matrix_f32(int64_t M, int64_t N, const int64_t* acc, float s_a,
                            const float* s_b, const float* bias, float lo, float hi, float* Y);

@@ -416,3 +416,30 @@ def test_o9_dequant_is_the_correctly_rounded_product(orc):
     for n in range(5):
         for k in range(100):
             assert got4[n, k] == np.float32(float(sw[n, k // 32]) * int(W4[n, k]))
+
+
+# ------------------------------------------------------------------ O6b
+def test_o6b_bf16_rounding_matches_torch_cast(orc):
+    """Round to nearest bf16, ties to even: the same values as torch's
+    float32 -> bfloat16 conversion (a library routine), over random scales
+    and hand-made ties."""
+    import torch
+    rng = np.random.default_rng(61)
+    x = np.concatenate([rng.uniform(1e-4, 1.0, 5000), rng.uniform(0.002, 0.02, 5000),
+                        np.exp(rng.uniform(-30, 30, 2000))]).astype(np.float32)
+    got = orc.round_bf16(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got, want)
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 0.75 + 2 ** -9, 3 + 2 ** -7], np.float32)
+    assert orc.round_bf16(ties).tolist() == [1.0, 1 + 2 ** -6, 0.75, 3.0]
+
+
+def test_o6b_bf16_rounding_properties(orc):
+    rng = np.random.default_rng(62)
+    x = np.sort(rng.uniform(1e-3, 10.0, 20000).astype(np.float32))
+    y = orc.round_bf16(x)
+    assert np.all(np.diff(y) >= 0)                                  # monotone
+    assert np.array_equal(orc.round_bf16(y), y)                     # idempotent
+    assert np.all(np.abs(y.astype(np.float64) / x - 1) <= 2.0 ** -8)  # half an ulp of 8 bits
+    # the low 16 bits of a bf16 value are zero
+    assert not np.any(y.view(np.uint32) & 0xFFFF)
