@@ -288,6 +288,23 @@ def main():
             "note": "per-launch average, HIP graph replay of back-to-back launches (events)"}
         del blobs
 
+        # the same GEMV with the group scales stored as bf16 (blob format 3)
+        blob16, info16 = qp.pack_s4(Wd, swd, scale_dtype="bf16")
+        nbytes16 = nbytes_alg - 4096 * 128 * 2
+        copies16 = int(np.ceil(2 * INFINITY_CACHE / blob16.numel())) + 1
+        blobs16 = [blob16] + [blob16.clone() for _ in range(copies16 - 1)]
+        idx16 = [0]
+
+        def gemv16_cold():
+            i = idx16[0] = (idx16[0] + 1) % copies16
+            qp.qgemm_a8w4_blockwise_f32(Xg, blobs16[i], info16, bg, -6.0, 6.0, out=Yg, ws=ws4)
+        ms16 = graph_time(gemv16_cold, copies16)
+        gbs16 = nbytes16 / ms16 / 1e6
+        workloads["a8w4_gemv_1x4096x4096_bf16_scales"] = {
+            "quantize_plus_gemv_cold_us": round(ms16 * 1e3, 3), "GBps_cold": round(gbs16, 1),
+            "frac_hbm_peak_cold": round(gbs16 / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes16}
+        del blobs16
+
         # A8W4 GEMM, M in {16, 128}, N=11008, K=4096
         for Mg in (16, 128):
             gg = synth.a8w4_gemm(Mg)

@@ -55,14 +55,31 @@ __device__ __forceinline__ float finish(float S16, float sa, int32_t za, float w
 }
 
 // The int4 blob (group 32): channel n, 128-K block b at
-// ((n/16)*nblk + b)*1024 + (n%16)*64 bytes; its four group scales at float
-// ((n/16)*nblk + b)*64 + (n%16)*4.
+// ((n/16)*nblk + b)*1024 + (n%16)*64 bytes; its four group scales at scale
+// element ((n/16)*nblk + b)*64 + (n%16)*4, f32 (format 2) or bf16 (format 3).
 struct W4 {
   const uint8_t* data;
-  const float* scale;
+  const uint8_t* scale;
   const float* wsum;     // [Npad]
   int64_t N, Npad, Kpad, nblk;
+  int32_t bf16;          // scales stored as bf16
 };
+
+// The four group scales of one channel and block, as f32.  A bf16 value is
+// the upper half of the f32 with the same value.
+template <bool kBf16>
+__device__ __forceinline__ float4 load_scale4(const uint8_t* p) {
+  if constexpr (kBf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const uint32_t lo = u.x, hi = u.y;
+    return make_float4(__builtin_bit_cast(float, lo << 16),
+                       __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                       __builtin_bit_cast(float, hi << 16),
+                       __builtin_bit_cast(float, hi & 0xFFFF0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
 
 // ---- GEMV: a workgroup per 16-channel tile, waves split the 128-K blocks ----
 // Lane l handles channel l/4 of the tile and 16-byte chunk c = l%4 of each
@@ -76,7 +93,7 @@ struct W4 {
 // from memory (row-major).  Partial sums are reduced across the four lanes
 // of a channel with DPP and then across the waves through LDS, in a fixed
 // order.  Rows m > 0 reuse the weights held in registers.
-template <int NT, bool kFused>
+template <int NT, bool kFused, bool kBf16>
 __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__ X, int64_t K,
                                                        const int8_t* __restrict__ qa_g,
                                                        int64_t lda, const float* __restrict__ sa_g,
@@ -98,7 +115,8 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   const int64_t tile = blockIdx.x;
   const int64_t nb = w.nblk;
   const uint8_t* wbase = w.data + tile * nb * 1024 + lane * 16;
-  const float* sbase = w.scale + tile * nb * 64 + ch * 4;
+  constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
+  const uint8_t* sbase = w.scale + (tile * nb * 64 + ch * 4) * ES;
   // per-channel epilogue operands, fetched up front (off the critical path)
   const int64_t n_out = tile * 16 + (tid & 15);
   float wsum_c = 0.0f, bias_c = 0.0f;
@@ -137,7 +155,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
       const int64_t b = (j * BB + u) * NW + wave;
       blk[u] = b < nb ? b : nb - 1;
       wv[u] = *reinterpret_cast<const uint4*>(wbase + blk[u] * 1024);
-      const float4 s4 = *reinterpret_cast<const float4*>(sbase + blk[u] * 64);
+      const float4 s4 = load_scale4<kBf16>(sbase + blk[u] * 64 * ES);
       sv[u] = b < nb ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if constexpr (kFused) {
@@ -228,7 +246,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 // before their results are rescaled, two group slots at a time, into two
 // f32 chains (even and odd slots) per output.  K-range partial sums are
 // added in wave order through LDS.
-template <int FM, int FN, int RW, int CW, int KS, bool kPerm>
+template <int FM, int FN, int RW, int CW, int KS, bool kPerm, bool kBf16>
 __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict__ qa,
                                                         int64_t lda, const float* __restrict__ sa_g,
                                                         const int32_t* __restrict__ za_g,
@@ -270,14 +288,15 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   const int64_t my_end = (ks * bpw + bpw < nblocks ? ks * bpw + bpw : nblocks);
 
   // ---- weight/scale sources (tile-contiguous blob) ----
+  constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
   const int8_t* wsrc[FN];
-  const float* ssrc[FN];
+  const uint8_t* ssrc[FN];
 #pragma unroll
   for (int q = 0; q < FN; ++q) {
     const int64_t n = n0 + q * 16 + (lane & 15);
     wsrc[q] = reinterpret_cast<const int8_t*>(w.data) + (n >> 4) * w.nblk * 1024 +
               (lane & 15) * 64 + 16 * c;
-    ssrc[q] = w.scale + (n >> 4) * w.nblk * 64 + (lane & 15) * 4;
+    ssrc[q] = w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
   }
 
   // ---- activation direct loads: thread slot s = tid + 256*i of a stage ->
@@ -322,7 +341,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       wr[u][q] = *reinterpret_cast<const uint4*>(wsrc[q] + b * 1024);
-      sr[u][q] = *reinterpret_cast<const float4*>(ssrc[q] + 64 * b);
+      sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
     }
   };
 
@@ -468,13 +487,13 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 
 W4 w4_of(const qp_packed_info* b, const void* blob) {
   const uint8_t* p = static_cast<const uint8_t*>(blob);
-  return W4{p + b->data_off, reinterpret_cast<const float*>(p + b->scale_off),
-            reinterpret_cast<const float*>(p + b->sum_off), b->N, b->Npad, b->Kpad,
-            b->Kpad / 128};
+  return W4{p + b->data_off, p + b->scale_off, reinterpret_cast<const float*>(p + b->sum_off),
+            b->N, b->Npad, b->Kpad, b->Kpad / 128, b->format == 3 ? 1 : 0};
 }
 
 qp_status validate_w4(const qp_packed_info* b, int64_t K) {
-  QP_REQUIRE(b && b->format == 2, QP_EINVAL, "a8w4: weights must be an int4 blob");
+  QP_REQUIRE(b && (b->format == 2 || b->format == 3), QP_EINVAL,
+             "a8w4: weights must be an int4 blob");
   QP_REQUIRE(b->group == 32, QP_EUNSUPPORTED, "a8w4: group size %lld not implemented (32 only)",
              (long long)b->group);
   QP_REQUIRE(K == b->K, QP_EINVAL, "a8w4: activation K=%lld but the weights have K=%lld",
@@ -489,12 +508,18 @@ qp_status launch_gemv_cfg(const float* X, int64_t K, const int8_t* qa, int64_t l
                           bool fused, hipStream_t stream) {
   const unsigned blocks = (unsigned)(w.Npad / 16);
   const size_t lds = fused ? (size_t)w.Kpad : 0;
-  if (fused)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true>), dim3(blocks), dim3(NT), lds, stream, X, K,
-                       qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  if (fused && w.bf16)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true, true>), dim3(blocks), dim3(NT), lds, stream, X,
+                       K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  else if (fused)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true, false>), dim3(blocks), dim3(NT), lds, stream,
+                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  else if (w.bf16)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, true>), dim3(blocks), dim3(NT), lds, stream,
+                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   else
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false>), dim3(blocks), dim3(NT), lds, stream, X, K,
-                       qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, false>), dim3(blocks), dim3(NT), lds, stream,
+                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w4 gemv");
 }
 
@@ -514,12 +539,19 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   const unsigned bx = (unsigned)ceil_div(w.N, 16 * FN * CW);
   const int64_t by = ceil_div(M, 16 * FM * RW);
   QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w4: M too large");
-  if (perm)
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true>), dim3(bx, (unsigned)by),
-                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  const dim3 grid(bx, (unsigned)by);
+  if (perm && w.bf16)
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true, true>), grid, dim3(256), 0,
+                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  else if (perm)
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true, false>), grid, dim3(256), 0,
+                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+  else if (w.bf16)
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, true>), grid, dim3(256), 0,
+                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   else
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false>), dim3(bx, (unsigned)by),
-                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, false>), grid, dim3(256), 0,
+                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w4 gemm");
 }
 

@@ -101,6 +101,16 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
 // channels of a tile store each block side by side (1 KiB per tile and
 // block), and their scales likewise in quads of four groups (256 bytes), so
 // one wave reads a tile's block, or its scales, as one contiguous piece.
+//
+// kBf16 (blob format 3): each scale is stored rounded to the nearest bf16,
+// ties to even (the upper half of the f32 after adding 0x7FFF plus the
+// lowest kept bit), and the channel's weight sum uses the rounded scales.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool kBf16>
 __global__ __launch_bounds__(256) void pack_s4_kernel(
     const int8_t* __restrict__ w, int64_t N, int64_t K, int64_t Kpad, int64_t group, int64_t sn,
     KMap km, const float* __restrict__ sw, int64_t ldsw, uint8_t* __restrict__ blob,
@@ -136,17 +146,28 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
   }
   if (bad) atomicOr(reinterpret_cast<int32_t*>(blob + kInvalidFlagOffset), 1);
   __syncthreads();
-  float* srow = reinterpret_cast<float*>(blob + scale_off) + (n / 16) * Gq * 64 + (n % 16) * 4;
-  for (int64_t g = threadIdx.x; g < 4 * Gq; g += blockDim.x)
-    srow[(g / 4) * 64 + g % 4] = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
+  // the stored value of group g's scale
+  auto stored = [&](int64_t g) -> float {
+    const float s = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
+    if constexpr (kBf16) return __builtin_bit_cast(float, bf16_bits(s) << 16);
+    return s;
+  };
+  const int64_t sidx = (n / 16) * Gq * 64 + (n % 16) * 4;
+  for (int64_t g = threadIdx.x; g < 4 * Gq; g += blockDim.x) {
+    const float s = stored(g);
+    if constexpr (kBf16)
+      reinterpret_cast<uint16_t*>(blob + scale_off)[sidx + (g / 4) * 64 + g % 4] =
+          (uint16_t)(__builtin_bit_cast(uint32_t, s) >> 16);
+    else
+      reinterpret_cast<float*>(blob + scale_off)[sidx + (g / 4) * 64 + g % 4] = s;
+  }
   if (threadIdx.x == 0) {
     double acc = 0.0;
     const int64_t rpg = group / 32;
     for (int64_t g = 0; g < G; ++g) {
       int64_t gs = 0;
       for (int64_t r = g * rpg; r < (g + 1) * rpg; ++r) gs += run_sum[r];
-      const double s = (live && g < Greal) ? (double)sw[n * ldsw + g] : 0.0;
-      acc = acc + s * (double)gs;
+      acc = acc + (double)stored(g) * (double)gs;
     }
     reinterpret_cast<float*>(blob + sum_off)[n] = live ? (float)acc : 0.0f;
   }
@@ -193,11 +214,11 @@ qp_status format_of(const qp_qtensor* w, int32_t* format) {
                "int8 weights support per-tensor or per-channel scales (scheme %d)", w->scheme);
     *format = 1;
   } else if (w->dtype == QP_S4) {
-    QP_REQUIRE(w->scheme == QP_BLOCKWISE, QP_EUNSUPPORTED,
+    QP_REQUIRE(w->scheme == QP_BLOCKWISE || w->scheme == QP_BLOCKWISE_BF16, QP_EUNSUPPORTED,
                "int4 weights support blockwise scales only (scheme %d)", w->scheme);
     QP_REQUIRE(w->zero_points == nullptr && w->zero_point == 0, QP_EUNSUPPORTED,
                "int4 blockwise weights are symmetric: zero points must be absent");
-    *format = 2;
+    *format = w->scheme == QP_BLOCKWISE_BF16 ? 3 : 2;
   } else {
     QP_FAIL(QP_EUNSUPPORTED, "weights must be QP_S8 or QP_S4 (dtype %d)", w->dtype);
   }
@@ -216,7 +237,7 @@ extern "C" qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int
   int32_t format = 0;
   if ((st = format_of(w, &format))) return st;
   qp_packed_info g;
-  if ((st = blob_geometry(format, w->scheme, v.N, v.K, format == 2 ? w->group_size : 0, &g)))
+  if ((st = blob_geometry(format, w->scheme, v.N, v.K, format != 1 ? w->group_size : 0, &g)))
     return st;
   if (bytes) *bytes = (size_t)g.total_bytes;
   if (align) *align = (size_t)kRegionAlign;
@@ -234,7 +255,7 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
   int32_t format = 0;
   if ((st = format_of(w, &format))) return st;
   qp_packed_info g;
-  if ((st = blob_geometry(format, w->scheme, v.N, v.K, format == 2 ? w->group_size : 0, &g)))
+  if ((st = blob_geometry(format, w->scheme, v.N, v.K, format != 1 ? w->group_size : 0, &g)))
     return st;
   QP_REQUIRE(w_dev && packed_dev && info, QP_EINVAL, "qpack_weights: null pointer argument");
   QP_REQUIRE(packed_bytes >= (size_t)g.total_bytes, QP_ESIZE,
@@ -312,9 +333,14 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
     if ((st = check_launch("qpack_weights header"))) return st;
     size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / 32);
-    hipLaunchKernelGGL(pack_s4_kernel, dim3((unsigned)g.Npad), dim3(256), lds, stream, src, v.N,
-                       v.K, g.Kpad, g.group, v.sn, v.km, w->scales, ceil_div(v.K, g.group), blob,
-                       g.data_off, g.scale_off, g.sum_off);
+    if (format == 3)
+      hipLaunchKernelGGL(pack_s4_kernel<true>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
+                         v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales, ceil_div(v.K, g.group),
+                         blob, g.data_off, g.scale_off, g.sum_off);
+    else
+      hipLaunchKernelGGL(pack_s4_kernel<false>, dim3((unsigned)g.Npad), dim3(256), lds, stream,
+                         src, v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales,
+                         ceil_div(v.K, g.group), blob, g.data_off, g.scale_off, g.sum_off);
     if ((st = check_launch("qpack_weights int4"))) return st;
     g.has_zero_points = 0;
   }

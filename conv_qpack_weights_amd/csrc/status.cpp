@@ -43,7 +43,7 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.sum_off = g.scale_off + round_up(4 * g.Npad, kRegionAlign);
     g.zp_off = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
     g.total_bytes = g.zp_off + round_up(4 * g.Npad, kRegionAlign);
-  } else if (format == 2) {
+  } else if (format == 2 || format == 3) {
     QP_REQUIRE(group > 0 && group % kRunK4 == 0 && (kBlockK4 % group == 0 || group % kBlockK4 == 0),
                QP_EUNSUPPORTED, "int4 group size must be 32, 64, 128 or a multiple of 128 (got %lld)",
                (long long)group);
@@ -51,8 +51,11 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.Kpad = round_up(K, group > kBlockK4 ? group : kBlockK4);
     g.data_bytes = g.Npad * g.Kpad / 2;
     g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
-    // scales in quads of 4 groups: f32 [Npad/16][ceil(G/4)][16][4]
-    g.sum_off = g.scale_off + round_up(16 * g.Npad * ceil_div(g.Kpad / group, 4), kRegionAlign);
+    // scales in quads of 4 groups: [Npad/16][ceil(G/4)][16][4] of f32
+    // (format 2) or bf16 (format 3)
+    const int64_t es = format == 2 ? 4 : 2;
+    g.sum_off =
+        g.scale_off + round_up(4 * es * g.Npad * ceil_div(g.Kpad / group, 4), kRegionAlign);
     g.zp_off = 0;
     g.total_bytes = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
   } else {

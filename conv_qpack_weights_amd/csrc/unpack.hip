@@ -16,6 +16,16 @@
 namespace qp {
 namespace {
 
+// Scale element e of an int4 blob: f32 (format 2) or bf16 (format 3, the
+// upper half of the f32 of the same value).
+__device__ __forceinline__ float scale_at(const uint8_t* blob, const qp_packed_info& b, int64_t e) {
+  if (b.format == 3) {
+    const uint32_t h = reinterpret_cast<const uint16_t*>(blob + b.scale_off)[e];
+    return __builtin_bit_cast(float, h << 16);
+  }
+  return reinterpret_cast<const float*>(blob + b.scale_off)[e];
+}
+
 // One thread per (channel, k) of the requested range.
 __global__ __launch_bounds__(256) void unpack_s8_kernel(const uint8_t* __restrict__ blob,
                                                         qp_packed_info b, int64_t n0,
@@ -59,8 +69,7 @@ __global__ __launch_bounds__(256) void unpack_s4_kernel(const uint8_t* __restric
   if (deq) {
     const int64_t g = k / b.group;
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
-    const float s = reinterpret_cast<const float*>(
-        blob + b.scale_off)[((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4];
+    const float s = scale_at(blob, b, ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4);
     deq[i * ldd + k] = s * (float)q;
   }
 }
@@ -82,8 +91,8 @@ __global__ __launch_bounds__(256) void unpack_scales_kernel(const uint8_t* __res
     if (zp) zp[i] = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
   } else if (scales) {
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
-    scales[i * lds + g] = reinterpret_cast<const float*>(
-        blob + b.scale_off)[((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4];
+    scales[i * lds + g] =
+        scale_at(blob, b, ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4);
   }
 }
 
@@ -98,7 +107,7 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   using namespace qp;
   clear_error();
   QP_REQUIRE(info && packed_dev, QP_EINVAL, "qunpack_weights: null blob");
-  QP_REQUIRE(info->format == 1 || info->format == 2, QP_EINVAL,
+  QP_REQUIRE(info->format >= 1 && info->format <= 3, QP_EINVAL,
              "qunpack_weights: unknown blob format %d", info->format);
   QP_REQUIRE(n_begin >= 0 && n_count >= 0 && n_begin + n_count <= info->N, QP_EINVAL,
              "qunpack_weights: channels [%lld, %lld) outside [0, %lld)", (long long)n_begin,

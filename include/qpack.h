@@ -51,7 +51,11 @@ typedef enum {
   QP_PER_TENSOR = 0,
   QP_PER_CHANNEL = 1,
   QP_BLOCKWISE = 2,
-  QP_DYNAMIC_PER_ROW = 3
+  QP_DYNAMIC_PER_ROW = 3,
+  /* blockwise int4 whose f32 group scales are stored rounded to bf16
+   * (nearest, ties to even), as the KleidiAI kernel keeps them ([KLEIDI]
+   * review of the wrapper's scale conversion); blob format 3 */
+  QP_BLOCKWISE_BF16 = 4
 } qp_qscheme;
 
 typedef enum { QP_ROUND_HALF_EVEN = 0 } qp_rounding;
@@ -164,8 +168,11 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  *   carries the same 8 K of four consecutive groups.  Scales f32 in quads
  *   of four groups with the tile's 16 channels side by side: sw[n][g] at
  *   float ((n/16)*ceil(G/4) + g/4)*64 + (n%16)*4 + g%4, G = Kpad/group
- *   (zero for groups past K);
- *   f32 wsum[Npad] = sum_g sw[n,g] * sum_{k in g} w[n,k], accumulated in fp64
+ *   (zero for groups past K).  Format 3 (scheme QP_BLOCKWISE_BF16) stores
+ *   the same scale array as bf16, each the given f32 rounded to nearest,
+ *   ties to even, at the same element index (2 bytes each);
+ *   f32 wsum[Npad] = sum_g sw[n,g] * sum_{k in g} w[n,k] (with the stored
+ *   scales), accumulated in fp64
  *   (the weight kernel sum that folds the activation zero point,
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
  * All padding bytes are zero.  int4 values outside [-8,7] set the header word

@@ -91,3 +91,46 @@ def test_a8w4_deterministic(qp):
     first = _host(qp.qgemm_a8w4_blockwise_f32(X, blob, info, b, -6.0, 6.0))
     for _ in range(10):
         assert np.array_equal(first, _host(qp.qgemm_a8w4_blockwise_f32(X, blob, info, b, -6.0, 6.0)))
+
+
+# ---- group scales stored as bf16 (blob format 3): the oracle takes the
+# scales rounded by O6b, everything else unchanged
+def _case_bf16(qp, orc, d, rows=None, prequant=False):
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]), scale_dtype="bf16")
+    assert info.format == 3
+    sw16 = orc.round_bf16(d["sw"])
+    if prequant:
+        import torch
+        M = d["X"].shape[0]
+        q = torch.zeros((M, info.Kpad), dtype=torch.int8, device="cuda")
+        q, s, z = qp.qquantize_rows_s8(_dev(d["X"]), q=q)
+        Y = _host(qp.qgemm_a8w4_prequant_f32(q, s, z, blob, info, _dev(d["bias"]),
+                                             d["clamp_lo"], d["clamp_hi"]))
+    else:
+        Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
+                                              d["clamp_lo"], d["clamp_hi"]))
+    X = d["X"] if rows is None else d["X"][rows]
+    want = orc.a8w4_forward(X, d["W"], sw16, d["bias"], d["clamp_lo"], d["clamp_hi"])
+    _check_close(Y if rows is None else Y[rows], want, "a8w4 bf16-scale output")
+    return blob, info, sw16
+
+
+def test_a8w4_bf16_scales_gemv_workload(qp, orc):
+    d = synth.a8w4_gemv()
+    blob, info, sw16 = _case_bf16(qp, orc, d)
+    # the blob holds exactly the rounded scales, and they differ from the f32 ones
+    _, sc, _, _ = qp.qunpack_weights(blob, info, values=False)
+    assert np.array_equal(_host(sc), sw16) and not np.array_equal(sw16, d["sw"])
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_a8w4_bf16_scales_gemm_workload(qp, orc, M):
+    rows = None if M == 16 else np.r_[0:8, 120:128]
+    _case_bf16(qp, orc, synth.a8w4_gemm(M), rows)
+
+
+@pytest.mark.parametrize("M,N,K,prequant", [(1, 70, 96, False), (3, 64, 4096, True),
+                                            (5, 77, 1000, False), (33, 48, 160, True),
+                                            (130, 48, 320, False)])
+def test_a8w4_bf16_scales_shapes(qp, orc, M, N, K, prequant):
+    _case_bf16(qp, orc, synth.a8w4(synth.BASE_SEED + 11 * M + N + K, M, N, K), prequant=prequant)
