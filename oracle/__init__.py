@@ -71,6 +71,8 @@ _SIGS = {
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
     "orc_round_bf16_array": (None, [_I64, _P, _P]),
+    "orc_a8w4_blockwise_asym": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P,
+                                          _P, _I64, _P, _F, _F, _P, _I64]),
     "orc_dequant_matrix_f32": (C.c_int, [_I64, _I64, _P, _F, _P, _P, _F, _F, _P]),
     "orc_a8w4_blockwise": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P, _I64,
                                      _P, _F, _F, _P, _I64]),
@@ -226,6 +228,33 @@ def requant_matrix(acc, s_a, s_b, s_out, zp_out, relu):
                                   int(zp_out), int(bool(relu)), _ptr(out), C.byref(nd))
     _check(rc, "orc_requant_matrix")
     return out, nd.value
+
+
+# ---------------------------------------------------------------- O6c
+def a8w4_blockwise_asym(qa, sa, za, qw, sw, bw, bias, clamp_lo, clamp_hi, group=32):
+    """O6c: asymmetric int4, w = sw*q + bw per group."""
+    qa = _arr(qa, np.int8)
+    qw = _arr(qw, np.int8)
+    sw = _arr(sw, np.float32)
+    bw = _arr(bw, np.float32)
+    assert sw.shape == bw.shape
+    M, K = qa.shape
+    N = qw.shape[0]
+    sa = _arr(sa, np.float32)
+    za = _arr(za, np.int32)
+    biasv = None if bias is None else _arr(bias, np.float32)
+    Y = np.zeros((M, N), dtype=np.float32)
+    rc = lib().orc_a8w4_blockwise_asym(M, N, K, group, _ptr(qa), K, _ptr(sa), _ptr(za), _ptr(qw),
+                                       K, _ptr(sw), _ptr(bw), sw.shape[1], _ptr(biasv),
+                                       float(clamp_lo), float(clamp_hi), _ptr(Y), N)
+    _check(rc, "orc_a8w4_blockwise_asym")
+    return Y
+
+
+def a8w4_forward_asym(X, qw, sw, bw, bias, clamp_lo, clamp_hi, group=32):
+    """Dynamic per-row quantization (O5) then O6c."""
+    qa, sa, za = quantize_rows_s8(X)
+    return a8w4_blockwise_asym(qa, sa, za, qw, sw, bw, bias, clamp_lo, clamp_hi, group)
 
 
 # ---------------------------------------------------------------- O6b

@@ -539,6 +539,46 @@ int orc_a8w4_blockwise(int64_t M, int64_t N, int64_t K, int64_t group, const int
 }
 
 /* ========================================================================
+ * O6c -- asymmetric int4 weights: a float offset per group besides the
+ * scale.  [MNN] _computeReorderQuantInfo / the KleidiAI branch of the weight
+ * preparation: for asymmetric weights each (channel, block) carries a pair
+ * (zero, scale) with real weight = scale*q + zero (the zero shifted by the
+ * int4 origin offset), and the weight kernel sum becomes the sum of the real
+ * weights.  Reading: logical q in [-8, 7], w[n,k] = sw[n,g]*q[n,k] + bw[n,g]
+ * (the caller gives bw already for that q), the rest as O6:
+ *   Y[m,n] = clamp(sa[m] * sum_k (qa[m,k] - za[m]) * w[n,k] + bias[n], lo, hi)
+ * summed per group as sw*D + bw*E, D = sum (qa-za)*q and E = sum (qa-za)
+ * exact integers, the groups in fp64, one rounding to f32.
+ * ====================================================================== */
+int orc_a8w4_blockwise_asym(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t* qa,
+                            int64_t lda, const float* sa, const int32_t* za, const int8_t* qw,
+                            int64_t ldw, const float* sw, const float* bw, int64_t ldsw,
+                            const float* bias, float clamp_lo, float clamp_hi, float* Y,
+                            int64_t ldy) {
+  if (M < 0 || N < 0 || K < 0 || group <= 0) return ORC_EINVAL;
+  int64_t G = orc_ceil_div(K, group);
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = 0.0;
+      for (int64_t g = 0; g < G; ++g) {
+        int64_t d = 0, e = 0;
+        int64_t k1 = (g + 1) * group < K ? (g + 1) * group : K;
+        for (int64_t k = g * group; k < k1; ++k) {
+          int64_t a = (int64_t)qa[m * lda + k] - za[m];
+          d += a * (int64_t)qw[n * ldw + k];
+          e += a;
+        }
+        sum += (double)sw[n * ldsw + g] * (double)d + (double)bw[n * ldsw + g] * (double)e;
+      }
+      double y = (double)sa[m] * sum + (bias ? (double)bias[n] : 0.0);
+      if (y < (double)clamp_lo) y = (double)clamp_lo;
+      if (y > (double)clamp_hi) y = (double)clamp_hi;
+      Y[m * ldy + n] = (float)y;
+    }
+  return 0;
+}
+
+/* ========================================================================
  * O7 -- reference writer of the library's packed-weight blob, written from
  * the format definition (not from the GPU packer).  Prior art for what a
  * packed operand holds: [TRACT] PackedI8K4 (K-inner int8 panels with

@@ -443,3 +443,87 @@ def test_o6b_bf16_rounding_properties(orc):
     assert np.all(np.abs(y.astype(np.float64) / x - 1) <= 2.0 ** -8)  # half an ulp of 8 bits
     # the low 16 bits of a bf16 value are zero
     assert not np.any(y.view(np.uint32) & 0xFFFF)
+
+
+# ------------------------------------------------------------------ O6c
+def _o6c_inputs(rng, M, N, K, G):
+    qa = _rand_i8(rng, (M, K))
+    sa = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    za = rng.integers(-128, 128, M).astype(np.int32)
+    qw = _rand_i8(rng, (N, K), -8, 7)
+    sw = rng.uniform(0.002, 0.02, (N, G)).astype(np.float32)
+    bw = rng.uniform(-0.05, 0.05, (N, G)).astype(np.float32)
+    return qa, sa, za, qw, sw, bw
+
+
+def test_o6c_zero_offsets_reduce_to_o6(orc):
+    rng = np.random.default_rng(71)
+    qa, sa, za, qw, sw, _ = _o6c_inputs(rng, 3, 9, 100, 4)
+    bias = rng.uniform(-1, 1, 9).astype(np.float32)
+    got = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, np.zeros_like(sw), bias, -6, 6)
+    assert np.array_equal(got, orc.a8w4_blockwise(qa, sa, za, qw, sw, bias, -6, 6))
+
+
+def test_o6c_closed_form_constant_operands(orc):
+    # qa == 5, za == -3, q == -2, sw = 2^-6, bw = 2^-3, K = 96 (three groups):
+    # every output is sa * K * (5+3) * (-2*2^-6 + 2^-3) + bias, exactly
+    M, N, K = 2, 3, 96
+    qa = np.full((M, K), 5, np.int8)
+    qw = np.full((N, K), -2, np.int8)
+    sw = np.full((N, 3), 2.0 ** -6, np.float32)
+    bw = np.full((N, 3), 2.0 ** -3, np.float32)
+    sa = np.array([0.5, 0.25], np.float32)
+    za = np.array([-3, -3], np.int32)
+    bias = np.array([1.0, -2.0, 0.0], np.float32)
+    y = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, bw, bias, -1e9, 1e9)
+    for m in range(M):
+        for n in range(N):
+            assert y[m, n] == np.float32(float(sa[m]) * K * 8 * (-2 * 2.0 ** -6 + 2.0 ** -3)
+                                         + float(bias[n]))
+
+
+def test_o6c_integer_zero_points_match_direct_sum(orc):
+    """bw = -sw*zw with an integer zero point per group is the affine form
+    sw*(q - zw): compare with the sum written out in exact rationals."""
+    rng = np.random.default_rng(72)
+    M, N, K, G = 2, 4, 70, 3
+    qa, sa, za, qw, sw, _ = _o6c_inputs(rng, M, N, K, G)
+    sw = (2.0 ** -rng.integers(4, 9, (N, G))).astype(np.float32)   # powers of two: exact
+    zw = rng.integers(-8, 8, (N, G))
+    bw = (-sw * zw).astype(np.float32)
+    y = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, bw, None, -1e30, 1e30)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                g = k // 32
+                s += (int(qa[m, k]) - int(za[m])) * Fraction(float(sw[n, g])) \
+                    * (int(qw[n, k]) - int(zw[n, g]))
+            exact = Fraction(float(sa[m])) * s
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 23) \
+                + Fraction(1, 2 ** 60)
+
+
+def test_o6c_brute_force_rational(orc):
+    rng = np.random.default_rng(73)
+    M, N, K, G = 3, 5, 45, 2
+    qa, sa, za, qw, sw, bw = _o6c_inputs(rng, M, N, K, G)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    y = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, bw, bias, -1e30, 1e30)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                g = k // 32
+                w = Fraction(float(sw[n, g])) * int(qw[n, k]) + Fraction(float(bw[n, g]))
+                s += (int(qa[m, k]) - int(za[m])) * w
+            exact = Fraction(float(sa[m])) * s + Fraction(float(bias[n]))
+            err = abs(Fraction(float(y[m, n])) - exact)
+            assert err <= abs(exact) * Fraction(1, 2 ** 23) + Fraction(1, 2 ** 40)
+    # the offsets are per (channel, group): moving one group's offset changes
+    # only that channel
+    bw2 = bw.copy()
+    bw2[1, 1] += 0.01
+    y2 = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, bw2, bias, -1e30, 1e30)
+    assert np.array_equal(np.delete(y2, 1, axis=1), np.delete(y, 1, axis=1))
+    assert not np.array_equal(y2[:, 1], y[:, 1])
