@@ -278,12 +278,16 @@ def dequant_weights_s8(W_nk, s, z):
     return sv[:, None] * (W - zv[:, None]).astype(np.float32)
 
 
-def dequant_weights_s4(W_nk, sw, group=32):
-    """O9 (int4): f32 sw[n, k // group]*q[n,k], one IEEE f32 product per value."""
+def dequant_weights_s4(W_nk, sw, group=32, bw=None):
+    """O9 (int4): f32 sw[n, k // group]*q[n,k], one IEEE f32 product per value;
+    asymmetric weights (O6c) then add the group offset in f32."""
     W = np.asarray(W_nk).astype(np.float32)
     sw = np.asarray(sw, np.float32)
     g = np.arange(W.shape[1]) // group
-    return sw[:, g] * W
+    y = sw[:, g] * W
+    if bw is not None:
+        y = y + np.asarray(bw, np.float32)[:, g]
+    return y
 
 
 # ---------------------------------------------------------------- O8

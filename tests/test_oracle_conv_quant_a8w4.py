@@ -527,3 +527,15 @@ def test_o6c_brute_force_rational(orc):
     y2 = orc.a8w4_blockwise_asym(qa, sa, za, qw, sw, bw2, bias, -1e30, 1e30)
     assert np.array_equal(np.delete(y2, 1, axis=1), np.delete(y, 1, axis=1))
     assert not np.array_equal(y2[:, 1], y[:, 1])
+
+
+def test_o9_asymmetric_dequant_adds_the_group_offset(orc):
+    rng = np.random.default_rng(93)
+    W4 = _rand_i8(rng, (3, 70), -8, 7)
+    sw = rng.uniform(1e-3, 1e-2, (3, 3)).astype(np.float32)
+    bw = rng.uniform(-0.05, 0.05, (3, 3)).astype(np.float32)
+    got = orc.dequant_weights_s4(W4, sw, 32, bw)
+    for n in range(3):
+        for k in range(70):
+            p = np.float32(float(sw[n, k // 32]) * int(W4[n, k]))     # exact product, one rounding
+            assert got[n, k] == np.float32(float(p) + float(bw[n, k // 32]))
