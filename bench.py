@@ -305,6 +305,25 @@ def main():
             "frac_hbm_peak_cold": round(gbs16 / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes16}
         del blobs16
 
+        # asymmetric int4 (a float offset per group, blob format 4)
+        bw = torch.from_numpy(np.random.default_rng(1).uniform(
+            -0.05, 0.05, gv["sw"].shape).astype(np.float32)).to(dev)
+        blobA, infoA = qp.pack_s4(Wd, swd, offsets=bw)
+        nbytesA = nbytes_alg + 4096 * 128 * 4
+        copiesA = int(np.ceil(2 * INFINITY_CACHE / blobA.numel())) + 1
+        blobsA = [blobA] + [blobA.clone() for _ in range(copiesA - 1)]
+        idxA = [0]
+
+        def gemvA_cold():
+            i = idxA[0] = (idxA[0] + 1) % copiesA
+            qp.qgemm_a8w4_blockwise_f32(Xg, blobsA[i], infoA, bg, -6.0, 6.0, out=Yg, ws=ws4)
+        msA = graph_time(gemvA_cold, copiesA)
+        gbsA = nbytesA / msA / 1e6
+        workloads["a8w4_gemv_1x4096x4096_asymmetric"] = {
+            "quantize_plus_gemv_cold_us": round(msA * 1e3, 3), "GBps_cold": round(gbsA, 1),
+            "frac_hbm_peak_cold": round(gbsA / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytesA}
+        del blobsA
+
         # A8W4 GEMM, M in {16, 128}, N=11008, K=4096
         for Mg in (16, 128):
             gg = synth.a8w4_gemm(Mg)

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libqpack.so")
 
 QP_OK, QP_EINVAL, QP_EUNSUPPORTED, QP_EOVERFLOW, QP_ESIZE, QP_EALIGN, QP_EHIP = 0, -1, -2, -3, -4, -5, -6
 QP_S8, QP_S4, QP_S32, QP_F32 = 1, 2, 3, 4
-QP_PER_TENSOR, QP_PER_CHANNEL, QP_BLOCKWISE, QP_DYNAMIC_PER_ROW, QP_BLOCKWISE_BF16 = 0, 1, 2, 3, 4
+QP_PER_TENSOR, QP_PER_CHANNEL, QP_BLOCKWISE, QP_DYNAMIC_PER_ROW = 0, 1, 2, 3
+QP_BLOCKWISE_BF16, QP_BLOCKWISE_ASYM = 4, 5
 QP_ROUND_HALF_EVEN = 0
 
 _STATUS = {0: "QP_OK", -1: "QP_EINVAL", -2: "QP_EUNSUPPORTED", -3: "QP_EOVERFLOW",
@@ -190,11 +191,17 @@ def pack_s8(w: torch.Tensor, scales=None, scale=1.0, zero_points=None, zero_poin
     return qpack_weights(w, desc, k_axis, n_axis)
 
 
-def pack_s4(w: torch.Tensor, scales: torch.Tensor, group_size=32, scale_dtype="f32"):
+def pack_s4(w: torch.Tensor, scales: torch.Tensor, group_size=32, scale_dtype="f32",
+            offsets=None):
     """Pack int4 values (one per int8 byte, in [-8,7]) given as [N, K] with
     f32 group scales [N, ceil(K/group)]; scale_dtype "bf16" stores the
-    scales rounded to bf16."""
+    scales rounded to bf16; `offsets` [N, ceil(K/group)] makes the weights
+    asymmetric (real weight = scale*q + offset)."""
     scheme = {"f32": QP_BLOCKWISE, "bf16": QP_BLOCKWISE_BF16}[scale_dtype]
+    if offsets is not None:
+        assert scale_dtype == "f32", "asymmetric int4 keeps f32 scales"
+        scheme = QP_BLOCKWISE_ASYM
+        scales = torch.stack((offsets.float(), scales.float()), dim=-1).contiguous()
     desc = qtensor(QP_S4, list(w.shape), list(w.stride()), scheme=scheme, scales=scales,
                    group_size=group_size, axis=0)
     return qpack_weights(w, desc, 1, 0)
@@ -216,6 +223,8 @@ def qunpack_weights(blob: torch.Tensor, info: PackedInfo, n_begin=0, n_count=Non
     dev = blob.device
     K = info.K
     groups = 1 if info.format == 1 else (K + info.group - 1) // info.group
+    if info.format == 4:
+        groups *= 2   # (offset, scale) pairs
     w = torch.empty((n_count, K), dtype=torch.int8, device=dev) if values else None
     sc = None
     if scales:

@@ -62,8 +62,17 @@ struct W4 {
   const uint8_t* scale;
   const float* wsum;     // [Npad]
   int64_t N, Npad, Kpad, nblk;
-  int32_t bf16;          // scales stored as bf16
+  int32_t kind;          // 0: f32 scales, 1: bf16 scales, 2: f32 scales + offsets
+  const uint8_t* offs;   // kind 2: f32 group offsets, laid out as the scales
 };
+
+// 16 * the sum of the 8 activation bytes of one word's K (the factor 16
+// matches word_dot16).
+__device__ __forceinline__ int32_t word_sum16(uint32_t a0, uint32_t a1) {
+  return __builtin_amdgcn_sdot4((int)a1, 0x10101010, __builtin_amdgcn_sdot4((int)a0, 0x10101010, 0,
+                                                                           false),
+                                false);
+}
 
 // The four group scales of one channel and block, as f32.  A bf16 value is
 // the upper half of the f32 with the same value.
@@ -93,7 +102,7 @@ __device__ __forceinline__ float4 load_scale4(const uint8_t* p) {
 // from memory (row-major).  Partial sums are reduced across the four lanes
 // of a channel with DPP and then across the waves through LDS, in a fixed
 // order.  Rows m > 0 reuse the weights held in registers.
-template <int NT, bool kFused, bool kBf16>
+template <int NT, bool kFused, int kKind>
 __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__ X, int64_t K,
                                                        const int8_t* __restrict__ qa_g,
                                                        int64_t lda, const float* __restrict__ sa_g,
@@ -115,8 +124,10 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   const int64_t tile = blockIdx.x;
   const int64_t nb = w.nblk;
   const uint8_t* wbase = w.data + tile * nb * 1024 + lane * 16;
+  constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
   const uint8_t* sbase = w.scale + (tile * nb * 64 + ch * 4) * ES;
+  const uint8_t* obase = kAsym ? w.offs + (tile * nb * 64 + ch * 4) * 4 : nullptr;
   // per-channel epilogue operands, fetched up front (off the critical path)
   const int64_t n_out = tile * 16 + (tid & 15);
   float wsum_c = 0.0f, bias_c = 0.0f;
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   const int64_t nbatch = (nb + (int64_t)NW * BB - 1) / ((int64_t)NW * BB);
   for (int64_t j = 0; j < nbatch; ++j) {
     uint4 wv[BB];
-    float4 sv[BB];
+    float4 sv[BB], ov[BB];
     int64_t blk[BB];
 #pragma unroll
     for (int u = 0; u < BB; ++u) {
@@ -157,6 +168,10 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
       wv[u] = *reinterpret_cast<const uint4*>(wbase + blk[u] * 1024);
       const float4 s4 = load_scale4<kBf16>(sbase + blk[u] * 64 * ES);
       sv[u] = b < nb ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (kAsym) {
+        const float4 o4 = load_scale4<false>(obase + blk[u] * 64 * 4);
+        ov[u] = b < nb ? o4 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
     if constexpr (kFused) {
       if (j == 0) {  // quantize the row while the first loads are in flight
@@ -188,10 +203,23 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
           const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
           const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
           const float d3 = (float)word_dot16(wq.w, a[3].x, a[3].y);
-          part[m] = part[m] + sv[u].x * d0;
-          part[m] = part[m] + sv[u].y * d1;
-          part[m] = part[m] + sv[u].z * d2;
-          part[m] = part[m] + sv[u].w * d3;
+          if constexpr (kAsym) {
+            // a group piece's term scale*d + offset*(16 * activation sum) is
+            // formed first, so the running sum takes one addition per piece
+            const float e0 = (float)word_sum16(a[0].x, a[0].y);
+            const float e1 = (float)word_sum16(a[1].x, a[1].y);
+            const float e2 = (float)word_sum16(a[2].x, a[2].y);
+            const float e3 = (float)word_sum16(a[3].x, a[3].y);
+            part[m] = part[m] + __builtin_fmaf(ov[u].x, e0, sv[u].x * d0);
+            part[m] = part[m] + __builtin_fmaf(ov[u].y, e1, sv[u].y * d1);
+            part[m] = part[m] + __builtin_fmaf(ov[u].z, e2, sv[u].z * d2);
+            part[m] = part[m] + __builtin_fmaf(ov[u].w, e3, sv[u].w * d3);
+          } else {
+            part[m] = part[m] + sv[u].x * d0;
+            part[m] = part[m] + sv[u].y * d1;
+            part[m] = part[m] + sv[u].z * d2;
+            part[m] = part[m] + sv[u].w * d3;
+          }
         }
       }
     }
@@ -246,7 +274,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 // before their results are rescaled, two group slots at a time, into two
 // f32 chains (even and odd slots) per output.  K-range partial sums are
 // added in wave order through LDS.
-template <int FM, int FN, int RW, int CW, int KS, bool kPerm, bool kBf16>
+template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind>
 __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict__ qa,
                                                         int64_t lda, const float* __restrict__ sa_g,
                                                         const int32_t* __restrict__ za_g,
@@ -288,15 +316,18 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   const int64_t my_end = (ks * bpw + bpw < nblocks ? ks * bpw + bpw : nblocks);
 
   // ---- weight/scale sources (tile-contiguous blob) ----
+  constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
   const int8_t* wsrc[FN];
   const uint8_t* ssrc[FN];
+  const uint8_t* osrc[FN];
 #pragma unroll
   for (int q = 0; q < FN; ++q) {
     const int64_t n = n0 + q * 16 + (lane & 15);
     wsrc[q] = reinterpret_cast<const int8_t*>(w.data) + (n >> 4) * w.nblk * 1024 +
               (lane & 15) * 64 + 16 * c;
     ssrc[q] = w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
+    osrc[q] = kAsym ? w.offs + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * 4 : nullptr;
   }
 
   // ---- activation direct loads: thread slot s = tid + 256*i of a stage ->
@@ -336,12 +367,13 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
         for (int i = 0; i < 4; ++i) acc[h][f][q][i] = 0.0f;
 
   uint4 wr[P][FN];
-  float4 sr[P][FN];
+  float4 sr[P][FN], orr[P][FN];
   auto load_w = [&](int u, int64_t b) {
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       wr[u][q] = *reinterpret_cast<const uint4*>(wsrc[q] + b * 1024);
       sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
+      if constexpr (kAsym) orr[u][q] = load_scale4<false>(osrc[q] + 64 * 4 * b);
     }
   };
 
@@ -373,17 +405,19 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       }
     }
     uint4 cw4[FN];
-    float4 cs[FN];
+    float4 cs[FN], co[FN];
     const bool live = ks * bpw + j < my_end;
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       cw4[q] = wr[u][q];
       cs[q] = live ? sr[u][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (kAsym) co[q] = live ? orr[u][q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     load_w(u, range_block(ks, j + P));
 #pragma unroll
     for (int t2 = 0; t2 < 4; t2 += 2) {
       v4i d[2][FM][FN];
+      v4i e[2][FM];  // asymmetric: 16 * the rows' activation sums per group
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -397,17 +431,37 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
             d[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, v4i{0, 0, 0, 0}, 0, 0, 0);
           }
         }
+        if constexpr (kAsym) {
+#pragma unroll
+          for (int f = 0; f < FM; ++f) {
+            const long aop = (long)(((uint64_t)ca[f][t2 + h].y << 32) | ca[f][t2 + h].x);
+            e[h][f] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, (long)0x1010101010101010LL,
+                                                            v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int q = 0; q < FN; ++q) {
           const float sc = h == 0 ? (t2 == 0 ? cs[q].x : cs[q].z) : (t2 == 0 ? cs[q].y : cs[q].w);
+          if constexpr (kAsym) {
+            // the group's term scale*d + offset*e first, then one addition
+            const float oc =
+                h == 0 ? (t2 == 0 ? co[q].x : co[q].z) : (t2 == 0 ? co[q].y : co[q].w);
 #pragma unroll
-          for (int f = 0; f < FM; ++f)
+            for (int f = 0; f < FM; ++f)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[h][f][q][i] = __builtin_fmaf(sc, (float)d[h][f][q][i], acc[h][f][q][i]);
+              for (int i = 0; i < 4; ++i)
+                acc[h][f][q][i] = acc[h][f][q][i] + __builtin_fmaf(oc, (float)e[h][f][i],
+                                                                   sc * (float)d[h][f][q][i]);
+          } else {
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[h][f][q][i] = __builtin_fmaf(sc, (float)d[h][f][q][i], acc[h][f][q][i]);
+          }
         }
     }
   };
@@ -488,11 +542,12 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 W4 w4_of(const qp_packed_info* b, const void* blob) {
   const uint8_t* p = static_cast<const uint8_t*>(blob);
   return W4{p + b->data_off, p + b->scale_off, reinterpret_cast<const float*>(p + b->sum_off),
-            b->N, b->Npad, b->Kpad, b->Kpad / 128, b->format == 3 ? 1 : 0};
+            b->N, b->Npad, b->Kpad, b->Kpad / 128, (int32_t)(b->format - 2),
+            b->format == 4 ? p + b->zp_off : nullptr};
 }
 
 qp_status validate_w4(const qp_packed_info* b, int64_t K) {
-  QP_REQUIRE(b && (b->format == 2 || b->format == 3), QP_EINVAL,
+  QP_REQUIRE(b && b->format >= 2 && b->format <= 4, QP_EINVAL,
              "a8w4: weights must be an int4 blob");
   QP_REQUIRE(b->group == 32, QP_EUNSUPPORTED, "a8w4: group size %lld not implemented (32 only)",
              (long long)b->group);
@@ -508,18 +563,19 @@ qp_status launch_gemv_cfg(const float* X, int64_t K, const int8_t* qa, int64_t l
                           bool fused, hipStream_t stream) {
   const unsigned blocks = (unsigned)(w.Npad / 16);
   const size_t lds = fused ? (size_t)w.Kpad : 0;
-  if (fused && w.bf16)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true, true>), dim3(blocks), dim3(NT), lds, stream, X,
-                       K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else if (fused)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, true, false>), dim3(blocks), dim3(NT), lds, stream,
-                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else if (w.bf16)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, true>), dim3(blocks), dim3(NT), lds, stream,
-                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, false>), dim3(blocks), dim3(NT), lds, stream,
-                       X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+#define QP_GEMV(F, KIND)                                                                      \
+  hipLaunchKernelGGL((a8w4_gemv_kernel<NT, F, KIND>), dim3(blocks), dim3(NT), lds, stream, X, K, \
+                     qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy)
+  if (fused) {
+    if (w.kind == 1) QP_GEMV(true, 1);
+    else if (w.kind == 2) QP_GEMV(true, 2);
+    else QP_GEMV(true, 0);
+  } else {
+    if (w.kind == 1) QP_GEMV(false, 1);
+    else if (w.kind == 2) QP_GEMV(false, 2);
+    else QP_GEMV(false, 0);
+  }
+#undef QP_GEMV
   return check_launch("a8w4 gemv");
 }
 
@@ -540,18 +596,19 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   const int64_t by = ceil_div(M, 16 * FM * RW);
   QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w4: M too large");
   const dim3 grid(bx, (unsigned)by);
-  if (perm && w.bf16)
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true, true>), grid, dim3(256), 0,
-                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else if (perm)
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, true, false>), grid, dim3(256), 0,
-                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else if (w.bf16)
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, true>), grid, dim3(256), 0,
-                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
-  else
-    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, false>), grid, dim3(256), 0,
-                       stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
+#define QP_GEMM(PERM, KIND)                                                                \
+  hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, PERM, KIND>), grid, dim3(256), 0, \
+                     stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy)
+  if (perm) {
+    if (w.kind == 1) QP_GEMM(true, 1);
+    else if (w.kind == 2) QP_GEMM(true, 2);
+    else QP_GEMM(true, 0);
+  } else {
+    if (w.kind == 1) QP_GEMM(false, 1);
+    else if (w.kind == 2) QP_GEMM(false, 2);
+    else QP_GEMM(false, 0);
+  }
+#undef QP_GEMM
   return check_launch("a8w4 gemm");
 }
 

@@ -102,19 +102,26 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
 // block), and their scales likewise in quads of four groups (256 bytes), so
 // one wave reads a tile's block, or its scales, as one contiguous piece.
 //
-// kBf16 (blob format 3): each scale is stored rounded to the nearest bf16,
-// ties to even (the upper half of the f32 after adding 0x7FFF plus the
-// lowest kept bit), and the channel's weight sum uses the rounded scales.
+// kKind selects the group-scale storage:
+//  0  f32 scales (blob format 2);
+//  1  bf16 scales (format 3): each scale rounded to the nearest bf16, ties
+//     to even (the upper half of the f32 after adding 0x7FFF plus the lowest
+//     kept bit); the channel's weight sum uses the rounded scales;
+//  2  asymmetric (format 4): the source holds (offset, scale) pairs per
+//     group, real weight = scale*q + offset; scales and offsets are stored
+//     as two f32 arrays of the same layout, and the weight sum is that of
+//     the real weights, sum_g (scale*sum q + offset*(real K in g)).
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <bool kBf16>
+template <int kKind>
 __global__ __launch_bounds__(256) void pack_s4_kernel(
     const int8_t* __restrict__ w, int64_t N, int64_t K, int64_t Kpad, int64_t group, int64_t sn,
     KMap km, const float* __restrict__ sw, int64_t ldsw, uint8_t* __restrict__ blob,
-    int64_t data_off, int64_t scale_off, int64_t sum_off) {
+    int64_t data_off, int64_t scale_off, int64_t sum_off, int64_t off_off) {
+  constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   extern __shared__ int32_t run_sum[];  // Kpad/32 entries
   const int64_t n = blockIdx.x;
   const bool live = n < N;
@@ -146,20 +153,26 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
   }
   if (bad) atomicOr(reinterpret_cast<int32_t*>(blob + kInvalidFlagOffset), 1);
   __syncthreads();
-  // the stored value of group g's scale
+  // the stored values of group g's scale and offset
   auto stored = [&](int64_t g) -> float {
-    const float s = (live && g < Greal) ? sw[n * ldsw + g] : 0.0f;
+    const bool real = live && g < Greal;
+    const float s = real ? sw[n * ldsw + (kAsym ? 2 * g + 1 : g)] : 0.0f;
     if constexpr (kBf16) return __builtin_bit_cast(float, bf16_bits(s) << 16);
     return s;
+  };
+  auto offset = [&](int64_t g) -> float {
+    return (kAsym && live && g < Greal) ? sw[n * ldsw + 2 * g] : 0.0f;
   };
   const int64_t sidx = (n / 16) * Gq * 64 + (n % 16) * 4;
   for (int64_t g = threadIdx.x; g < 4 * Gq; g += blockDim.x) {
     const float s = stored(g);
+    const int64_t e = sidx + (g / 4) * 64 + g % 4;
     if constexpr (kBf16)
-      reinterpret_cast<uint16_t*>(blob + scale_off)[sidx + (g / 4) * 64 + g % 4] =
+      reinterpret_cast<uint16_t*>(blob + scale_off)[e] =
           (uint16_t)(__builtin_bit_cast(uint32_t, s) >> 16);
     else
-      reinterpret_cast<float*>(blob + scale_off)[sidx + (g / 4) * 64 + g % 4] = s;
+      reinterpret_cast<float*>(blob + scale_off)[e] = s;
+    if constexpr (kAsym) reinterpret_cast<float*>(blob + off_off)[e] = offset(g);
   }
   if (threadIdx.x == 0) {
     double acc = 0.0;
@@ -168,6 +181,11 @@ __global__ __launch_bounds__(256) void pack_s4_kernel(
       int64_t gs = 0;
       for (int64_t r = g * rpg; r < (g + 1) * rpg; ++r) gs += run_sum[r];
       acc = acc + (double)stored(g) * (double)gs;
+      if constexpr (kAsym) {
+        int64_t cnt = K - g * group;
+        cnt = cnt < 0 ? 0 : (cnt > group ? group : cnt);
+        acc = acc + (double)offset(g) * (double)cnt;
+      }
     }
     reinterpret_cast<float*>(blob + sum_off)[n] = live ? (float)acc : 0.0f;
   }
@@ -214,11 +232,14 @@ qp_status format_of(const qp_qtensor* w, int32_t* format) {
                "int8 weights support per-tensor or per-channel scales (scheme %d)", w->scheme);
     *format = 1;
   } else if (w->dtype == QP_S4) {
-    QP_REQUIRE(w->scheme == QP_BLOCKWISE || w->scheme == QP_BLOCKWISE_BF16, QP_EUNSUPPORTED,
-               "int4 weights support blockwise scales only (scheme %d)", w->scheme);
+    QP_REQUIRE(w->scheme == QP_BLOCKWISE || w->scheme == QP_BLOCKWISE_BF16 ||
+                   w->scheme == QP_BLOCKWISE_ASYM,
+               QP_EUNSUPPORTED, "int4 weights support blockwise scales only (scheme %d)",
+               w->scheme);
     QP_REQUIRE(w->zero_points == nullptr && w->zero_point == 0, QP_EUNSUPPORTED,
-               "int4 blockwise weights are symmetric: zero points must be absent");
-    *format = w->scheme == QP_BLOCKWISE_BF16 ? 3 : 2;
+               "int4 blockwise weights take no integer zero points (asymmetric weights give "
+               "per-group offsets through QP_BLOCKWISE_ASYM)");
+    *format = w->scheme == QP_BLOCKWISE_BF16 ? 3 : (w->scheme == QP_BLOCKWISE_ASYM ? 4 : 2);
   } else {
     QP_FAIL(QP_EUNSUPPORTED, "weights must be QP_S8 or QP_S4 (dtype %d)", w->dtype);
   }
@@ -333,14 +354,19 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
     if ((st = check_launch("qpack_weights header"))) return st;
     size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / 32);
+    const int64_t groups = ceil_div(v.K, g.group);
     if (format == 3)
-      hipLaunchKernelGGL(pack_s4_kernel<true>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
-                         v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales, ceil_div(v.K, g.group),
-                         blob, g.data_off, g.scale_off, g.sum_off);
+      hipLaunchKernelGGL(pack_s4_kernel<1>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
+                         v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales, groups, blob,
+                         g.data_off, g.scale_off, g.sum_off, g.zp_off);
+    else if (format == 4)
+      hipLaunchKernelGGL(pack_s4_kernel<2>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
+                         v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales, 2 * groups, blob,
+                         g.data_off, g.scale_off, g.sum_off, g.zp_off);
     else
-      hipLaunchKernelGGL(pack_s4_kernel<false>, dim3((unsigned)g.Npad), dim3(256), lds, stream,
-                         src, v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales,
-                         ceil_div(v.K, g.group), blob, g.data_off, g.scale_off, g.sum_off);
+      hipLaunchKernelGGL(pack_s4_kernel<0>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
+                         v.N, v.K, g.Kpad, g.group, v.sn, v.km, w->scales, groups, blob,
+                         g.data_off, g.scale_off, g.sum_off, g.zp_off);
     if ((st = check_launch("qpack_weights int4"))) return st;
     g.has_zero_points = 0;
   }

@@ -43,7 +43,7 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.sum_off = g.scale_off + round_up(4 * g.Npad, kRegionAlign);
     g.zp_off = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
     g.total_bytes = g.zp_off + round_up(4 * g.Npad, kRegionAlign);
-  } else if (format == 2 || format == 3) {
+  } else if (format >= 2 && format <= 4) {
     QP_REQUIRE(group > 0 && group % kRunK4 == 0 && (kBlockK4 % group == 0 || group % kBlockK4 == 0),
                QP_EUNSUPPORTED, "int4 group size must be 32, 64, 128 or a multiple of 128 (got %lld)",
                (long long)group);
@@ -53,11 +53,15 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
     g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
     // scales in quads of 4 groups: [Npad/16][ceil(G/4)][16][4] of f32
     // (format 2) or bf16 (format 3)
-    const int64_t es = format == 2 ? 4 : 2;
-    g.sum_off =
-        g.scale_off + round_up(4 * es * g.Npad * ceil_div(g.Kpad / group, 4), kRegionAlign);
+    const int64_t es = format == 3 ? 2 : 4;
+    const int64_t scale_bytes = round_up(4 * es * g.Npad * ceil_div(g.Kpad / group, 4), kRegionAlign);
+    g.sum_off = g.scale_off + scale_bytes;
     g.zp_off = 0;
     g.total_bytes = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
+    if (format == 4) {  // asymmetric: f32 group offsets, laid out as the scales
+      g.zp_off = g.total_bytes;
+      g.total_bytes += scale_bytes;
+    }
   } else {
     QP_FAIL(QP_EINVAL, "unknown packed format %d", format);
   }

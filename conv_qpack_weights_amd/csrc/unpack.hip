@@ -7,8 +7,8 @@
 // a range of output channels [n0, n0 + count) comes out as logical int8
 // values ([-8, 7] for int4 blobs), their scales (and zero points for int8),
 // and optionally the dequantized f32 weights: sB[n]*(q - zB[n]) for int8,
-// sw[n, k/group]*q for int4.  Only real K is written; padding is never
-// exposed.
+// sw[n, k/group]*q for int4 (plus the group offset for asymmetric int4).
+// Only real K is written; padding is never exposed.
 #include "qp_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -69,8 +69,12 @@ __global__ __launch_bounds__(256) void unpack_s4_kernel(const uint8_t* __restric
   if (deq) {
     const int64_t g = k / b.group;
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
-    const float s = scale_at(blob, b, ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4);
-    deq[i * ldd + k] = s * (float)q;
+    const int64_t e = ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4;
+    const float s = scale_at(blob, b, e);
+    if (b.format == 4)  // asymmetric: scale*q + offset
+      deq[i * ldd + k] = s * (float)q + reinterpret_cast<const float*>(blob + b.zp_off)[e];
+    else
+      deq[i * ldd + k] = s * (float)q;
   }
 }
 
@@ -91,8 +95,13 @@ __global__ __launch_bounds__(256) void unpack_scales_kernel(const uint8_t* __res
     if (zp) zp[i] = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
   } else if (scales) {
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
-    scales[i * lds + g] =
-        scale_at(blob, b, ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4);
+    const int64_t e = ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4;
+    if (b.format == 4) {  // (offset, scale) pairs, as given to the packer
+      scales[i * lds + 2 * g] = reinterpret_cast<const float*>(blob + b.zp_off)[e];
+      scales[i * lds + 2 * g + 1] = scale_at(blob, b, e);
+    } else {
+      scales[i * lds + g] = scale_at(blob, b, e);
+    }
   }
 }
 
@@ -107,7 +116,7 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   using namespace qp;
   clear_error();
   QP_REQUIRE(info && packed_dev, QP_EINVAL, "qunpack_weights: null blob");
-  QP_REQUIRE(info->format >= 1 && info->format <= 3, QP_EINVAL,
+  QP_REQUIRE(info->format >= 1 && info->format <= 4, QP_EINVAL,
              "qunpack_weights: unknown blob format %d", info->format);
   QP_REQUIRE(n_begin >= 0 && n_count >= 0 && n_begin + n_count <= info->N, QP_EINVAL,
              "qunpack_weights: channels [%lld, %lld) outside [0, %lld)", (long long)n_begin,
@@ -117,8 +126,9 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   QP_REQUIRE(info->format == 1 || !zp_out, QP_EINVAL,
              "qunpack_weights: int4 blobs have no zero points (zp_out must be NULL)");
   const int64_t groups = info->format == 1 ? 1 : ceil_div(info->K, info->group);
-  QP_REQUIRE(!scales_out || info->format == 1 || lds >= groups, QP_EINVAL,
-             "qunpack_weights: lds smaller than the %lld groups", (long long)groups);
+  const int64_t per_row = info->format == 4 ? 2 * groups : groups;
+  QP_REQUIRE(!scales_out || info->format == 1 || lds >= per_row, QP_EINVAL,
+             "qunpack_weights: lds smaller than %lld", (long long)per_row);
   if (n_count == 0) return QP_OK;
   const uint8_t* blob = static_cast<const uint8_t*>(packed_dev);
   const qp_packed_info b = *info;

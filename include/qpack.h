@@ -55,7 +55,11 @@ typedef enum {
   /* blockwise int4 whose f32 group scales are stored rounded to bf16
    * (nearest, ties to even), as the KleidiAI kernel keeps them ([KLEIDI]
    * review of the wrapper's scale conversion); blob format 3 */
-  QP_BLOCKWISE_BF16 = 4
+  QP_BLOCKWISE_BF16 = 4,
+  /* asymmetric blockwise int4: `scales` holds f32 (offset, scale) pairs
+   * [N][ceil(K/group)][2], real weight = scale*q + offset, the pair order of
+   * [MNN] _computeReorderQuantInfo's quantization info; blob format 4 */
+  QP_BLOCKWISE_ASYM = 5
 } qp_qscheme;
 
 typedef enum { QP_ROUND_HALF_EVEN = 0 } qp_rounding;
@@ -170,9 +174,12 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  *   float ((n/16)*ceil(G/4) + g/4)*64 + (n%16)*4 + g%4, G = Kpad/group
  *   (zero for groups past K).  Format 3 (scheme QP_BLOCKWISE_BF16) stores
  *   the same scale array as bf16, each the given f32 rounded to nearest,
- *   ties to even, at the same element index (2 bytes each);
+ *   ties to even, at the same element index (2 bytes each).  Format 4
+ *   (scheme QP_BLOCKWISE_ASYM) adds, after wsum, the f32 group offsets in
+ *   the layout of the scales (zp_off points there);
  *   f32 wsum[Npad] = sum_g sw[n,g] * sum_{k in g} w[n,k] (with the stored
- *   scales), accumulated in fp64
+ *   scales; format 4 adds offset[n,g] * (real K in g): the sum of the real
+ *   weights), accumulated in fp64
  *   (the weight kernel sum that folds the activation zero point,
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
  * All padding bytes are zero.  int4 values outside [-8,7] set the header word
@@ -198,11 +205,13 @@ qp_status qp_packed_info_from_header(const void* header_host, qp_packed_info* in
  *   w_out      int8 [n_count][ldw] (ldw >= K): the logical values (int4
  *              blobs: [-8, 7]); NULL to skip.
  *   scales_out int8 blob: f32 [n_count]; int4 blob: f32 [n_count][lds]
- *              (lds >= ceil(K/group)); NULL to skip.
+ *              (lds >= ceil(K/group)); asymmetric int4 (format 4): the
+ *              (offset, scale) pairs, lds >= 2*ceil(K/group); NULL to skip.
  *   zp_out     int8 blob: int32 [n_count] (zeros when symmetric); must be
  *              NULL for int4 blobs.
  *   deq_out    f32 [n_count][ldd] (ldd >= K): sB[n]*(q - zB[n]) for int8,
- *              sw[n, k/group]*q for int4, one f32 rounding; NULL to skip.
+ *              sw[n, k/group]*q for int4, one f32 rounding (format 4: then
+ *              plus the group offset, a second rounding); NULL to skip.
  * Padding (K..Kpad, N..Npad) is never written.  Asynchronous on `stream`.
  */
 qp_status qunpack_weights(const qp_packed_info* info, const void* packed_dev, int64_t n_begin,

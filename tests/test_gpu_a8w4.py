@@ -134,3 +134,55 @@ def test_a8w4_bf16_scales_gemm_workload(qp, orc, M):
                                             (130, 48, 320, False)])
 def test_a8w4_bf16_scales_shapes(qp, orc, M, N, K, prequant):
     _case_bf16(qp, orc, synth.a8w4(synth.BASE_SEED + 11 * M + N + K, M, N, K), prequant=prequant)
+
+
+# ---- asymmetric int4 (blob format 4): a float offset per group, oracle O6c
+def _offsets(d, seed):
+    rng = np.random.default_rng(seed)
+    return rng.uniform(-0.05, 0.05, d["sw"].shape).astype(np.float32)
+
+
+def _case_asym(qp, orc, d, bw, rows=None, prequant=False):
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]), offsets=_dev(bw))
+    assert info.format == 4
+    if prequant:
+        import torch
+        M = d["X"].shape[0]
+        q = torch.zeros((M, info.Kpad), dtype=torch.int8, device="cuda")
+        q, s, z = qp.qquantize_rows_s8(_dev(d["X"]), q=q)
+        Y = _host(qp.qgemm_a8w4_prequant_f32(q, s, z, blob, info, _dev(d["bias"]),
+                                             d["clamp_lo"], d["clamp_hi"]))
+    else:
+        Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
+                                              d["clamp_lo"], d["clamp_hi"]))
+    X = d["X"] if rows is None else d["X"][rows]
+    want = orc.a8w4_forward_asym(X, d["W"], d["sw"], bw, d["bias"], d["clamp_lo"],
+                                 d["clamp_hi"])
+    _check_close(Y if rows is None else Y[rows], want, "asymmetric a8w4 output")
+    return blob, info
+
+
+def test_a8w4_asym_gemv_workload(qp, orc):
+    d = synth.a8w4_gemv()
+    bw = _offsets(d, 1)
+    blob, info = _case_asym(qp, orc, d, bw)
+    _, sc, _, dq = qp.qunpack_weights(blob, info, values=False, dequant=True)
+    pairs = _host(sc).reshape(4096, -1, 2)
+    assert np.array_equal(pairs[..., 0], bw) and np.array_equal(pairs[..., 1], d["sw"])
+    assert np.array_equal(_host(dq), orc.dequant_weights_s4(d["W"], d["sw"], 32, bw))
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_a8w4_asym_gemm_workload(qp, orc, M):
+    d = synth.a8w4_gemm(M)
+    rows = None if M == 16 else np.r_[0:8, 120:128]
+    _case_asym(qp, orc, d, _offsets(d, M), rows)
+
+
+@pytest.mark.parametrize("M,N,K,prequant", [(1, 70, 96, False), (1, 33, 1000, False),
+                                            (3, 64, 4096, True), (5, 77, 1000, False),
+                                            (33, 48, 160, True), (40, 33, 64, False),
+                                            (130, 48, 320, False)])
+def test_a8w4_asym_shapes(qp, orc, M, N, K, prequant):
+    d = synth.a8w4(synth.BASE_SEED + 13 * M + N + K, M, N, K)
+    _case_asym(qp, orc, d, _offsets(d, M + N + K), prequant=prequant)
