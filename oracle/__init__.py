@@ -71,6 +71,9 @@ _SIGS = {
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
     "orc_round_bf16_array": (None, [_I64, _P, _P]),
+    "orc_quantize_rows_s8_blocked": (None, [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64]),
+    "orc_a8w4_blockwise_blockq": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _I64, _P,
+                                            _I64, _P, _I64, _P, _F, _F, _P, _I64]),
     "orc_a8w4_blockwise_asym": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I64, _P,
                                           _P, _I64, _P, _F, _F, _P, _I64]),
     "orc_dequant_matrix_f32": (C.c_int, [_I64, _I64, _P, _F, _P, _P, _F, _F, _P]),
@@ -228,6 +231,45 @@ def requant_matrix(acc, s_a, s_b, s_out, zp_out, relu):
                                   int(zp_out), int(bool(relu)), _ptr(out), C.byref(nd))
     _check(rc, "orc_requant_matrix")
     return out, nd.value
+
+
+# ---------------------------------------------------------------- O5b / O6d
+def quantize_rows_s8_blocked(X, block=32):
+    """O5b: O5 on every block of `block` K of every row -> q, scale [M,G], zp [M,G]."""
+    X = _arr(X, np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    M, K = X.shape
+    G = (K + block - 1) // block
+    q = np.zeros((M, K), dtype=np.int8)
+    sc = np.zeros((M, G), dtype=np.float32)
+    zp = np.zeros((M, G), dtype=np.int32)
+    lib().orc_quantize_rows_s8_blocked(M, K, block, _ptr(X), K, _ptr(q), K, _ptr(sc), _ptr(zp), G)
+    return q, sc, zp
+
+
+def a8w4_blockwise_blockq(qa, sa, za, qw, sw, bias, clamp_lo, clamp_hi, group=32):
+    """O6d: int4 group weights x per-block quantized activations."""
+    qa = _arr(qa, np.int8)
+    qw = _arr(qw, np.int8)
+    sw = _arr(sw, np.float32)
+    sa = _arr(sa, np.float32)
+    za = _arr(za, np.int32)
+    M, K = qa.shape
+    N = qw.shape[0]
+    biasv = None if bias is None else _arr(bias, np.float32)
+    Y = np.zeros((M, N), dtype=np.float32)
+    rc = lib().orc_a8w4_blockwise_blockq(M, N, K, group, _ptr(qa), K, _ptr(sa), _ptr(za),
+                                         sa.shape[1], _ptr(qw), K, _ptr(sw), sw.shape[1],
+                                         _ptr(biasv), float(clamp_lo), float(clamp_hi), _ptr(Y), N)
+    _check(rc, "orc_a8w4_blockwise_blockq")
+    return Y
+
+
+def a8w4_forward_blockq(X, qw, sw, bias, clamp_lo, clamp_hi, group=32):
+    """Per-block dynamic quantization (O5b, blocks = the weight groups) then O6d."""
+    qa, sa, za = quantize_rows_s8_blocked(X, group)
+    return a8w4_blockwise_blockq(qa, sa, za, qw, sw, bias, clamp_lo, clamp_hi, group)
 
 
 # ---------------------------------------------------------------- O6c

@@ -451,6 +451,26 @@ void orc_quantize_rows_s8(int64_t M, int64_t K, const float* X, int64_t ldx, int
 }
 
 /* ========================================================================
+ * O5b -- dynamic quantization per row AND per block of K.  [MNN]
+ * DenseConvInt8TiledExecutor::onResize: with dynamicQuantOption 2 the input
+ * is cut into as many K blocks as the weights (mInputBlockNum = mBlockNum)
+ * and BatchAsyDynamicQuant computes a scale and zero point per block.
+ * Reading: O5's op sequence applied to each block of `block` consecutive K
+ * of a row on its own (the last block may be shorter).
+ * ====================================================================== */
+void orc_quantize_rows_s8_blocked(int64_t M, int64_t K, int64_t block, const float* X,
+                                  int64_t ldx, int8_t* Q, int64_t ldq, float* scale,
+                                  int32_t* zp, int64_t ldsz) {
+  int64_t G = orc_ceil_div(K, block);
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t g = 0; g < G; ++g) {
+      int64_t k0 = g * block, len = K - k0 < block ? K - k0 : block;
+      orc_quantize_row_s8(X + m * ldx + k0, len, Q + m * ldq + k0, &scale[m * ldsz + g],
+                          &zp[m * ldsz + g]);
+    }
+}
+
+/* ========================================================================
  * O5s -- dynamic per-row symmetric quantization to int8.
  * [MNN] BatchSymDynamicQuant: per row the largest magnitude (MNNAbsMax), a
  * scale from it (MNNQuantScale), then the codes (MNNDynamicQuant) with the
@@ -531,6 +551,39 @@ int orc_a8w4_blockwise(int64_t M, int64_t N, int64_t K, int64_t group, const int
         sum += (double)sw[n * ldsw + g] * (double)d;
       }
       double y = (double)sa[m] * sum + (bias ? (double)bias[n] : 0.0);
+      if (y < (double)clamp_lo) y = (double)clamp_lo;
+      if (y > (double)clamp_hi) y = (double)clamp_hi;
+      Y[m * ldy + n] = (float)y;
+    }
+  return 0;
+}
+
+/* ========================================================================
+ * O6d -- int4 group weights times activations quantized per block (O5b),
+ * the activation blocks being the weight groups: each group then has its
+ * own activation scale and zero point as well as its weight scale.
+ *   Y[m,n] = clamp(sum_g sa[m,g]*sw[n,g] * sum_{k in g} (qa[m,k]-za[m,g])*qw[n,k]
+ *                  + bias[n], lo, hi)
+ * Group sums exact in integers, the rest in fp64, one rounding to f32.
+ * ====================================================================== */
+int orc_a8w4_blockwise_blockq(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t* qa,
+                              int64_t lda, const float* sa, const int32_t* za, int64_t ldsz,
+                              const int8_t* qw, int64_t ldw, const float* sw, int64_t ldsw,
+                              const float* bias, float clamp_lo, float clamp_hi, float* Y,
+                              int64_t ldy) {
+  if (M < 0 || N < 0 || K < 0 || group <= 0) return ORC_EINVAL;
+  int64_t G = orc_ceil_div(K, group);
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = 0.0;
+      for (int64_t g = 0; g < G; ++g) {
+        int64_t d = 0;
+        int64_t k1 = (g + 1) * group < K ? (g + 1) * group : K;
+        for (int64_t k = g * group; k < k1; ++k)
+          d += ((int64_t)qa[m * lda + k] - za[m * ldsz + g]) * (int64_t)qw[n * ldw + k];
+        sum += (double)sa[m * ldsz + g] * (double)sw[n * ldsw + g] * (double)d;
+      }
+      double y = sum + (bias ? (double)bias[n] : 0.0);
       if (y < (double)clamp_lo) y = (double)clamp_lo;
       if (y > (double)clamp_hi) y = (double)clamp_hi;
       Y[m * ldy + n] = (float)y;

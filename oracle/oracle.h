@@ -39,6 +39,16 @@ int orc_gemm_affine_points(int64_t npts, const int64_t* ms, const int64_t* ns, i
                            const int8_t* B, int64_t b_sk, int64_t b_sn, const int32_t* zB,
                            const int32_t* bias, int64_t* acc);
 
+/* ---- O5b / O6d: per-block activation quantization ------------------------ */
+void orc_quantize_rows_s8_blocked(int64_t M, int64_t K, int64_t block, const float* X,
+                                  int64_t ldx, int8_t* Q, int64_t ldq, float* scale,
+                                  int32_t* zp, int64_t ldsz);
+int orc_a8w4_blockwise_blockq(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t* qa,
+                              int64_t lda, const float* sa, const int32_t* za, int64_t ldsz,
+                              const int8_t* qw, int64_t ldw, const float* sw, int64_t ldsw,
+                              const float* bias, float clamp_lo, float clamp_hi, float* Y,
+                              int64_t ldy);
+
 /* ---- O6c: asymmetric int4 (scale and offset per group) ------------------- */
 int orc_a8w4_blockwise_asym(int64_t M, int64_t N, int64_t K, int64_t group, const int8_t* qa,
                             int64_t lda, const float* sa, const int32_t* za, const int8_t* qw,

@@ -539,3 +539,70 @@ def test_o9_asymmetric_dequant_adds_the_group_offset(orc):
         for k in range(70):
             p = np.float32(float(sw[n, k // 32]) * int(W4[n, k]))     # exact product, one rounding
             assert got[n, k] == np.float32(float(p) + float(bw[n, k // 32]))
+
+
+# ------------------------------------------------------------------ O5b / O6d
+def test_o5b_blocks_are_independent_rows(orc):
+    """Each block of a row is quantized exactly as O5 quantizes that block
+    given as a row of its own; block = K is O5 itself."""
+    rng = np.random.default_rng(51)
+    X = (rng.standard_normal((3, 100)) * rng.uniform(0.1, 10, (3, 1))).astype(np.float32)
+    X[1, 32:64] = 0.0                       # an all-zero block: scale 1, zp 0
+    X[2, 64:96] = np.abs(X[2, 64:96]) + 1   # an all-positive block
+    q, sc, zp = orc.quantize_rows_s8_blocked(X, 32)
+    assert sc.shape == (3, 4) and zp.shape == (3, 4)
+    for m in range(3):
+        for g in range(4):
+            qq, ss, zz = orc.quantize_rows_s8(X[m, 32 * g:32 * g + 32])
+            assert np.array_equal(q[m, 32 * g:32 * g + 32], qq[0])
+            assert sc[m, g] == ss[0] and zp[m, g] == zz[0]
+    assert sc[1, 1] == 1.0 and zp[1, 1] == 0 and not q[1, 32:64].any()
+    qa, sa, za = orc.quantize_rows_s8(X)
+    qb, sb, zb = orc.quantize_rows_s8_blocked(X, 100)
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb[:, 0]) and np.array_equal(za, zb[:, 0])
+    # finer blocks never quantize worse: every block's error bound is its own scale
+    err = np.abs((q.astype(np.float64) - np.repeat(zp, 32, 1)[:, :100]) *
+                 np.repeat(sc, 32, 1)[:, :100] - X)
+    assert np.all(err <= np.repeat(sc, 32, 1)[:, :100])
+
+
+def test_o6d_uniform_activation_params_reduce_to_o6(orc):
+    rng = np.random.default_rng(52)
+    M, N, K = 3, 7, 96
+    qa = _rand_i8(rng, (M, K))
+    qw = _rand_i8(rng, (N, K), -8, 7)
+    sw = rng.uniform(0.002, 0.02, (N, 3)).astype(np.float32)
+    sa = rng.uniform(0.01, 0.05, M).astype(np.float32)
+    za = rng.integers(-100, 100, M).astype(np.int32)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    got = orc.a8w4_blockwise_blockq(qa, np.repeat(sa[:, None], 3, 1), np.repeat(za[:, None], 3, 1),
+                                    qw, sw, bias, -6, 6)
+    want = orc.a8w4_blockwise(qa, sa, za, qw, sw, bias, -6, 6)
+    assert np.max(np.abs(got.astype(np.float64) - want)) <= 1e-6 * np.max(np.abs(want))
+
+
+def test_o6d_brute_force_rational(orc):
+    rng = np.random.default_rng(53)
+    M, N, K = 2, 4, 70
+    qa = _rand_i8(rng, (M, K))
+    qw = _rand_i8(rng, (N, K), -8, 7)
+    sw = rng.uniform(0.002, 0.02, (N, 3)).astype(np.float32)
+    sa = rng.uniform(0.01, 0.05, (M, 3)).astype(np.float32)
+    za = rng.integers(-128, 128, (M, 3)).astype(np.int32)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    y = orc.a8w4_blockwise_blockq(qa, sa, za, qw, sw, bias, -1e30, 1e30)
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                g = k // 32
+                s += Fraction(float(sa[m, g])) * Fraction(float(sw[n, g])) \
+                    * (int(qa[m, k]) - int(za[m, g])) * int(qw[n, k])
+            exact = s + Fraction(float(bias[n]))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 23) \
+                + Fraction(1, 2 ** 40)
+    # a block's activation zero point touches only its own group
+    za2 = za.copy()
+    za2[0, 2] += 5
+    y2 = orc.a8w4_blockwise_blockq(qa, sa, za2, qw, sw, bias, -1e30, 1e30)
+    assert np.array_equal(y2[1], y[1]) and not np.array_equal(y2[0], y[0])
