@@ -303,7 +303,23 @@ def main():
         workloads["a8w4_gemv_1x4096x4096_bf16_scales"] = {
             "quantize_plus_gemv_cold_us": round(ms16 * 1e3, 3), "GBps_cold": round(gbs16, 1),
             "frac_hbm_peak_cold": round(gbs16 / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes16}
-        del blobs16
+
+        # per-block activation quantization (quantizer + GEMV launches)
+        wsq = torch.empty(qp.qgemm_a8w4_blockq_f32_ws_size(1, info4), dtype=torch.uint8,
+                          device=dev)
+        idxq = [0]
+
+        def gemvq_cold():
+            i = idxq[0] = (idxq[0] + 1) % copies
+            qp.qgemm_a8w4_blockq_f32(Xg, blobs[i], info4, bg, -6.0, 6.0, out=Yg, ws=wsq)
+        blobs = [blob4] + [blob4.clone() for _ in range(copies - 1)]
+        msq = graph_time(gemvq_cold, copies)
+        workloads["a8w4_gemv_1x4096x4096_blockq"] = {
+            "quantize_plus_gemv_cold_us": round(msq * 1e3, 3),
+            "GBps_cold": round(nbytes_alg / msq / 1e6, 1),
+            "frac_hbm_peak_cold": round(nbytes_alg / msq / 1e6 / PEAK_HBM_GBS, 4),
+            "note": "activations quantized per block of 32; two launches"}
+        del blobs, blobs16
 
         # asymmetric int4 (a float offset per group, blob format 4)
         bw = torch.from_numpy(np.random.default_rng(1).uniform(
@@ -347,6 +363,18 @@ def main():
                 "frac_hbm_peak": round(byt / msg / 1e6 / PEAK_HBM_GBS, 4),
                 "TOPS": round(2 * mac / msg / 1e9, 2),
                 "frac_mfma_peak": round(2 * mac / msg / 1e9 / PEAK_INT8_TOPS, 5)}
+            # the same product with the activations quantized per block of 32
+            wsb = torch.empty(qp.qgemm_a8w4_blockq_f32_ws_size(Mg, i4), dtype=torch.uint8,
+                              device=dev)
+
+            def gm_bq_cold():
+                k = j[0] = (j[0] + 1) % cps
+                qp.qgemm_a8w4_blockq_f32(Xm, bl[k], i4, bm, -6.0, 6.0, out=Ym, ws=wsb)
+            msb = graph_time(gm_bq_cold, cps, 10)
+            workloads["a8w4_gemm_%dx11008x4096_blockq" % Mg] = {
+                "cold_us": round(msb * 1e3, 2), "GBps": round(byt / msb / 1e6, 1),
+                "frac_hbm_peak": round(byt / msb / 1e6 / PEAK_HBM_GBS, 4),
+                "note": "per-block (32) activation quantization + product, two launches"}
             del bl
 
         # dynamic per-row activation quantization (asymmetric and symmetric),

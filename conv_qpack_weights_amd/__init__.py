@@ -73,6 +73,13 @@ SIGNATURES = {
                                      _P]),
     "qgemm_s8s8_dequant_f32": (C.c_int, [_QT, _P, _PI, _P, _P, _F, _F, _P, _I64, _P,
                                          C.c_size_t, _P]),
+    "qquantize_rows_s8_blocked": (C.c_int, [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _P,
+                                            _I64, _P]),
+    "qgemm_a8w4_blockq_f32_ws_size": (C.c_int, [_I64, _PI, _SZ]),
+    "qgemm_a8w4_blockq_f32": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P, _I64, _P,
+                                        C.c_size_t, _P]),
+    "qgemm_a8w4_blockq_prequant_f32": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _PI, _P, _P, _F,
+                                                 _F, _P, _I64, _P]),
     "qgemm_a8w4_blockwise_f32_ws_size": (C.c_int, [_I64, _PI, _SZ]),
     "qgemm_a8w4_blockwise_f32": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P, _I64,
                                            _P, C.c_size_t, _P]),
@@ -360,6 +367,59 @@ def qgemm_a8w4_prequant_f32(qa: torch.Tensor, sa: torch.Tensor, za: torch.Tensor
                                         C.byref(info), _ptr(blob), _ptr(bias), clamp_lo, clamp_hi,
                                         _ptr(out), out.stride(0), _stream(qa.device)),
            "qgemm_a8w4_prequant_f32")
+    return out
+
+
+def qquantize_rows_s8_blocked(x: torch.Tensor, block=32, kpad=None, q=None, scale=None,
+                              zp=None):
+    """Per-(row, block of 32) dynamic quantization: q [M, kpad], scale and zp
+    [M, kpad/32]."""
+    assert x.dim() == 2 and x.dtype == torch.float32 and x.stride(1) == 1
+    M, K = x.shape
+    kpad = ((K + 31) // 32) * 32 if kpad is None else kpad
+    nb = kpad // 32
+    q = torch.empty((M, kpad), dtype=torch.int8, device=x.device) if q is None else q
+    scale = torch.empty((M, nb), dtype=torch.float32, device=x.device) if scale is None else scale
+    zp = torch.empty((M, nb), dtype=torch.int32, device=x.device) if zp is None else zp
+    _check(_lib.qquantize_rows_s8_blocked(_ptr(x), M, K, x.stride(0), block, kpad, _ptr(q),
+                                          q.stride(0), _ptr(scale), _ptr(zp), scale.stride(0),
+                                          _stream(x.device)), "qquantize_rows_s8_blocked")
+    return q, scale, zp
+
+
+def qgemm_a8w4_blockq_f32_ws_size(M: int, info: PackedInfo) -> int:
+    n = C.c_size_t()
+    _check(_lib.qgemm_a8w4_blockq_f32_ws_size(M, C.byref(info), C.byref(n)),
+           "qgemm_a8w4_blockq_f32_ws_size")
+    return n.value
+
+
+def qgemm_a8w4_blockq_f32(X: torch.Tensor, blob: torch.Tensor, info: PackedInfo, bias=None,
+                          clamp_lo=-float("inf"), clamp_hi=float("inf"), out=None, ws=None):
+    assert X.dtype == torch.float32 and X.dim() == 2 and X.stride(1) == 1
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = _alloc_bytes(qgemm_a8w4_blockq_f32_ws_size(M, info), X.device)
+    _check(_lib.qgemm_a8w4_blockq_f32(_ptr(X), M, K, X.stride(0), C.byref(info), _ptr(blob),
+                                      _ptr(bias), clamp_lo, clamp_hi, _ptr(out), out.stride(0),
+                                      _ptr(ws), ws.numel(), _stream(X.device)),
+           "qgemm_a8w4_blockq_f32")
+    return out
+
+
+def qgemm_a8w4_blockq_prequant_f32(qa: torch.Tensor, sa: torch.Tensor, za: torch.Tensor,
+                                   blob: torch.Tensor, info: PackedInfo, bias=None,
+                                   clamp_lo=-float("inf"), clamp_hi=float("inf"), out=None):
+    M = qa.shape[0]
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=qa.device)
+    _check(_lib.qgemm_a8w4_blockq_prequant_f32(_ptr(qa), M, qa.stride(0), _ptr(sa), _ptr(za),
+                                               sa.stride(0), C.byref(info), _ptr(blob),
+                                               _ptr(bias), clamp_lo, clamp_hi, _ptr(out),
+                                               out.stride(0), _stream(qa.device)),
+           "qgemm_a8w4_blockq_prequant_f32")
     return out
 
 

@@ -43,6 +43,22 @@ __device__ __forceinline__ int32_t word_dot16(uint32_t w, uint32_t a0, uint32_t 
   return __builtin_amdgcn_sdot4((int)a1, (int)nib_hi16(w), d, false);
 }
 
+// 16 * the sum of the eight int4 values of one word
+__device__ __forceinline__ int32_t word_wsum16(uint32_t w) {
+  return __builtin_amdgcn_sdot4((int)nib_hi16(w), 0x01010101,
+                                __builtin_amdgcn_sdot4((int)nib_lo16(w), 0x01010101, 0, false),
+                                false);
+}
+
+// Per-block activation quantization: S16 already holds
+// 16 * sum_g sa[g]*sw[g]*sum (qa - za[g])*q, so only the bias remains.
+__device__ __forceinline__ float finish_bq(float S16, float bias, float lo, float hi) {
+  float y = S16 * 0.0625f + bias;
+  y = y < lo ? lo : y;
+  y = y > hi ? hi : y;
+  return y;
+}
+
 __device__ __forceinline__ float finish(float S16, float sa, int32_t za, float wsum, float bias,
                                         float lo, float hi) {
   // y = sa * (S16/16) - (sa*za) * wsum + bias, then clamp
@@ -102,7 +118,11 @@ __device__ __forceinline__ float4 load_scale4(const uint8_t* p) {
 // from memory (row-major).  Partial sums are reduced across the four lanes
 // of a channel with DPP and then across the waves through LDS, in a fixed
 // order.  Rows m > 0 reuse the weights held in registers.
-template <int NT, bool kFused, int kKind>
+// kBQ: the activations were quantized per block of 32 (one scale and zero
+// point per row and group, [M][ldsz]); one row.  Each group piece then
+// contributes sa[g]*sw[g] * (dot - za[g] * sum q), exactly in integers up to
+// that product.
+template <int NT, bool kFused, int kKind, bool kBQ = false>
 __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__ X, int64_t K,
                                                        const int8_t* __restrict__ qa_g,
                                                        int64_t lda, const float* __restrict__ sa_g,
@@ -111,6 +131,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
                                                        const float* __restrict__ bias, float lo,
                                                        float hi, float* __restrict__ Y,
                                                        int64_t ldy) {
+  static_assert(!kBQ || (!kFused && kKind != 2), "per-block activations: prequantized, symmetric");
   constexpr int NW = NT / 64;
   constexpr int BB = 4;      // blocks a wave holds in registers per batch
   constexpr int MR = 4;      // rows per call (M = 1 fused, M <= 4 prequantized)
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   int32_t za_m[MR];
   if constexpr (kFused) {
     xfirst = quantize_row_first<NT, 8>(X, K, xvec);  // before the weights
-  } else {
+  } else if constexpr (!kBQ) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       sa_m[m] = m < M ? sa_g[m] : 0.0f;
@@ -159,7 +180,8 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   const int64_t nbatch = (nb + (int64_t)NW * BB - 1) / ((int64_t)NW * BB);
   for (int64_t j = 0; j < nbatch; ++j) {
     uint4 wv[BB];
-    float4 sv[BB], ov[BB];
+    float4 sv[BB], ov[BB], saq[BB];
+    int4 zaq[BB];
     int64_t blk[BB];
 #pragma unroll
     for (int u = 0; u < BB; ++u) {
@@ -171,6 +193,10 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
       if constexpr (kAsym) {
         const float4 o4 = load_scale4<false>(obase + blk[u] * 64 * 4);
         ov[u] = b < nb ? o4 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if constexpr (kBQ) {  // the row's four group parameters of this block
+        saq[u] = *reinterpret_cast<const float4*>(sa_g + 4 * blk[u]);
+        zaq[u] = *reinterpret_cast<const int4*>(za_g + 4 * blk[u]);
       }
     }
     if constexpr (kFused) {
@@ -199,6 +225,18 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
             for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint2*>(ab + 32 * t);
           }
           const uint4 wq = wv[u];
+          if constexpr (kBQ) {
+            const int32_t z0 = zaq[u].x, z1 = zaq[u].y, z2 = zaq[u].z, z3 = zaq[u].w;
+            const int32_t e0 = word_dot16(wq.x, a[0].x, a[0].y) - z0 * word_wsum16(wq.x);
+            const int32_t e1 = word_dot16(wq.y, a[1].x, a[1].y) - z1 * word_wsum16(wq.y);
+            const int32_t e2 = word_dot16(wq.z, a[2].x, a[2].y) - z2 * word_wsum16(wq.z);
+            const int32_t e3 = word_dot16(wq.w, a[3].x, a[3].y) - z3 * word_wsum16(wq.w);
+            part[m] = part[m] + (saq[u].x * sv[u].x) * (float)e0;
+            part[m] = part[m] + (saq[u].y * sv[u].y) * (float)e1;
+            part[m] = part[m] + (saq[u].z * sv[u].z) * (float)e2;
+            part[m] = part[m] + (saq[u].w * sv[u].w) * (float)e3;
+            continue;
+          }
           const float d0 = (float)word_dot16(wq.x, a[0].x, a[0].y);
           const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
           const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
@@ -245,7 +283,11 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
             za = za_m[r];
           }
       }
-      if (n_out < w.N) Y[m * ldy + n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
+      if constexpr (kBQ) {
+        if (n_out < w.N) Y[m * ldy + n_out] = finish_bq(S, bias_c, lo, hi);
+      } else {
+        if (n_out < w.N) Y[m * ldy + n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
+      }
     }
     __syncthreads();
   }
@@ -274,16 +316,23 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 // before their results are rescaled, two group slots at a time, into two
 // f32 chains (even and odd slots) per output.  K-range partial sums are
 // added in wave order through LDS.
-template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind>
+// kBQ (activations quantized per block of 32: sa, za are [M][ldsz]): the
+// MFMA is issued the other way round, (weights, activations), so a lane
+// holds channels 4*(l/16)+i of row l%16 and needs one row's group
+// parameters; a second MFMA against the row's zero point replicated over K
+// gives za*sum q, and each group adds sa*sw * (d - that) per output.
+template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind, bool kBQ = false>
 __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict__ qa,
                                                         int64_t lda, const float* __restrict__ sa_g,
                                                         const int32_t* __restrict__ za_g,
                                                         int64_t M, W4 w,
                                                         const float* __restrict__ bias, float lo,
                                                         float hi, float* __restrict__ Y,
-                                                        int64_t ldy) {
+                                                        int64_t ldy, int64_t ldsz) {
+  static_assert(!kBQ || kKind != 2, "per-block activations take symmetric weights");
   static_assert(RW * CW * KS == 4, "four waves");
-  constexpr int P = FM * FN >= 4 ? 3 : 5;   // weight prefetch depth in blocks
+  // weight prefetch depth in blocks (kBQ holds more per block: two)
+  constexpr int P = kBQ ? 2 : (FM * FN >= 4 ? 3 : 5);
   constexpr int R = 4;                      // activation ring stages
   constexpr int MT = 16 * FM * RW;          // rows per workgroup
   constexpr int SLOTS = KS * MT * 8;        // 16-byte pieces per stage
@@ -326,8 +375,20 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     const int64_t n = n0 + q * 16 + (lane & 15);
     wsrc[q] = reinterpret_cast<const int8_t*>(w.data) + (n >> 4) * w.nblk * 1024 +
               (lane & 15) * 64 + 16 * c;
-    ssrc[q] = w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
+    // kBQ: the scales of channels 4c..4c+3 (16 consecutive values) instead
+    ssrc[q] = kBQ ? w.scale + ((n >> 4) * w.nblk * 64 + 16 * c) * ES
+                  : w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
     osrc[q] = kAsym ? w.offs + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * 4 : nullptr;
+  }
+  // kBQ: this lane's rows' per-block activation parameters
+  const float* sap[FM];
+  const int32_t* zap[FM];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    int64_t m = mw + rw * 16 * FM + f * 16 + (lane & 15);
+    m = m < M ? m : M - 1;
+    sap[f] = kBQ ? sa_g + m * ldsz : nullptr;
+    zap[f] = kBQ ? za_g + m * ldsz : nullptr;
   }
 
   // ---- activation direct loads: thread slot s = tid + 256*i of a stage ->
@@ -368,12 +429,28 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 
   uint4 wr[P][FN];
   float4 sr[P][FN], orr[P][FN];
+  float4 sr4[kBQ ? P : 1][FN][4];     // kBQ: [channel 4c+i] x 4 groups
+  float4 sar[kBQ ? P : 1][FM];        // kBQ: the row's 4 group scales
+  int4 zar[kBQ ? P : 1][FM];          //      and zero points
   auto load_w = [&](int u, int64_t b) {
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       wr[u][q] = *reinterpret_cast<const uint4*>(wsrc[q] + b * 1024);
-      sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
+      if constexpr (kBQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sr4[u][q][i] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b + 4 * ES * i);
+      } else {
+        sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
+      }
       if constexpr (kAsym) orr[u][q] = load_scale4<false>(osrc[q] + 64 * 4 * b);
+    }
+    if constexpr (kBQ) {
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        sar[u][f] = *reinterpret_cast<const float4*>(sap[f] + 4 * b);
+        zar[u][f] = *reinterpret_cast<const int4*>(zap[f] + 4 * b);
+      }
     }
   };
 
@@ -407,6 +484,64 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     uint4 cw4[FN];
     float4 cs[FN], co[FN];
     const bool live = ks * bpw + j < my_end;
+    if constexpr (kBQ) {
+      // per output (channel 4c+i, row): sa[row, g] * sw[channel, g], with
+      // the row scales zeroed past the end of the K range
+      float4 a4[FM], s4[FN][4];
+      int4 zq[FM];
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        a4[f] = live ? sar[u][f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        zq[f] = zar[u][f];
+      }
+#pragma unroll
+      for (int q = 0; q < FN; ++q) {
+        cw4[q] = wr[u][q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[q][i] = sr4[u][q][i];
+      }
+      load_w(u, range_block(ks, j + P));
+#pragma unroll
+      for (int t2 = 0; t2 < 4; t2 += 2) {
+        v4i d[2][FM][FN], e[2][FM][FN];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = t2 + h;
+#pragma unroll
+          for (int q = 0; q < FN; ++q) {
+            const uint32_t wd = h == 0 ? (t2 == 0 ? cw4[q].x : cw4[q].z)
+                                       : (t2 == 0 ? cw4[q].y : cw4[q].w);
+            const long bop = (long)(((uint64_t)nib_hi16(wd) << 32) | nib_lo16(wd));
+#pragma unroll
+            for (int f = 0; f < FM; ++f) {
+              const long aop = (long)(((uint64_t)ca[f][t].y << 32) | ca[f][t].x);
+              const int32_t z = t == 0 ? zq[f].x : (t == 1 ? zq[f].y : (t == 2 ? zq[f].z : zq[f].w));
+              const long zop = (long)((uint64_t)(uint8_t)(int8_t)z * 0x0101010101010101ull);
+              d[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, aop, v4i{0, 0, 0, 0}, 0, 0, 0);
+              e[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, zop, v4i{0, 0, 0, 0}, 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = t2 + h;
+#pragma unroll
+          for (int f = 0; f < FM; ++f) {
+            const float ar = t == 0 ? a4[f].x : (t == 1 ? a4[f].y : (t == 2 ? a4[f].z : a4[f].w));
+#pragma unroll
+            for (int q = 0; q < FN; ++q)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float4 k4 = s4[q][i];
+                const float sc = t == 0 ? k4.x : (t == 1 ? k4.y : (t == 2 ? k4.z : k4.w));
+                acc[h][f][q][i] = __builtin_fmaf(ar * sc, (float)(d[h][f][q][i] - e[h][f][q][i]),
+                                                 acc[h][f][q][i]);
+              }
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       cw4[q] = wr[u][q];
@@ -477,7 +612,10 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   // Loads issued after stage j+1's direct loads, in the steady state: the
   // weights refilled by step j+2-R, and R-2 whole steps (direct loads and a
   // weight refill each).  Earlier stages were drained in the prologue.
-  constexpr int A_WAIT = 2 * FN + (R - 2) * (ND + 2 * FN);
+  // loads per weight refill: weights and scales (kBQ: four scale vectors
+  // and the rows' two parameter vectors; asymmetric: the offsets too)
+  constexpr int LW = kBQ ? 5 * FN + 2 * FM : (kAsym ? 3 * FN : 2 * FN);
+  constexpr int A_WAIT = LW + (R - 2) * (ND + LW);
   static_assert(A_WAIT < 64, "vmcnt range");
   // The step loop is unrolled by P so the weight ring index is static.
   for (int64_t j0 = 0; j0 < bpw; j0 += P) {
@@ -522,6 +660,21 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
           for (int r = 0; r < KS - 1; ++r)
             out[f][q][i] = out[f][q][i] + red[slot * (KS - 1) + r][f][q][i][lane];
+  }
+  if constexpr (kBQ) {  // lane: row l%16 of fragment f, channels 4c+i
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int64_t m = mw + rw * 16 * FM + f * 16 + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < FN; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t n = n0 + q * 16 + 4 * c + i;
+          if (n < w.N) Y[m * ldy + n] = finish_bq(out[f][q][i], bias ? bias[n] : 0.0f, lo, hi);
+        }
+    }
+    return;
   }
 #pragma unroll
   for (int q = 0; q < FN; ++q) {
@@ -587,10 +740,24 @@ qp_status launch_gemv(const float* X, int64_t K, const int8_t* qa, int64_t lda,
   return launch_gemv_cfg<512>(X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, fused, stream);
 }
 
+// One row quantized per block: sa, za hold the row's group parameters.
+qp_status launch_gemv_bq(const int8_t* qa, const float* sa, const int32_t* za, const W4& w,
+                         const float* bias, float lo, float hi, float* Y, hipStream_t stream) {
+  constexpr int NT = 512;
+  const unsigned blocks = (unsigned)(w.Npad / 16);
+  if (w.kind == 1)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, 1, true>), dim3(blocks), dim3(NT), 0, stream,
+                       nullptr, w.Kpad, qa, w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
+  else
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, 0, true>), dim3(blocks), dim3(NT), 0, stream,
+                       nullptr, w.Kpad, qa, w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
+  return check_launch("a8w4 gemv (per-block activations)");
+}
+
 template <int FM, int FN, int RW, int CW, int KS>
 qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                           const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
-                          float hi, float* Y, int64_t ldy, hipStream_t stream) {
+                          float hi, float* Y, int64_t ldy, int64_t ldsz, hipStream_t stream) {
   static_assert(64 % (16 * FN * CW) == 0, "channel tiles must tile the 64-channel padding");
   const unsigned bx = (unsigned)ceil_div(w.N, 16 * FN * CW);
   const int64_t by = ceil_div(M, 16 * FM * RW);
@@ -598,8 +765,14 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   const dim3 grid(bx, (unsigned)by);
 #define QP_GEMM(PERM, KIND)                                                                \
   hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, PERM, KIND>), grid, dim3(256), 0, \
-                     stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy)
-  if (perm) {
+                     stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, (int64_t)0)
+#define QP_GEMM_BQ(KIND)                                                                      \
+  hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, KIND, true>), grid, dim3(256), \
+                     0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz)
+  if (ldsz > 0) {  // per-block activation parameters
+    if (w.kind == 1) QP_GEMM_BQ(1);
+    else QP_GEMM_BQ(0);
+  } else if (perm) {
     if (w.kind == 1) QP_GEMM(true, 1);
     else if (w.kind == 2) QP_GEMM(true, 2);
     else QP_GEMM(true, 0);
@@ -609,24 +782,28 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
     else QP_GEMM(false, 0);
   }
 #undef QP_GEMM
+#undef QP_GEMM_BQ
   return check_launch("a8w4 gemm");
 }
 
 // perm: the activations are permuted inside each 128-K block (as written by
-// the fused quantization); otherwise plain row-major.
+// the fused quantization); otherwise plain row-major.  ldsz > 0: sa, za are
+// per-block parameters [M][ldsz] (row-major activations).
 qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                       const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
-                      float hi, float* Y, int64_t ldy, hipStream_t stream) {
+                      float hi, float* Y, int64_t ldy, hipStream_t stream, int64_t ldsz = 0) {
   // <FM, FN, RW, CW, KS>: rows per workgroup 16*FM*RW, channels 16*FN*CW.
   // Small M splits K over the waves (enough waves stream the weights); larger
   // M shares each staged activation row among four channel groups.
   if (M <= 16)
     return launch_gemm_cfg<1, 1, 1, 1, 4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
-                                          stream);
+                                          ldsz, stream);
   if (M <= 32)
     return launch_gemm_cfg<2, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
-                                          stream);
-  return launch_gemm_cfg<4, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, stream);}
+                                          ldsz, stream);
+  return launch_gemm_cfg<4, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
+                                        stream);
+}
 
 }  // namespace
 }  // namespace qp
@@ -692,4 +869,82 @@ extern "C" qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_
     return launch_gemv(nullptr, w->K, qa, lda, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy,
                        false, stream);
   return launch_gemm(qa, lda, false, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
+}
+
+// ---- activations quantized per block of 32 K ----------------------------
+extern "C" qp_status qgemm_a8w4_blockq_f32_ws_size(int64_t M, const qp_packed_info* w,
+                                                   size_t* bytes) {
+  using namespace qp;
+  QP_REQUIRE(w && bytes && M >= 0, QP_EINVAL, "qgemm_a8w4_blockq_f32_ws_size: bad argument");
+  const int64_t nb = w->Kpad / 32;
+  *bytes = (size_t)(round_up(M * w->Kpad, 256) + 2 * round_up(4 * M * nb, 256));
+  return QP_OK;
+}
+
+static qp_status validate_bq(const qp_packed_info* w, int64_t K) {
+  using namespace qp;
+  qp_status st = validate_w4(w, K);
+  if (st) return st;
+  QP_REQUIRE(w->format != 4, QP_EUNSUPPORTED,
+             "a8w4 per-block activations: asymmetric weights are not supported");
+  return QP_OK;
+}
+
+extern "C" qp_status qgemm_a8w4_blockq_prequant_f32(const int8_t* qa, int64_t M, int64_t lda,
+                                                    const float* sa, const int32_t* za,
+                                                    int64_t ldsz, const qp_packed_info* w,
+                                                    const void* packedW_dev, const float* bias,
+                                                    float clamp_lo, float clamp_hi, float* Y,
+                                                    int64_t ldy, hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  qp_status st = validate_bq(w, w ? w->K : 0);
+  if (st) return st;
+  QP_REQUIRE(M >= 0 && lda >= w->Kpad && lda % 16 == 0 && ldy >= w->N, QP_EINVAL,
+             "a8w4: lda must be >= Kpad and a multiple of 16; ldy >= N");
+  QP_REQUIRE(ldsz >= w->Kpad / 32 && ldsz % 4 == 0, QP_EINVAL,
+             "a8w4 per-block: ldsz must be >= Kpad/32 and a multiple of 4");
+  QP_REQUIRE(!(clamp_lo > clamp_hi), QP_EINVAL, "a8w4: clamp_lo > clamp_hi");
+  if (M == 0) return QP_OK;
+  QP_REQUIRE(qa && sa && za && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
+  QP_REQUIRE(((uintptr_t)qa % 16) == 0 && ((uintptr_t)sa % 16) == 0 && ((uintptr_t)za % 16) == 0,
+             QP_EALIGN, "a8w4 per-block: qa, sa and za must be 16-byte aligned");
+  QP_REQUIRE(lda <= (INT64_C(1) << 24), QP_EUNSUPPORTED, "a8w4: lda above 2^24 bytes");
+  const W4 wv = w4_of(w, packedW_dev);
+  if (M == 1 && lda == w->Kpad && ldy >= w->N)
+    return launch_gemv_bq(qa, sa, za, wv, bias, clamp_lo, clamp_hi, Y, stream);
+  return launch_gemm(qa, lda, false, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream, ldsz);
+}
+
+extern "C" qp_status qgemm_a8w4_blockq_f32(const float* X, int64_t M, int64_t K, int64_t ldx,
+                                           const qp_packed_info* w, const void* packedW_dev,
+                                           const float* bias, float clamp_lo, float clamp_hi,
+                                           float* Y, int64_t ldy, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  qp_status st = validate_bq(w, K);
+  if (st) return st;
+  QP_REQUIRE(M >= 0 && ldx >= K && ldy >= w->N, QP_EINVAL, "a8w4: bad M/ldx/ldy");
+  QP_REQUIRE(!(clamp_lo > clamp_hi), QP_EINVAL, "a8w4: clamp_lo > clamp_hi");
+  if (M == 0) return QP_OK;
+  QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
+  size_t need = 0;
+  qgemm_a8w4_blockq_f32_ws_size(M, w, &need);
+  QP_REQUIRE(ws_bytes >= need, QP_ESIZE, "a8w4: workspace holds %zu bytes, needs %zu", ws_bytes,
+             need);
+  QP_REQUIRE(ws && ((uintptr_t)ws % 256) == 0, QP_EALIGN,
+             "a8w4: workspace must be non-null and 256-byte aligned");
+  const int64_t nb = w->Kpad / 32;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  int8_t* qa = reinterpret_cast<int8_t*>(p);
+  float* sa = reinterpret_cast<float*>(p + round_up(M * w->Kpad, 256));
+  int32_t* za = reinterpret_cast<int32_t*>(p + round_up(M * w->Kpad, 256) + round_up(4 * M * nb, 256));
+  st = launch_quantize_blocks32(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, nb, stream);
+  if (st) return st;
+  const W4 wv = w4_of(w, packedW_dev);
+  if (M == 1 && ldy >= w->N)
+    return launch_gemv_bq(qa, sa, za, wv, bias, clamp_lo, clamp_hi, Y, stream);
+  return launch_gemm(qa, w->Kpad, false, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream,
+                     nb);
 }

@@ -65,6 +65,11 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
 qp_status launch_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, int64_t kfill, float* row_scale, int32_t* row_zp,
                                bool perm, hipStream_t stream);
+// Per-block (32 K) dynamic quantization: q [M][ldq] up to kpad (zeros past
+// K), scale / zp [M][ldsz] for kpad/32 blocks (blocks past K: 1 and 0).
+qp_status launch_quantize_blocks32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                   int64_t ldq, int64_t kpad, float* scale, int32_t* zp,
+                                   int64_t ldsz, hipStream_t stream);
 qp_status conv_out_dims(int64_t H, int64_t W, int32_t KH, int32_t KW, int32_t sh, int32_t sw,
                         int32_t pt, int32_t pl, int32_t pb, int32_t pr, int32_t dh, int32_t dw,
                         int64_t* OH, int64_t* OW);

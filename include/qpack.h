@@ -249,6 +249,23 @@ qp_status qquantize_rows_s8_sym(const float* x, int64_t M, int64_t K, int64_t ld
                                 int64_t ldq, float* row_scale, hipStream_t stream);
 
 /*
+ * qquantize_rows_s8_blocked -- the dynamic quantization of qquantize_rows_s8
+ * applied to every block of `block` consecutive K of every row on its own
+ * ([MNN] DenseConvInt8TiledExecutor::onResize: with dynamicQuantOption 2 the
+ * input is cut into the weights' K blocks, mInputBlockNum = mBlockNum, and
+ * BatchAsyDynamicQuant gives each block a scale and zero point).
+ *   block    32 only (the int4 group size).
+ *   kpad     >= K, a multiple of 32: q is written for k < kpad (zeros past
+ *            K); parameters for kpad/32 blocks (blocks wholly past K get
+ *            scale 1, zero point 0).
+ *   q        device int8 [M][ldq], ldq >= kpad.
+ *   scale, zp  device f32 / int32 [M][ldsz], ldsz >= kpad/32.
+ */
+qp_status qquantize_rows_s8_blocked(const float* x, int64_t M, int64_t K, int64_t ldx,
+                                    int64_t block, int64_t kpad, int8_t* q, int64_t ldq,
+                                    float* scale, int32_t* zp, int64_t ldsz, hipStream_t stream);
+
+/*
  * qgemm_s8s8_requant -- C = requant(A x B + bias), INT8 affine operands
  * ([NPU] sections 1-5; [MNN] tileSplitFunction's post-treat parameters).
  *   acc[m,n] = sum_{k<K} (A[m,k]-zA)(B[k,n]-zB[n]) + bias[n]   (exact INT32,
@@ -336,6 +353,32 @@ qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_t lda, cons
                                   const int32_t* za, const qp_packed_info* w,
                                   const void* packedW_dev, const float* bias, float clamp_lo,
                                   float clamp_hi, float* Y, int64_t ldy, hipStream_t stream);
+
+/*
+ * qgemm_a8w4_blockq_f32 -- the A8W4 product with the activations quantized
+ * per block of 32 K (qquantize_rows_s8_blocked), each block being one int4
+ * group, so every group carries its own activation scale and zero point:
+ *   Y[m,n] = clamp(sum_g sa[m,g]*sw[n,g] * sum_{k in g} (qa[m,k]-za[m,g])*q[n,k]
+ *                  + bias[n], lo, hi)
+ *   the sum inside a group exact in int32, across groups f32.
+ * Weights: int4 blobs with f32 or bf16 scales (not the asymmetric format).
+ *   ws       device workspace of qgemm_a8w4_blockq_f32_ws_size bytes.
+ * qgemm_a8w4_blockq_prequant_f32 is the matmul step alone:
+ *   qa       device int8 [M][lda], lda >= Kpad, a multiple of 16, 16-byte
+ *            aligned, zero for K <= k < Kpad.
+ *   sa, za   device f32 / int32 [M][ldsz], ldsz >= Kpad/32 and a multiple
+ *            of 4, 16-byte aligned; entries past ceil(K/32) must be finite.
+ */
+qp_status qgemm_a8w4_blockq_f32_ws_size(int64_t M, const qp_packed_info* w, size_t* bytes);
+qp_status qgemm_a8w4_blockq_f32(const float* X, int64_t M, int64_t K, int64_t ldx,
+                                const qp_packed_info* w, const void* packedW_dev,
+                                const float* bias, float clamp_lo, float clamp_hi, float* Y,
+                                int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+qp_status qgemm_a8w4_blockq_prequant_f32(const int8_t* qa, int64_t M, int64_t lda,
+                                         const float* sa, const int32_t* za, int64_t ldsz,
+                                         const qp_packed_info* w, const void* packedW_dev,
+                                         const float* bias, float clamp_lo, float clamp_hi,
+                                         float* Y, int64_t ldy, hipStream_t stream);
 
 /*
  * qim2col_s8 -- explicit int8 im2col of an NHWC input ([MNN] tileSplitFunction:

@@ -186,3 +186,66 @@ def test_a8w4_asym_gemm_workload(qp, orc, M):
 def test_a8w4_asym_shapes(qp, orc, M, N, K, prequant):
     d = synth.a8w4(synth.BASE_SEED + 13 * M + N + K, M, N, K)
     _case_asym(qp, orc, d, _offsets(d, M + N + K), prequant=prequant)
+
+
+# ---- activations quantized per block of 32 (O5b), product O6d
+@pytest.mark.parametrize("M,K", [(1, 4096), (3, 100), (130, 320), (16, 4096), (5, 33)])
+def test_quantize_rows_blocked_bit_exact(qp, orc, M, K):
+    rng = np.random.default_rng(M * 7 + K)
+    X = (rng.standard_normal((M, K)) * rng.uniform(0.05, 20, (M, 1))).astype(np.float32)
+    if K >= 64:
+        X[0, 32:64] = 0.0                          # an all-zero block
+        X[-1, :32] = np.abs(X[-1, :32]) + 0.5      # an all-positive block
+    kpad = ((K + 127) // 128) * 128
+    q, sc, zp = qp.qquantize_rows_s8_blocked(_dev(X), kpad=kpad)
+    q, sc, zp = _host(q), _host(sc), _host(zp)
+    wq, ws, wz = orc.quantize_rows_s8_blocked(X, 32)
+    G = (K + 31) // 32
+    assert np.array_equal(q[:, :K], wq) and not q[:, K:].any()
+    assert np.array_equal(sc[:, :G], ws) and np.array_equal(zp[:, :G], wz)
+    assert np.all(sc[:, G:] == 1.0) and not zp[:, G:].any()
+
+
+def _case_bq(qp, orc, d, rows=None, prequant=False, scale_dtype="f32"):
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]), scale_dtype=scale_dtype)
+    sw = orc.round_bf16(d["sw"]) if scale_dtype == "bf16" else d["sw"]
+    if prequant:
+        q, sa, za = qp.qquantize_rows_s8_blocked(_dev(d["X"]), kpad=info.Kpad)
+        Y = _host(qp.qgemm_a8w4_blockq_prequant_f32(q, sa, za, blob, info, _dev(d["bias"]),
+                                                    d["clamp_lo"], d["clamp_hi"]))
+    else:
+        Y = _host(qp.qgemm_a8w4_blockq_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
+                                           d["clamp_lo"], d["clamp_hi"]))
+    X = d["X"] if rows is None else d["X"][rows]
+    want = orc.a8w4_forward_blockq(X, d["W"], sw, d["bias"], d["clamp_lo"], d["clamp_hi"])
+    _check_close(Y if rows is None else Y[rows], want, "per-block a8w4 output")
+
+
+def test_a8w4_blockq_gemv_workload(qp, orc):
+    _case_bq(qp, orc, synth.a8w4_gemv())
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_a8w4_blockq_gemm_workload(qp, orc, M):
+    rows = None if M == 16 else np.r_[0:8, 120:128]
+    _case_bq(qp, orc, synth.a8w4_gemm(M), rows)
+
+
+@pytest.mark.parametrize("M,N,K,prequant,sdt", [(1, 70, 96, False, "f32"),
+                                                (1, 33, 1000, True, "bf16"),
+                                                (2, 130, 200, False, "f32"),
+                                                (5, 77, 1000, True, "f32"),
+                                                (17, 100, 256, False, "bf16"),
+                                                (33, 48, 160, True, "f32"),
+                                                (130, 48, 320, False, "f32")])
+def test_a8w4_blockq_shapes(qp, orc, M, N, K, prequant, sdt):
+    _case_bq(qp, orc, synth.a8w4(synth.BASE_SEED + 17 * M + N + K, M, N, K), prequant=prequant,
+             scale_dtype=sdt)
+
+
+def test_a8w4_blockq_rejects_asymmetric_weights(qp):
+    d = synth.a8w4(synth.BASE_SEED + 90, 2, 32, 64)
+    bw = np.zeros_like(d["sw"])
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]), offsets=_dev(bw))
+    with pytest.raises(qp.QPackError):
+        qp.qgemm_a8w4_blockq_f32(_dev(d["X"]), blob, info)
