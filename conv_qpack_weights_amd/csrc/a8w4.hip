@@ -798,7 +798,8 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   if (M <= 16)
     return launch_gemm_cfg<1, 1, 1, 1, 4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
-  if (M <= 32)
+  // (the per-block variant holds more per row fragment: two fragments a wave)
+  if (M <= 32 || ldsz > 0)
     return launch_gemm_cfg<2, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
   return launch_gemm_cfg<4, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
