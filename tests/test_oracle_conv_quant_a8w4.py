@@ -606,3 +606,30 @@ def test_o6d_brute_force_rational(orc):
     za2[0, 2] += 5
     y2 = orc.a8w4_blockwise_blockq(qa, sa, za2, qw, sw, bias, -1e30, 1e30)
     assert np.array_equal(y2[1], y[1]) and not np.array_equal(y2[0], y[0])
+
+
+# ------------------------------------------------------------------ O6 on int8 blocks
+@pytest.mark.parametrize("group", [64, 128])
+def test_o6_int8_weight_blocks_against_exact_rationals(orc, group):
+    """O6's definition read for block-quantized int8 weights: full int8
+    values, one scale per block of 64 or 128 K."""
+    rng = np.random.default_rng(group)
+    M, N, K = 2, 3, 2 * group + 37
+    G = (K + group - 1) // group
+    qa = _rand_i8(rng, (M, K))
+    qw = _rand_i8(rng, (N, K))                       # full [-128, 127]
+    sa = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    za = rng.integers(-128, 128, M).astype(np.int32)
+    sw = rng.uniform(1e-4, 1e-3, (N, G)).astype(np.float32)
+    bias = rng.uniform(-1, 1, N).astype(np.float32)
+    Y = orc.a8w4_blockwise(qa, sa, za, qw, sw, bias, -1e30, 1e30, group)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for g in range(G):
+                d = sum((int(qa[m, k]) - int(za[m])) * int(qw[n, k])
+                        for k in range(g * group, min(K, g * group + group)))
+                tot += Fraction(float(sw[n, g])) * d
+            y = Fraction(float(sa[m])) * tot + Fraction(float(bias[n]))
+            assert abs(Fraction(float(Y[m, n])) - y) <= abs(y) * Fraction(1, 2 ** 23) \
+                + Fraction(1, 2 ** 40)
