@@ -377,6 +377,34 @@ def main():
                 "note": "per-block (32) activation quantization + product, two launches"}
             del bl
 
+        # block-quantized int8 weights (a scale per channel and 128 K), dynamic
+        # int8 activations: M = 1 (4096x4096) and M = 16, 128 (11008x4096)
+        rngw = np.random.default_rng(5)
+        for Mw, Nw in ((1, 4096), (16, 11008), (128, 11008)):
+            Ww = d(rngw.integers(-127, 128, (Nw, 4096)).astype(np.int8))
+            sww = d(rngw.uniform(1e-4, 1e-3, (Nw, 32)).astype(np.float32))
+            bw8, iw8 = qp.pack_s8_blockwise(Ww, sww, block=128)
+            Xw = d(synth.a8w4(synth.BASE_SEED + 3, Mw, Nw, 4096)["X"])
+            bbw = torch.zeros(Nw, dtype=torch.float32, device=dev)
+            Yw = torch.empty((Mw, Nw), dtype=torch.float32, device=dev)
+            wsw = torch.empty(qp.qgemm_a8w8_blockwise_f32_ws_size(Mw, iw8), dtype=torch.uint8,
+                              device=dev)
+            cpw = int(np.ceil(2 * INFINITY_CACHE / bw8.numel())) + 1
+            blw = [bw8] + [bw8.clone() for _ in range(cpw - 1)]
+            jw = [0]
+
+            def w8_cold():
+                k = jw[0] = (jw[0] + 1) % cpw
+                qp.qgemm_a8w8_blockwise_f32(Xw, blw[k], iw8, bbw, -6.0, 6.0, out=Yw, ws=wsw)
+            msw = graph_time(w8_cold, cpw, 10)
+            bytw = Nw * 4096 + Nw * 32 * 4 + Mw * 4096 * 4 + 2 * Nw * 4 + Mw * Nw * 4
+            workloads["a8w8_blockwise_%dx%dx4096" % (Mw, Nw)] = {
+                "cold_us": round(msw * 1e3, 2), "GBps": round(bytw / msw / 1e6, 1),
+                "frac_hbm_peak": round(bytw / msw / 1e6 / PEAK_HBM_GBS, 4),
+                "TOPS": round(2 * Mw * Nw * 4096 / msw / 1e9, 2),
+                "note": "dynamic row quantization + product; weights rotated (cold)"}
+            del blw, Ww
+
         # dynamic per-row activation quantization (asymmetric and symmetric),
         # the A8W4 GEMM's activation shape: M=128, K=4096
         xq = d(synth.a8w4_gemm(128)["X"])

@@ -80,6 +80,11 @@ SIGNATURES = {
                                         C.c_size_t, _P]),
     "qgemm_a8w4_blockq_prequant_f32": (C.c_int, [_P, _I64, _I64, _P, _P, _I64, _PI, _P, _P, _F,
                                                  _F, _P, _I64, _P]),
+    "qgemm_a8w8_blockwise_f32_ws_size": (C.c_int, [_I64, _PI, _SZ]),
+    "qgemm_a8w8_blockwise_f32": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P, _I64,
+                                           _P, C.c_size_t, _P]),
+    "qgemm_a8w8_blockwise_prequant_f32": (C.c_int, [_P, _I64, _I64, _P, _P, _PI, _P, _P, _F, _F,
+                                                    _P, _I64, _P]),
     "qgemm_a8w4_blockwise_f32_ws_size": (C.c_int, [_I64, _PI, _SZ]),
     "qgemm_a8w4_blockwise_f32": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P, _I64,
                                            _P, C.c_size_t, _P]),
@@ -195,6 +200,15 @@ def pack_s8(w: torch.Tensor, scales=None, scale=1.0, zero_points=None, zero_poin
     scheme = QP_PER_CHANNEL if scales is not None else QP_PER_TENSOR
     desc = qtensor(QP_S8, list(w.shape), [s for s in w.stride()], scheme=scheme, scale=scale,
                    scales=scales, zero_point=zero_point, zero_points=zero_points, axis=n_axis)
+    return qpack_weights(w, desc, k_axis, n_axis)
+
+
+def pack_s8_blockwise(w: torch.Tensor, scales: torch.Tensor, block=128):
+    """Pack int8 weights [N, K] (or OIHW, K = KH*KW*IC) with one f32 scale
+    per channel and block of `block` K: scales [N, ceil(K/block)]."""
+    k_axis, n_axis = 1, 0
+    desc = qtensor(QP_S8, list(w.shape), list(w.stride()), scheme=QP_BLOCKWISE, scales=scales,
+                   group_size=block, axis=n_axis)
     return qpack_weights(w, desc, k_axis, n_axis)
 
 
@@ -420,6 +434,42 @@ def qgemm_a8w4_blockq_prequant_f32(qa: torch.Tensor, sa: torch.Tensor, za: torch
                                                _ptr(bias), clamp_lo, clamp_hi, _ptr(out),
                                                out.stride(0), _stream(qa.device)),
            "qgemm_a8w4_blockq_prequant_f32")
+    return out
+
+
+def qgemm_a8w8_blockwise_f32_ws_size(M: int, info: PackedInfo) -> int:
+    n = C.c_size_t()
+    _check(_lib.qgemm_a8w8_blockwise_f32_ws_size(M, C.byref(info), C.byref(n)),
+           "qgemm_a8w8_blockwise_f32_ws_size")
+    return n.value
+
+
+def qgemm_a8w8_blockwise_f32(X: torch.Tensor, blob: torch.Tensor, info: PackedInfo, bias=None,
+                             clamp_lo=-float("inf"), clamp_hi=float("inf"), out=None, ws=None):
+    assert X.dtype == torch.float32 and X.dim() == 2 and X.stride(1) == 1
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = _alloc_bytes(qgemm_a8w8_blockwise_f32_ws_size(M, info), X.device)
+    _check(_lib.qgemm_a8w8_blockwise_f32(_ptr(X), M, K, X.stride(0), C.byref(info), _ptr(blob),
+                                         _ptr(bias), clamp_lo, clamp_hi, _ptr(out), out.stride(0),
+                                         _ptr(ws), ws.numel(), _stream(X.device)),
+           "qgemm_a8w8_blockwise_f32")
+    return out
+
+
+def qgemm_a8w8_blockwise_prequant_f32(qa: torch.Tensor, sa: torch.Tensor, za: torch.Tensor,
+                                      blob: torch.Tensor, info: PackedInfo, bias=None,
+                                      clamp_lo=-float("inf"), clamp_hi=float("inf"), out=None):
+    M = qa.shape[0]
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=qa.device)
+    _check(_lib.qgemm_a8w8_blockwise_prequant_f32(_ptr(qa), M, qa.stride(0), _ptr(sa), _ptr(za),
+                                                  C.byref(info), _ptr(blob), _ptr(bias),
+                                                  clamp_lo, clamp_hi, _ptr(out), out.stride(0),
+                                                  _stream(qa.device)),
+           "qgemm_a8w8_blockwise_prequant_f32")
     return out
 
 

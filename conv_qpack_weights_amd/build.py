@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqpack.so")
 SOURCES = ["status.cpp", "pack.hip", "quant.hip", "im2col.hip", "gemm_s8.hip", "conv.hip",
-           "conv_implicit.hip", "a8w4.hip", "unpack.hip"]
+           "conv_implicit.hip", "a8w4.hip", "a8w8b.hip", "unpack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -47,20 +47,33 @@ __global__ void write_header_kernel(BlobHeader h, uint8_t* blob) {
 // (n%32)*32 + k%32, so a GEMM wave fetches a 32-row x 32-K MFMA operand as
 // one contiguous kilobyte -- plus its scale, zero point and colsum (sum over
 // the real K only).
+// kBlock (format 5, block-quantized int8): instead, the row's block scales
+// scales[n*ldsw + b] (blocks of `group` K) and its weight kernel sum
+// wsum[n] = sum_b sw[n,b] * sum_{k in b} w[n,k] in fp64, from per-block
+// integer sums gathered in LDS.
+template <bool kBlock>
 __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__ w, int64_t N,
                                                       int64_t K, int64_t Kpad, int64_t sn, KMap km,
                                                       const float* __restrict__ scales,
                                                       float scale, const int32_t* __restrict__ zps,
                                                       int32_t zp, uint8_t* __restrict__ blob,
                                                       int64_t data_off, int64_t scale_off,
-                                                      int64_t sum_off, int64_t zp_off) {
+                                                      int64_t sum_off, int64_t zp_off,
+                                                      int64_t group, int64_t ldsw) {
+  extern __shared__ int32_t block_sum[];  // kBlock: Kpad/group entries
   const int64_t n = blockIdx.x;
   const int t = threadIdx.x;
   const bool live = n < N;
+  const int64_t nblk = kBlock ? Kpad / group : 0;
+  if constexpr (kBlock) {
+    for (int64_t b = t; b < nblk; b += 256) block_sum[b] = 0;
+    __syncthreads();
+  }
   int32_t part = 0;
   uint8_t* tiles = blob + data_off + (n / 32) * (Kpad / 32) * 1024 + (n % 32) * 32;
   for (int64_t k0 = (int64_t)t * 16; k0 < Kpad; k0 += 256 * 16) {
     uint32_t words[4];
+    int32_t chunk = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t v = 0;
@@ -69,13 +82,30 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
         int64_t k = k0 + 4 * q + j;
         int32_t b = 0;
         if (live && k < K) b = w[n * sn + km.off(k)];
-        part += b;
+        chunk += b;
         v |= (uint32_t)(uint8_t)(int8_t)b << (8 * j);
       }
       words[q] = v;
     }
+    part += chunk;
+    if constexpr (kBlock) atomicAdd(&block_sum[k0 / group], chunk);
     *reinterpret_cast<uint4*>(tiles + (k0 / 32) * 1024 + (k0 % 32)) =
         make_uint4(words[0], words[1], words[2], words[3]);
+  }
+  if constexpr (kBlock) {
+    __syncthreads();
+    const int64_t Greal = (K + group - 1) / group;
+    float* srow = reinterpret_cast<float*>(blob + scale_off) + n * nblk;
+    for (int64_t b = t; b < nblk; b += 256)
+      srow[b] = (live && b < Greal) ? scales[n * ldsw + b] : 0.0f;
+    if (t == 0) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < nblk; ++b)
+        acc = acc + (double)((live && b < Greal) ? scales[n * ldsw + b] : 0.0f) *
+                        (double)block_sum[b];
+      reinterpret_cast<float*>(blob + sum_off)[n] = live ? (float)acc : 0.0f;
+    }
+    return;
   }
   __shared__ int32_t red[256];
   red[t] = part;
@@ -228,9 +258,14 @@ qp_status weight_view(const qp_qtensor* w, int32_t k_axis, int32_t n_axis, Weigh
 
 qp_status format_of(const qp_qtensor* w, int32_t* format) {
   if (w->dtype == QP_S8) {
-    QP_REQUIRE(w->scheme == QP_PER_TENSOR || w->scheme == QP_PER_CHANNEL, QP_EUNSUPPORTED,
-               "int8 weights support per-tensor or per-channel scales (scheme %d)", w->scheme);
-    *format = 1;
+    QP_REQUIRE(w->scheme == QP_PER_TENSOR || w->scheme == QP_PER_CHANNEL ||
+                   w->scheme == QP_BLOCKWISE,
+               QP_EUNSUPPORTED, "int8 weights support per-tensor, per-channel or blockwise "
+               "scales (scheme %d)", w->scheme);
+    if (w->scheme == QP_BLOCKWISE)
+      QP_REQUIRE(w->zero_points == nullptr && w->zero_point == 0, QP_EUNSUPPORTED,
+                 "block-quantized int8 weights are symmetric: zero points must be absent");
+    *format = w->scheme == QP_BLOCKWISE ? 5 : 1;
   } else if (w->dtype == QP_S4) {
     QP_REQUIRE(w->scheme == QP_BLOCKWISE || w->scheme == QP_BLOCKWISE_BF16 ||
                    w->scheme == QP_BLOCKWISE_ASYM,
@@ -340,14 +375,26 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     h.has_zp = has_zp;
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
     if ((st = check_launch("qpack_weights header"))) return st;
-    hipLaunchKernelGGL(pack_s8_kernel, dim3((unsigned)g.Npad), dim3(256), 0, stream, src, v.N, v.K,
-                       g.Kpad, v.sn, v.km, per_channel ? w->scales : nullptr, w->scale,
+    hipLaunchKernelGGL(pack_s8_kernel<false>, dim3((unsigned)g.Npad), dim3(256), 0, stream, src,
+                       v.N, v.K, g.Kpad, v.sn, v.km, per_channel ? w->scales : nullptr, w->scale,
                        w->zero_points, w->zero_point, blob, g.data_off, g.scale_off, g.sum_off,
-                       g.zp_off);
+                       g.zp_off, (int64_t)0, (int64_t)0);
     if ((st = check_launch("qpack_weights int8"))) return st;
     g.has_zero_points = has_zp;
     g.scale_min = smin;
     g.scale_max = smax;
+  } else if (format == 5) {
+    QP_REQUIRE(w->scales != nullptr, QP_EINVAL, "blockwise weights need a scales array");
+    hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
+    if ((st = check_launch("qpack_weights header"))) return st;
+    const size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / g.group);
+    QP_REQUIRE(lds <= 65536, QP_EUNSUPPORTED, "block-quantized int8 packing: too many blocks");
+    hipLaunchKernelGGL(pack_s8_kernel<true>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
+                       v.N, v.K, g.Kpad, v.sn, v.km, w->scales, 0.0f, (const int32_t*)nullptr, 0,
+                       blob, g.data_off, g.scale_off, g.sum_off, g.zp_off, g.group,
+                       ceil_div(v.K, g.group));
+    if ((st = check_launch("qpack_weights int8 blockwise"))) return st;
+    g.has_zero_points = 0;
   } else {
     QP_REQUIRE(w->scales != nullptr, QP_EINVAL, "blockwise weights need a scales array");
     QP_REQUIRE(g.Kpad <= 65536, QP_EUNSUPPORTED, "int4 packing supports K <= 65536");

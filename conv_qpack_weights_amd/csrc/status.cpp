@@ -62,6 +62,17 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
       g.zp_off = g.total_bytes;
       g.total_bytes += scale_bytes;
     }
+  } else if (format == 5) {  // block-quantized int8: the int8 sub-tiles, a scale per block
+    QP_REQUIRE(group == 64 || group == 128, QP_EUNSUPPORTED,
+               "block-quantized int8 weights take blocks of 64 or 128 K (got %lld)",
+               (long long)group);
+    g.group = group;
+    g.Kpad = round_up(K, 128);
+    g.data_bytes = g.Npad * g.Kpad;
+    g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
+    g.sum_off = g.scale_off + round_up(4 * g.Npad * (g.Kpad / group), kRegionAlign);
+    g.zp_off = 0;
+    g.total_bytes = g.sum_off + round_up(4 * g.Npad, kRegionAlign);
   } else {
     QP_FAIL(QP_EINVAL, "unknown packed format %d", format);
   }

@@ -41,9 +41,15 @@ __global__ __launch_bounds__(256) void unpack_s8_kernel(const uint8_t* __restric
       blob + b.data_off))[((n / 32) * kblocks + k / 32) * 1024 + (n % 32) * 32 + k % 32];
   if (w) w[i * ldw + k] = q;
   if (deq) {
-    const float s = reinterpret_cast<const float*>(blob + b.scale_off)[n];
-    const int32_t z = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
-    deq[i * ldd + k] = s * (float)((int32_t)q - z);
+    if (b.format == 5) {  // a scale per block of `group` K, no zero point
+      const float s = reinterpret_cast<const float*>(blob + b.scale_off)[n * (b.Kpad / b.group) +
+                                                                           k / b.group];
+      deq[i * ldd + k] = s * (float)q;
+    } else {
+      const float s = reinterpret_cast<const float*>(blob + b.scale_off)[n];
+      const int32_t z = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
+      deq[i * ldd + k] = s * (float)((int32_t)q - z);
+    }
   }
 }
 
@@ -93,6 +99,10 @@ __global__ __launch_bounds__(256) void unpack_scales_kernel(const uint8_t* __res
   if (b.format == 1) {
     if (scales) scales[i] = reinterpret_cast<const float*>(blob + b.scale_off)[n];
     if (zp) zp[i] = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
+  } else if (b.format == 5) {
+    if (scales)
+      scales[i * lds + g] =
+          reinterpret_cast<const float*>(blob + b.scale_off)[n * (b.Kpad / b.group) + g];
   } else if (scales) {
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
     const int64_t e = ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4;
@@ -116,7 +126,7 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   using namespace qp;
   clear_error();
   QP_REQUIRE(info && packed_dev, QP_EINVAL, "qunpack_weights: null blob");
-  QP_REQUIRE(info->format >= 1 && info->format <= 4, QP_EINVAL,
+  QP_REQUIRE(info->format >= 1 && info->format <= 5, QP_EINVAL,
              "qunpack_weights: unknown blob format %d", info->format);
   QP_REQUIRE(n_begin >= 0 && n_count >= 0 && n_begin + n_count <= info->N, QP_EINVAL,
              "qunpack_weights: channels [%lld, %lld) outside [0, %lld)", (long long)n_begin,
@@ -124,7 +134,8 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   QP_REQUIRE(!w_out || ldw >= info->K, QP_EINVAL, "qunpack_weights: ldw smaller than K");
   QP_REQUIRE(!deq_out || ldd >= info->K, QP_EINVAL, "qunpack_weights: ldd smaller than K");
   QP_REQUIRE(info->format == 1 || !zp_out, QP_EINVAL,
-             "qunpack_weights: int4 blobs have no zero points (zp_out must be NULL)");
+             "qunpack_weights: only per-tensor/per-channel int8 blobs have zero points "
+             "(zp_out must be NULL)");
   const int64_t groups = info->format == 1 ? 1 : ceil_div(info->K, info->group);
   const int64_t per_row = info->format == 4 ? 2 * groups : groups;
   QP_REQUIRE(!scales_out || info->format == 1 || lds >= per_row, QP_EINVAL,
@@ -135,7 +146,7 @@ extern "C" qp_status qunpack_weights(const qp_packed_info* info, const void* pac
   if (w_out || deq_out) {
     const int64_t total = n_count * info->K;
     const unsigned blocks = (unsigned)ceil_div(total, 256);
-    if (info->format == 1)
+    if (info->format == 1 || info->format == 5)
       hipLaunchKernelGGL(unpack_s8_kernel, dim3(blocks), dim3(256), 0, stream, blob, b, n_begin,
                          n_count, w_out, ldw, deq_out, ldd);
     else

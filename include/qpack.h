@@ -182,6 +182,10 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  *   weights), accumulated in fp64
  *   (the weight kernel sum that folds the activation zero point,
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
+ * block-quantized int8 blob (format 5, QP_S8 with QP_BLOCKWISE, group 64 or
+ *   128): the int8 sub-tiles of format 1 with Kpad = roundup(K, 128), then
+ *   f32 scale[Npad][Kpad/group] (zero past K and N) and f32 wsum[Npad] =
+ *   sum_b scale[n,b] * sum_{k in b} w[n,k] (fp64); no zero points.
  * All padding bytes are zero.  int4 values outside [-8,7] set the header word
  * at byte 108 to non-zero (it is 0 for valid input).
  *   w_dev        device weights laid out as w->shape / w->stride.
@@ -379,6 +383,31 @@ qp_status qgemm_a8w4_blockq_prequant_f32(const int8_t* qa, int64_t M, int64_t ld
                                          const qp_packed_info* w, const void* packedW_dev,
                                          const float* bias, float clamp_lo, float clamp_hi,
                                          float* Y, int64_t ldy, hipStream_t stream);
+
+/*
+ * qgemm_a8w8_blockwise_f32 -- dynamically quantized int8 activations times
+ * block-quantized int8 weights (scheme QP_BLOCKWISE on QP_S8 weights, blob
+ * format 5: one f32 scale per output channel and block of 64 or 128 K;
+ * [MNN] _computeReorderQuantInfo's blockNum > 1), f32 out with bias and clamp:
+ *   Y[m,n] = clamp(sa[m] * sum_b sw[n,b] * sum_{k in b} (qa[m,k]-za[m])*q[n,k]
+ *                  + bias[n], lo, hi)
+ *   exact int32 inside a block, f32 across blocks; the rows quantized as by
+ *   qquantize_rows_s8.  For a GEMM (a linear layer, or a 1x1 convolution
+ *   whose OIHW weights were packed as K = C).
+ *   ws       device workspace of qgemm_a8w8_blockwise_f32_ws_size bytes.
+ * qgemm_a8w8_blockwise_prequant_f32 is the matmul step alone (qa [M][lda],
+ * lda >= Kpad and a multiple of 16, zero for K <= k < Kpad; sa, za [M]).
+ */
+qp_status qgemm_a8w8_blockwise_f32_ws_size(int64_t M, const qp_packed_info* w, size_t* bytes);
+qp_status qgemm_a8w8_blockwise_f32(const float* X, int64_t M, int64_t K, int64_t ldx,
+                                   const qp_packed_info* w, const void* packedW_dev,
+                                   const float* bias, float clamp_lo, float clamp_hi, float* Y,
+                                   int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
+qp_status qgemm_a8w8_blockwise_prequant_f32(const int8_t* qa, int64_t M, int64_t lda,
+                                            const float* sa, const int32_t* za,
+                                            const qp_packed_info* w, const void* packedW_dev,
+                                            const float* bias, float clamp_lo, float clamp_hi,
+                                            float* Y, int64_t ldy, hipStream_t stream);
 
 /*
  * qim2col_s8 -- explicit int8 im2col of an NHWC input ([MNN] tileSplitFunction:
