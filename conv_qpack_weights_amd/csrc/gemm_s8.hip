@@ -14,14 +14,15 @@
 // MNN "ConvInt8TiledExecutor.cpp" (tileSplitFunction): clamp [-128,127], and
 // with ReLU the lower clamp is the output zero point.
 //
-// Kernel design (gfx950, prior art only from the pages): a workgroup owns a
-// BM x BN output tile; A and B tiles of BK bytes of K are staged through LDS,
-// double buffered (one barrier per K step); each wave runs
-// v_mfma_i32_16x16x64_i8 on 16-byte per-lane fragments read with one
-// ds_read_b128 each.  Both operands are K-contiguous rows, so the same loader
-// serves A and the packed B.  The MFMA is issued as (B-fragment, A-fragment),
-// so every lane ends up holding 4 consecutive output channels of one row:
-// one 4-byte (int8) or 16-byte (int32) store per 4 outputs.
+// Kernel design (gfx950; the pages' designs are prior art only): a workgroup
+// owns a BM x BN output tile (256x256x128 for large shapes, 128x128 and
+// 64x64x64 below); the activation tile goes through a 4-deep LDS ring by
+// direct loads, the packed weights straight into registers one K tile ahead,
+// one barrier per K tile (see gemm_s8_core.hpp).  The MFMA is issued as
+// (B fragment, A fragment), so every lane ends up holding 4 consecutive
+// output channels of one row; full tiles are staged through LDS and written
+// as whole 16-byte row pieces.  Outputs: requantized int8, raw int32, or
+// f32 (dequantize, f32 bias, clamp).
 // The zero-point identity used is
 //   sum (a-zA)(b-zB) = sum ab - zB*rowsum(a) - zA*colsum(b) + K*zA*zB,
 // evaluated in wrapping 32-bit arithmetic, which is exact whenever the true

@@ -1,16 +1,22 @@
 // gemm_s8_core.hpp -- the INT8 MFMA GEMM kernel and its epilogue helpers.
 //
-// Included by gemm_s8.hip; see there for the numeric contract.  The kernel:
-//  * workgroup tile BM x BN, K in steps of BK bytes, STAGES-deep LDS ring;
-//  * tiles move HBM/L2 -> LDS with gfx950's direct loads
-//    (global_load_lds_dwordx4): each lane names the 16-byte chunk that lands
-//    at its slot, so the XOR swizzle is applied on the global side and no
-//    VGPRs stage the data;
-//  * each wave computes a TM x TN sub-tile with v_mfma_i32_16x16x64_i8 from
-//    16-byte fragments (one ds_read_b128 each), issued as
-//    (B-fragment, A-fragment) so a lane holds 4 consecutive channels of one
-//    output row;
-//  * one barrier per K step; the prefetch distance is STAGES-1 tiles.
+// Included by gemm_s8.hip (the numeric contract is stated there) and by the
+// implicit-GEMM convolution, which shares the epilogue helpers.  The kernel:
+//  * workgroup tile BM x BN, K in steps of BK bytes, an SA-deep LDS ring for
+//    the activations (A);
+//  * A moves HBM/L2 -> LDS with direct loads (buffer_load ... lds): each lane
+//    names the 16-byte chunk that lands at its slot, so the XOR swizzle is
+//    applied on the global side and no VGPRs stage the data;
+//  * the packed weights (B) go straight from the blob's 32x32 sub-tiles into
+//    VGPRs in MFMA operand order, one K tile ahead;
+//  * each wave computes all BM rows x BN/NW channels with
+//    v_mfma_i32_32x32x32_i8 (large tiles) or v_mfma_i32_16x16x64_i8 (small
+//    tiles), issued as (B fragment, A fragment) so a lane holds 4
+//    consecutive channels of one output row;
+//  * one barrier per K tile, halfway through it; the prefetch distance is
+//    SA-1 tiles; every tile runs the same branch-free body;
+//  * the epilogue applies the zero-point terms and bias and then the Q31
+//    requantization to int8, the raw int32, or the f32 dequantization.
 #pragma once
 
 #include <hip/hip_runtime.h>
