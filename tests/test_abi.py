@@ -197,3 +197,92 @@ def test_a8w4_quantize_im2col_conv_reject_bad_arguments(qp):
                                     3, 3, 1, 1, 1, 1, 1, 1, None, 0, C.byref(y), 1,
                                     C.c_void_p(FAKE), C.c_void_p(FAKE * 16), 1 << 20, None),
             qp.QP_EINVAL, "y must be")
+
+
+def test_blob_geometry_of_the_newer_formats(qp):
+    """bf16 scales halve the scale region, asymmetric int4 adds an offset
+    region of the scales' size, block-quantized int8 keeps the int8 tiles
+    and stores one scale per block."""
+    nb, al = C.c_size_t(), C.c_size_t()
+    L = qp.lib()
+    N, K = 100, 1000
+
+    def size(dtype, scheme, group=32):
+        d = qp.qtensor(dtype, [N, K], [K, 1], scheme=scheme, group_size=group)
+        assert L.qpack_weights_size(C.byref(d), 1, 0, C.byref(nb), C.byref(al)) == qp.QP_OK, \
+            qp.last_error()
+        return nb.value
+
+    Npad, Kpad4 = 128, 1024
+    def r256(x):
+        return (x + 255) // 256 * 256
+    data4 = r256(Npad * Kpad4 // 2)
+    sc32 = r256(16 * Npad * ((Kpad4 // 32 + 3) // 4))
+    assert size(qp.QP_S4, qp.QP_BLOCKWISE) == 256 + data4 + sc32 + r256(4 * Npad)
+    assert size(qp.QP_S4, qp.QP_BLOCKWISE_BF16) == 256 + data4 + r256(sc32 // 2) + r256(4 * Npad)
+    assert size(qp.QP_S4, qp.QP_BLOCKWISE_ASYM) == 256 + data4 + 2 * sc32 + r256(4 * Npad)
+    Kpad8 = 1024
+    for g in (64, 128):
+        assert size(qp.QP_S8, qp.QP_BLOCKWISE, g) == (256 + r256(Npad * Kpad8) +
+                                                      r256(4 * Npad * (Kpad8 // g)) + r256(4 * Npad))
+    d = qp.qtensor(qp.QP_S8, [N, K], [K, 1], scheme=qp.QP_BLOCKWISE, group_size=32)
+    _expect(qp, L.qpack_weights_size(C.byref(d), 1, 0, C.byref(nb), C.byref(al)),
+            qp.QP_EUNSUPPORTED, "64 or 128")
+
+
+def test_newer_entry_points_reject_bad_arguments(qp):
+    L = qp.lib()
+    i8 = _info8(qp)
+    a = qp.qtensor(qp.QP_S8, [130, 129], [129, 1], scale=0.02, zero_point=3)
+    # f32-output GEMM: reversed or NaN clamp bounds, short ldy
+    for lo, hi, ldy in [(1.0, 0.0, 70), (float("nan"), 1.0, 70), (0.0, 6.0, 69)]:
+        _expect(qp, L.qgemm_s8s8_dequant_f32(C.byref(a), C.c_void_p(FAKE), C.byref(i8),
+                                             C.c_void_p(FAKE), None, lo, hi, C.c_void_p(FAKE), ldy,
+                                             C.c_void_p(FAKE * 16), 1 << 20, None), qp.QP_EINVAL)
+    # per-block quantizer: block 64 unsupported, kpad below K
+    _expect(qp, L.qquantize_rows_s8_blocked(C.c_void_p(FAKE), 2, 100, 100, 64, 128,
+                                            C.c_void_p(FAKE), 128, C.c_void_p(FAKE),
+                                            C.c_void_p(FAKE), 4, None), qp.QP_EUNSUPPORTED)
+    _expect(qp, L.qquantize_rows_s8_blocked(C.c_void_p(FAKE), 2, 100, 100, 32, 96,
+                                            C.c_void_p(FAKE), 128, C.c_void_p(FAKE),
+                                            C.c_void_p(FAKE), 4, None), qp.QP_EINVAL, "kpad")
+    # per-block activations refuse asymmetric int4; the int8-blockwise GEMM refuses int4 blobs
+    i4 = qp.PackedInfo()
+    i4.format, i4.N, i4.K, i4.Npad, i4.Kpad, i4.group = 4, 64, 128, 64, 128, 32
+    _expect(qp, L.qgemm_a8w4_blockq_f32(C.c_void_p(FAKE), 2, 128, 128, C.byref(i4),
+                                        C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 64,
+                                        C.c_void_p(FAKE * 16), 1 << 20, None),
+            qp.QP_EUNSUPPORTED, "asymmetric")
+    i4.format = 2
+    _expect(qp, L.qgemm_a8w8_blockwise_f32(C.c_void_p(FAKE), 2, 128, 128, C.byref(i4),
+                                           C.c_void_p(FAKE), None, -6.0, 6.0, C.c_void_p(FAKE), 64,
+                                           C.c_void_p(FAKE * 16), 1 << 20, None),
+            qp.QP_EINVAL, "block-quantized")
+    # unpack: channel range outside the blob; zero points of an int4 blob
+    _expect(qp, L.qunpack_weights(C.byref(i8), C.c_void_p(FAKE), 60, 20, C.c_void_p(FAKE), 129,
+                                  None, 0, None, None, 0, None), qp.QP_EINVAL, "outside")
+    _expect(qp, L.qunpack_weights(C.byref(i4), C.c_void_p(FAKE), 0, 4, None, 0, None, 0,
+                                  C.c_void_p(FAKE), None, 0, None), qp.QP_EINVAL, "zero points")
+
+
+def test_conv_routes_and_workspace(qp):
+    """qconv2d_s8 picks the 1x1 fastway (GEMM workspace), the implicit GEMM
+    (no workspace) for C % 16 == 0, and the explicit im2col otherwise; bad
+    dilation is refused."""
+    L = qp.lib()
+    n = C.c_size_t()
+
+    def ws(C_, KH, pads, dil=(1, 1), stride=(1, 1)):
+        x = qp.qtensor(qp.QP_S8, [2, 8, 8, C_], [64 * C_, 8 * C_, C_, 1], scale=0.05)
+        info = _info8(qp, N=40, K=KH * KH * C_)
+        st = L.qconv2d_s8_ws_size(C.byref(x), C.byref(info), KH, KH, stride[0], stride[1], *pads,
+                                  dil[0], dil[1], C.byref(n))
+        return st, n.value
+
+    assert ws(64, 1, (0, 0, 0, 0)) == (qp.QP_OK, 128 * 64)          # fastway: GEMM copy of x
+    assert ws(32, 3, (1, 1, 1, 1)) == (qp.QP_OK, 0)                 # implicit
+    assert ws(16, 3, (2, 2, 2, 2), (2, 2)) == (qp.QP_OK, 0)
+    st, b = ws(3, 3, (1, 1, 1, 1))                                  # explicit im2col
+    assert st == qp.QP_OK and b >= 128 * 64
+    assert ws(16, 3, (1, 1, 1, 1), (0, 1))[0] == qp.QP_EINVAL
+    assert ws(16, 3, (0, 0, 0, 0), (4, 4))[0] == qp.QP_EINVAL       # span 9 > 8
