@@ -71,6 +71,9 @@ _SIGS = {
     "orc_quantize_rows_s8": (None, [_I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "orc_quantize_rows_s8_sym": (None, [_I64, _I64, _P, _I64, _P, _I64, _P]),
     "orc_round_bf16_array": (None, [_I64, _P, _P]),
+    "orc_conv2d_blockwise_f32": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I32, _F, _I64, _I64, _I64,
+                                           _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                           _I64, _P, _P, _F, _F, _P]),
     "orc_quantize_rows_s8_blocked": (None, [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64]),
     "orc_a8w4_blockwise_blockq": (C.c_int, [_I64, _I64, _I64, _I64, _P, _I64, _P, _P, _I64, _P,
                                             _I64, _P, _I64, _P, _F, _F, _P, _I64]),
@@ -368,6 +371,26 @@ def conv2d_direct(X, zp_in, Wt, stride=(1, 1), pad=(0, 0, 0, 0), bias=None, dila
                                  dilation[0], dilation[1], _ptr(biasv), _ptr(out))
     _check(rc, "orc_conv2d_direct")
     return out
+
+
+def conv2d_blockwise_f32(X, zx, sx, Wt, icb, sw, stride=(1, 1), pad=(0, 0, 0, 0), bias=None,
+                         dilation=(1, 1), lo=-np.inf, hi=np.inf):
+    """O4c: conv with per-(oc, input-channel block) weight scales, f32 out."""
+    X = _arr(X, np.int8)
+    Wt = _arr(Wt, np.int8)
+    NB, H, W, Cc = X.shape
+    OC, IC, KH, KW = Wt.shape
+    assert IC == Cc
+    OH, OW = conv_out_dims(H, W, KH, KW, stride, pad, dilation)
+    swv = _arr(sw, np.float32)
+    biasv = None if bias is None else _arr(bias, np.float32)
+    Y = np.zeros((NB, OH, OW, OC), dtype=np.float32)
+    rc = lib().orc_conv2d_blockwise_f32(NB, H, W, Cc, _ptr(X), int(zx), float(sx), OC, KH, KW,
+                                        _ptr(Wt), stride[0], stride[1], pad[0], pad[1], pad[2],
+                                        pad[3], dilation[0], dilation[1], icb, _ptr(swv),
+                                        _ptr(biasv), float(lo), float(hi), _ptr(Y))
+    _check(rc, "orc_conv2d_blockwise_f32")
+    return Y
 
 
 def im2col(X, pad_value, KH, KW, stride=(1, 1), pad=(0, 0, 0, 0), dilation=(1, 1)):

@@ -379,6 +379,55 @@ int orc_conv2d_direct(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t*
   return rc;
 }
 
+/* O4c -- convolution with channel-blocked int8 weights and f32 output.
+ * [MNN] _computeReorderQuantInfo / onResize: with blockNum > 1 each output
+ * channel has one scale per block of input channels (every kernel tap of
+ * those channels), the block partial sums are exact integers and are
+ * combined in float, and the output is float.  Reading: input per-tensor
+ * (sx, zx) with out-of-image taps at zx, weights OIHW with scale
+ * sw[oc][ic / icb]:
+ *   Y[b,oy,ox,oc] = clamp(sx * sum_{ky,kx,ic} sw[oc][ic/icb] * (xp - zx) * w
+ *                         + bias[oc], lo, hi)
+ * in fp64, one rounding to f32. */
+int orc_conv2d_blockwise_f32(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X,
+                             int32_t zx, float sx, int64_t OC, int64_t KH, int64_t KW,
+                             const int8_t* Wt, int64_t stride_h, int64_t stride_w, int64_t pad_t,
+                             int64_t pad_l, int64_t pad_b, int64_t pad_r, int64_t dil_h,
+                             int64_t dil_w, int64_t icb, const float* sw, const float* bias,
+                             float lo, float hi, float* Y) {
+  int64_t OH, OW;
+  if (icb <= 0 || C % icb != 0) return ORC_EINVAL;
+  int rc = orc_conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r, dil_h,
+                             dil_w, &OH, &OW);
+  if (rc) return rc;
+  int64_t nblk = C / icb;
+  for (int64_t b = 0; b < NB; ++b)
+    for (int64_t oy = 0; oy < OH; ++oy)
+      for (int64_t ox = 0; ox < OW; ++ox)
+        for (int64_t oc = 0; oc < OC; ++oc) {
+          double s = 0.0;
+          for (int64_t blk = 0; blk < nblk; ++blk) {
+            int64_t d = 0;
+            for (int64_t ky = 0; ky < KH; ++ky)
+              for (int64_t kx = 0; kx < KW; ++kx) {
+                int64_t iy = oy * stride_h + ky * dil_h - pad_t;
+                int64_t ix = ox * stride_w + kx * dil_w - pad_l;
+                int inside = iy >= 0 && iy < H && ix >= 0 && ix < W;
+                for (int64_t ic = blk * icb; ic < (blk + 1) * icb; ++ic) {
+                  int64_t xv = inside ? X[((b * H + iy) * W + ix) * C + ic] : zx;
+                  d += (xv - zx) * (int64_t)Wt[((oc * C + ic) * KH + ky) * KW + kx];
+                }
+              }
+            s += (double)sw[oc * nblk + blk] * (double)d;
+          }
+          double y = (double)sx * s + (bias ? (double)bias[oc] : 0.0);
+          if (y < (double)lo) y = (double)lo;
+          if (y > (double)hi) y = (double)hi;
+          Y[((b * OH + oy) * OW + ox) * OC + oc] = (float)y;
+        }
+  return 0;
+}
+
 /* Explicit im2col: row m = (b, oy, ox), column k = (ky, kx, ic) -- tap outer,
  * input channel inner, the K order of [MNN] reorderWeight. */
 int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int32_t pad_value,

@@ -103,6 +103,13 @@ int orc_im2col(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X, int
                int64_t pad_l, int64_t pad_b, int64_t pad_r, int64_t dil_h, int64_t dil_w,
                int8_t* col);
 
+int orc_conv2d_blockwise_f32(int64_t NB, int64_t H, int64_t W, int64_t C, const int8_t* X,
+                             int32_t zx, float sx, int64_t OC, int64_t KH, int64_t KW,
+                             const int8_t* Wt, int64_t stride_h, int64_t stride_w, int64_t pad_t,
+                             int64_t pad_l, int64_t pad_b, int64_t pad_r, int64_t dil_h,
+                             int64_t dil_w, int64_t icb, const float* sw, const float* bias,
+                             float lo, float hi, float* Y);
+
 /* ---- O5: dynamic per-row asymmetric int8 quantization (f32) ------------- */
 void orc_quantize_row_s8(const float* x, int64_t K, int8_t* q, float* scale, int32_t* zp);
 void orc_quantize_row_s8_sym(const float* x, int64_t K, int8_t* q, float* scale);

@@ -633,3 +633,63 @@ def test_o6_int8_weight_blocks_against_exact_rationals(orc, group):
             y = Fraction(float(sa[m])) * tot + Fraction(float(bias[n]))
             assert abs(Fraction(float(Y[m, n])) - y) <= abs(y) * Fraction(1, 2 ** 23) \
                 + Fraction(1, 2 ** 40)
+
+
+# ------------------------------------------------------------------ O4c
+def test_o4c_single_block_is_o4_scaled(orc):
+    """One block spanning every input channel: sx * sw[oc] * O4's integer
+    accumulator + bias (power-of-two scales keep it exact)."""
+    rng = np.random.default_rng(41)
+    X = _rand_i8(rng, (2, 7, 6, 8))
+    Wt = _rand_i8(rng, (5, 8, 3, 3), -127, 127)
+    sw = (2.0 ** -rng.integers(6, 10, (5, 1))).astype(np.float32)
+    bias = np.array([0.5, -1.0, 0.0, 2.0, -0.25], np.float32)
+    y = orc.conv2d_blockwise_f32(X, 7, 0.125, Wt, 8, sw, (1, 1), (1, 1, 1, 1), bias)
+    acc = orc.conv2d_direct(X, 7, Wt, (1, 1), (1, 1, 1, 1))
+    want = 0.125 * sw[:, 0].astype(np.float64) * acc + bias
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_o4c_blocks_are_input_channel_ranges(orc):
+    """Scaling one block's scale by 2 equals adding that block's own
+    contribution once more; the blocks split the input channels, each over
+    every kernel tap (a weight zeroed outside block 1 isolates it)."""
+    rng = np.random.default_rng(42)
+    X = _rand_i8(rng, (1, 6, 6, 12))
+    Wt = _rand_i8(rng, (3, 12, 3, 3), -127, 127)
+    sw = (2.0 ** -rng.integers(6, 9, (3, 3))).astype(np.float32)    # icb = 4: 3 blocks
+    base = orc.conv2d_blockwise_f32(X, -5, 0.5, Wt, 4, sw, (1, 1), (1, 1, 1, 1)).astype(np.float64)
+    only1 = Wt.copy()
+    only1[:, :4] = 0
+    only1[:, 8:] = 0
+    part1 = orc.conv2d_blockwise_f32(X, -5, 0.5, only1, 4, sw, (1, 1), (1, 1, 1, 1))
+    sw2 = sw.copy()
+    sw2[:, 1] *= 2
+    twice = orc.conv2d_blockwise_f32(X, -5, 0.5, Wt, 4, sw2, (1, 1), (1, 1, 1, 1))
+    assert np.array_equal(twice, (base + part1).astype(np.float32))
+    with pytest.raises(Exception):
+        orc.conv2d_blockwise_f32(X, -5, 0.5, Wt, 5, np.ones((3, 2), np.float32))   # 12 % 5
+
+
+def test_o4c_brute_force_rational(orc):
+    rng = np.random.default_rng(43)
+    X = _rand_i8(rng, (1, 4, 5, 4))
+    Wt = _rand_i8(rng, (2, 4, 2, 3), -127, 127)
+    sw = rng.uniform(1e-3, 1e-2, (2, 2)).astype(np.float32)
+    bias = rng.uniform(-1, 1, 2).astype(np.float32)
+    zx, sx = 9, np.float32(0.03)
+    y = orc.conv2d_blockwise_f32(X, zx, sx, Wt, 2, sw, (1, 2), (1, 0, 0, 2), bias, (2, 1))
+    OH, OW = orc.conv_out_dims(4, 5, 2, 3, (1, 2), (1, 0, 0, 2), (2, 1))
+    for oy in range(OH):
+        for ox in range(OW):
+            for oc in range(2):
+                s = Fraction(0)
+                for ky in range(2):
+                    for kx in range(3):
+                        iy, ix = oy * 1 + ky * 2 - 1, ox * 2 + kx * 1 - 0
+                        for ic in range(4):
+                            xv = int(X[0, iy, ix, ic]) if 0 <= iy < 4 and 0 <= ix < 5 else zx
+                            s += Fraction(float(sw[oc, ic // 2])) * (xv - zx) * int(Wt[oc, ic, ky, kx])
+                exact = Fraction(float(sx)) * s + Fraction(float(bias[oc]))
+                assert abs(Fraction(float(y[0, oy, ox, oc])) - exact) <= \
+                    abs(exact) * Fraction(1, 2 ** 23) + Fraction(1, 2 ** 40)
