@@ -486,6 +486,29 @@ def main():
             "frac_mfma_peak_implicit": round(copsb / msi / 1e9 / PEAK_INT8_TOPS, 4)}
         del Xb, Yb, wsb
 
+        # channel-blocked int8 weights (a scale per channel and 64 input
+        # channels), f32 output: the same 3x3 layer at batch 1 and 32
+        rngb = np.random.default_rng(8)
+        swb = d(rngb.uniform(1e-4, 1e-3, (64, 1)).astype(np.float32))
+        bcb, icb_ = qp.pack_s8_blockwise(d(c["W"]), swb, block=64)
+        bfb = torch.zeros(64, dtype=torch.float32, device=dev)
+        Yf1 = torch.empty((1, 56, 56, 64), dtype=torch.float32, device=dev)
+        Xb32 = d(synth.conv3x3_nhwc(NB=32)["X"])
+        Yf32 = torch.empty((32, 56, 56, 64), dtype=torch.float32, device=dev)
+        msb1 = graph_time(lambda: qp.qconv2d_s8_blockwise_f32(
+            Xc, c["s_in"], c["zp_in"], bcb, icb_, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), bfb, 0.0,
+            6.0, out=Yf1), 50)
+        f32c = lambda: qp.qconv2d_s8_blockwise_f32(Xb32, c["s_in"], c["zp_in"], bcb, icb_, 3, 3,
+                                                   (1, 1), (1, 1, 1, 1), (1, 1), bfb, 0.0, 6.0,
+                                                   out=Yf32)
+        f32c()
+        msb32 = ev_time(f32c, 20)
+        workloads["conv3x3_56x56x64_to_64_blockwise_f32"] = {
+            "batch1_us": round(msb1 * 1e3, 2), "batch32_us": round(msb32 * 1e3, 2),
+            "TOPS_batch32": round(32 * copsn / msb32 / 1e9, 1),
+            "note": "implicit GEMM, channel-blocked weights, f32 output"}
+        del Xb32, Yf32
+
         # 130x70x129 per-tensor GEMM (the worked example's shape)
         s = synth.gemm_affine_per_tensor()
         bs, is_ = qp.pack_s8(d(s["B"]), scale=s["sB"], zero_point=s["zB"], k_axis=0, n_axis=1)

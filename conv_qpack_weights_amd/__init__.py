@@ -96,6 +96,8 @@ SIGNATURES = {
                                             _I32, _SZ]),
     "qconv2d_s8_im2col": (C.c_int, [_QT, _P, _PI, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                     _I32, _P, _I64, _QT, _I32, _P, _P, C.c_size_t, _P]),
+    "qconv2d_s8_blockwise_f32": (C.c_int, [_QT, _P, _PI, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           _I32, _I32, _I32, _I32, _P, _F, _F, _P, _P]),
     "qconv2d_s8_ws_size": (C.c_int, [_QT, _PI, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                      _I32, _I32, _SZ]),
     "qconv2d_s8": (C.c_int, [_QT, _P, _PI, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -204,8 +206,9 @@ def pack_s8(w: torch.Tensor, scales=None, scale=1.0, zero_points=None, zero_poin
 
 
 def pack_s8_blockwise(w: torch.Tensor, scales: torch.Tensor, block=128):
-    """Pack int8 weights [N, K] (or OIHW, K = KH*KW*IC) with one f32 scale
-    per channel and block of `block` K: scales [N, ceil(K/block)]."""
+    """Pack int8 weights with one f32 scale per channel and block: rank 2
+    [N, K] with scales [N, ceil(K/block)] (blocks of K), or OIHW with scales
+    [OC, IC/block] (blocks of input channels, every kernel tap)."""
     k_axis, n_axis = 1, 0
     desc = qtensor(QP_S8, list(w.shape), list(w.stride()), scheme=QP_BLOCKWISE, scales=scales,
                    group_size=block, axis=n_axis)
@@ -541,4 +544,23 @@ def qconv2d_s8(X: torch.Tensor, s_in: float, zp_in: int, blob: torch.Tensor, inf
                            _ptr(bias), int(max_abs_bias), C.byref(y_desc), int(bool(relu)),
                            _ptr(out), _ptr(ws), ws.numel(), _stream(X.device)),
            "qconv2d_s8")
+    return out
+
+
+def qconv2d_s8_blockwise_f32(X: torch.Tensor, s_in: float, zp_in: int, blob: torch.Tensor,
+                             info: PackedInfo, KH: int, KW: int, stride=(1, 1), pad=(0, 0, 0, 0),
+                             dilation=(1, 1), bias=None, clamp_lo=-float("inf"),
+                             clamp_hi=float("inf"), out=None):
+    """Channel-blocked int8 convolution with f32 output (NHWC in and out)."""
+    NB, H, W, Cc = X.shape
+    OH = (H + pad[0] + pad[2] - (dilation[0] * (KH - 1) + 1)) // stride[0] + 1
+    OW = (W + pad[1] + pad[3] - (dilation[1] * (KW - 1) + 1)) // stride[1] + 1
+    x_desc = qtensor(QP_S8, [NB, H, W, Cc], scale=s_in, zero_point=zp_in)
+    if out is None:
+        out = torch.empty((NB, OH, OW, info.N), dtype=torch.float32, device=X.device)
+    _check(_lib.qconv2d_s8_blockwise_f32(C.byref(x_desc), _ptr(X), C.byref(info), _ptr(blob), KH,
+                                         KW, stride[0], stride[1], pad[0], pad[1], pad[2], pad[3],
+                                         dilation[0], dilation[1], _ptr(bias), clamp_lo, clamp_hi,
+                                         _ptr(out), _stream(X.device)),
+           "qconv2d_s8_blockwise_f32")
     return out

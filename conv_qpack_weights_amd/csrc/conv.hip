@@ -4,6 +4,8 @@
 // convolution = im2col of the int8 input, padded with the input zero point,
 // then the int8 GEMM with the requantizing post-treatment).  The weights are
 // an int8 blob packed from OIHW with K ordered (kh, kw, ic).
+#include <cmath>
+
 #include "qp_internal.hpp"
 
 namespace qp {
@@ -222,4 +224,57 @@ extern "C" qp_status qconv2d_s8(const qp_qtensor* x, const int8_t* X, const qp_p
                          ws_bytes - (size_t)p.ws_col, true, stream);
     }
   }
+}
+
+// ---- qconv2d_s8_blockwise_f32: channel-blocked int8 weights, f32 output ----
+//
+// MNN's dynamic-quant convolution with blockNum > 1: the weights carry one
+// scale per output channel and block of input channels, the exact block sums
+// are combined in float and the output is float.  The input here is int8
+// with a per-tensor scale and zero point; the route is the implicit GEMM.
+extern "C" qp_status qconv2d_s8_blockwise_f32(const qp_qtensor* x, const int8_t* X,
+                                              const qp_packed_info* w, const void* packedW_dev,
+                                              int32_t KH, int32_t KW, int32_t stride_h,
+                                              int32_t stride_w, int32_t pad_t, int32_t pad_l,
+                                              int32_t pad_b, int32_t pad_r, int32_t dil_h,
+                                              int32_t dil_w, const float* bias_dev,
+                                              float clamp_lo, float clamp_hi, float* Y,
+                                              hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  QP_REQUIRE(x && w, QP_EINVAL, "qconv2d_blockwise: null descriptor");
+  QP_REQUIRE(w->format == 5, QP_EINVAL,
+             "qconv2d_blockwise: weights must be a block-quantized int8 blob");
+  QP_REQUIRE(x->dtype == QP_S8 && x->rank == 4, QP_EINVAL,
+             "qconv2d_blockwise: x must be rank-4 NHWC QP_S8");
+  const int64_t NB = x->shape[0], H = x->shape[1], W = x->shape[2], C = x->shape[3];
+  QP_REQUIRE(NB > 0 && H > 0 && W > 0 && C > 0, QP_EINVAL, "qconv2d_blockwise: empty input");
+  QP_REQUIRE(x->stride[3] == 1 && x->stride[2] == C && x->stride[1] == W * C &&
+                 x->stride[0] == H * W * C,
+             QP_EUNSUPPORTED, "qconv2d_blockwise: x must be contiguous NHWC");
+  QP_REQUIRE(w->K == (int64_t)KH * KW * C, QP_EINVAL,
+             "qconv2d_blockwise: weights have K=%lld, kernel needs KH*KW*C=%lld", (long long)w->K,
+             (long long)KH * KW * C);
+  QP_REQUIRE(C % 16 == 0 && C % w->group == 0, QP_EUNSUPPORTED,
+             "qconv2d_blockwise: C must be a multiple of 16 and of the channel block (%lld)",
+             (long long)w->group);
+  QP_REQUIRE(x->scheme == QP_PER_TENSOR && x->rounding == QP_ROUND_HALF_EVEN, QP_EUNSUPPORTED,
+             "qconv2d_blockwise: x must be per-tensor, round-half-to-even");
+  QP_REQUIRE(x->zero_point >= -128 && x->zero_point <= 127, QP_EINVAL,
+             "qconv2d_blockwise: input zero point outside int8");
+  QP_REQUIRE(std::isfinite(x->scale) && x->scale > 0, QP_EINVAL,
+             "qconv2d_blockwise: input scale must be > 0");
+  QP_REQUIRE(!(clamp_lo > clamp_hi) && !std::isnan(clamp_lo) && !std::isnan(clamp_hi), QP_EINVAL,
+             "qconv2d_blockwise: clamp bounds must satisfy lo <= hi");
+  QP_REQUIRE(NB * H * W * C < (INT64_C(1) << 31), QP_EUNSUPPORTED,
+             "qconv2d_blockwise: input of 2^31 bytes or more");
+  int64_t OH = 0, OW = 0;
+  qp_status st = conv_out_dims(H, W, KH, KW, stride_h, stride_w, pad_t, pad_l, pad_b, pad_r,
+                               dil_h, dil_w, &OH, &OW);
+  if (st) return st;
+  QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "qconv2d_blockwise: null data pointer");
+  QP_REQUIRE(((uintptr_t)X % 16) == 0, QP_EALIGN, "qconv2d_blockwise: x must be 16-byte aligned");
+  const ConvShape cs{NB, H, W, C, OH, OW, KH, KW, stride_h, stride_w, pad_t, pad_l, dil_h, dil_w};
+  return launch_conv_implicit_blk(X, cs, x->scale, x->zero_point, w, packedW_dev, bias_dev,
+                                  clamp_lo, clamp_hi, Y, stream);
 }

@@ -55,6 +55,13 @@ struct ConvKArgs {
   void* Y;
   int64_t ldy;
   int32_t tiles_n;
+  // channel-blocked weights (f32 output): scale of channel n and K block kb
+  // at sw_blk[n*nblk + kb], blocks of 64 << blk_shift K
+  const float* sw_blk;
+  int64_t nblk;
+  int32_t blk_shift;
+  const float* bias_f;
+  float clo, chi;
 };
 
 // q = k / d for 0 <= k < 2^22, 0 < d: the f32 quotient is within one of
@@ -66,11 +73,16 @@ __device__ __forceinline__ int div_small(int k, int d, float rcp) {
   return q;
 }
 
-template <int FM, int FN, int P, bool kOut32, bool kRowSum>
+// kBlk: channel-blocked weights with f32 output.  Each K-step's products are
+// kept apart: d = MFMA(weights, pieces) and e = MFMA(weights, the input zero
+// point over the real K), so d - e is the step's exact sum of (x - zx)*w,
+// which is scaled by its block's weight scale into an f32 sum; the output
+// is sx * that + bias, clamped.
+template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
 __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   constexpr int BM = 4 * FM * 16;  // four waves stacked along the pixels
   constexpr int BN = FN * 16;
-  constexpr int LOADS = FM + FN;  // loads per K-step and lane
+  constexpr int LOADS = FM + FN + (kBlk ? 4 * FN : 0);  // loads per K-step and lane
   static_assert((P - 1) * LOADS < 64, "vmcnt range");
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
 
@@ -86,7 +98,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   const int64_t n0 = (int64_t)tile_n * BN;
 
   // ---- per-column epilogue constants (read after the main loop) ----
-  if (tid < BN) {
+  if (!kBlk && tid < BN) {
     const int64_t n = n0 + tid;
     int32_t mm = 0, ss = 1, cc = 0, zb = 0;
     if (n < g.N) {
@@ -131,6 +143,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   v4i ar[P][FM], br[P][FN];
   uint32_t vbits[P];  // bit j: fragment j's piece is an in-image load
   int32_t fill[P];    // the pattern of the other pieces: zero point, or 0 past K
+  float swr[kBlk ? P : 1][FN][4];  // kBlk: the step's block scale, channels 4*grp+r
   auto issue = [&](int slot, int kt) {
     const int k = kt * 64 + grp * 16;
     const int tap = div_small(k, g.C, g.rcpC);
@@ -154,7 +167,22 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     const int64_t kc = kt < g.nk ? kt : g.nk - 1;
 #pragma unroll
     for (int i = 0; i < FN; ++i) br[slot][i] = *reinterpret_cast<const v4i*>(b_src[i] + kc * 2048);
+    if constexpr (kBlk) {
+      const int64_t kb = kc >> g.blk_shift;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          swr[slot][i][r] = g.sw_blk[(n0 + i * 16 + 4 * grp + r) * g.nblk + kb];
+    }
   };
+  float accf[kBlk ? FN : 1][kBlk ? FM : 1][4];
+#pragma unroll
+  for (int i = 0; i < (kBlk ? FN : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < (kBlk ? FM : 1); ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
 
   v4i acc[FN][FM];
   int32_t rsum[FM];
@@ -187,6 +215,30 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
           rsum[j] = s;
         }
       }
+      if constexpr (kBlk) {
+        // the input zero point over this lane's real K (0 past K)
+        const v4i zop = v4i{fill[u], fill[u], fill[u], fill[u]};
+        float sc[FN][4];
+        v4i d[FN][FM], e[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[i][r] = swr[u][i][r];
+          e[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], zop, v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+            d[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], a[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+        }
+        issue(u, kt0 + u + P);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              accf[i][j][r] = __builtin_fmaf(sc[i][r], (float)(d[i][j][r] - e[i][r]), accf[i][j][r]);
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
@@ -196,6 +248,27 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     }
   }
   wait_vmcnt<0>();
+  if constexpr (kBlk) {  // y = sx * sum + bias, clamped; lane: channels 4*grp+r of row r16
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int64_t n = n0 + i * 16 + 4 * grp;
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int64_t m = m0 + j * 16 + r16;
+        if (m >= g.M) continue;
+        float* row = static_cast<float*>(g.Y) + m * g.ldy;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= g.N) continue;
+          float y = g.sA * accf[i][j][r] + (g.bias_f ? g.bias_f[n + r] : 0.0f);
+          y = y < g.clo ? g.clo : y;
+          y = y > g.chi ? g.chi : y;
+          row[n + r] = y;
+        }
+      }
+    }
+    return;
+  }
   __syncthreads();  // the column constants
 
   // Row sums: the four lanes of a pixel hold the four K pieces.
@@ -260,44 +333,52 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   }
 }
 
-template <int FM, int FN, int P, bool kOut32, bool kRowSum>
+template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_cfg(ConvKArgs a, hipStream_t stream) {
   constexpr int BM = 4 * FM * 16, BN = FN * 16;
   a.tiles_n = (int32_t)ceil_div(a.N, BN);
   const int64_t blocks = ceil_div(a.M, BM) * a.tiles_n;
   QP_REQUIRE(blocks < (INT64_C(1) << 31), QP_EUNSUPPORTED, "qconv2d: too many tiles");
-  hipLaunchKernelGGL((conv_implicit_kernel<FM, FN, P, kOut32, kRowSum>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((conv_implicit_kernel<FM, FN, P, kOut32, kRowSum, kBlk>), dim3((unsigned)blocks),
                      dim3(256), 0, stream, a);
   return check_launch("qconv2d implicit kernel");
 }
 
 // The K loop runs in whole groups of P steps; P is picked so that few
 // steps fall past the end of K.
-template <int FM, int FN, bool kOut32, bool kRowSum>
+template <int FM, int FN, bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_depth(const ConvKArgs& a, hipStream_t stream) {
-  if (a.nk <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum>(a, stream);
-  if (a.nk % 4 != 0 && a.nk % 3 == 0) return launch_cfg<FM, FN, 3, kOut32, kRowSum>(a, stream);
-  return launch_cfg<FM, FN, 4, kOut32, kRowSum>(a, stream);
+  if (a.nk <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum, kBlk>(a, stream);
+  if (a.nk % 4 != 0 && a.nk % 3 == 0)
+    return launch_cfg<FM, FN, 3, kOut32, kRowSum, kBlk>(a, stream);
+  return launch_cfg<FM, FN, 4, kOut32, kRowSum, kBlk>(a, stream);
 }
 
-template <bool kOut32, bool kRowSum>
+template <bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_sel(const ConvKArgs& a, hipStream_t stream) {
-  // Two 128-pixel workgroups per compute unit or more: 32 pixels per wave
-  // (fewer weight loads per MFMA).  Otherwise 16 pixels per wave, for more
-  // workgroups; narrow layers or too few tiles take 32-channel tiles.
-  if (ceil_div(a.M, 128) * ceil_div(a.N, 64) >= 512)
-    return launch_depth<2, 4, kOut32, kRowSum>(a, stream);
-  if (ceil_div(a.M, 64) * ceil_div(a.N, 64) >= 256 && a.N > 32)
-    return launch_depth<1, 4, kOut32, kRowSum>(a, stream);
-  return launch_depth<1, 2, kOut32, kRowSum>(a, stream);
+  if constexpr (kBlk) {
+    // four scale loads per channel quad and step: 32-channel tiles keep the
+    // loads in flight within the wait counter's range
+    if (ceil_div(a.M, 128) * ceil_div(a.N, 32) >= 512)
+      return launch_depth<2, 2, kOut32, kRowSum, kBlk>(a, stream);
+    return launch_depth<1, 2, kOut32, kRowSum, kBlk>(a, stream);
+  } else {
+    // Two 128-pixel workgroups per compute unit or more: 32 pixels per wave
+    // (fewer weight loads per MFMA).  Otherwise 16 pixels per wave, for more
+    // workgroups; narrow layers or too few tiles take 32-channel tiles.
+    if (ceil_div(a.M, 128) * ceil_div(a.N, 64) >= 512)
+      return launch_depth<2, 4, kOut32, kRowSum>(a, stream);
+    if (ceil_div(a.M, 64) * ceil_div(a.N, 64) >= 256 && a.N > 32)
+      return launch_depth<1, 4, kOut32, kRowSum>(a, stream);
+    return launch_depth<1, 2, kOut32, kRowSum>(a, stream);
+  }
 }
 
 }  // namespace
 
-qp_status launch_conv_implicit(const int8_t* X, const ConvShape& cs, float sA, int32_t zA,
-                               const qp_packed_info* w, const void* packedW,
-                               const int32_t* bias, float sOut, int32_t zp_out, bool out32,
-                               int32_t relu, void* Y, hipStream_t stream) {
+namespace {
+ConvKArgs conv_args(const int8_t* X, const ConvShape& cs, float sA, int32_t zA,
+                    const qp_packed_info* w, const void* packedW, void* Y) {
   const uint8_t* blob = static_cast<const uint8_t*>(packedW);
   ConvKArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -325,20 +406,44 @@ qp_status launch_conv_implicit(const int8_t* X, const ConvShape& cs, float sA, i
   a.colsum = reinterpret_cast<const int32_t*>(blob + w->sum_off);
   a.zpB = reinterpret_cast<const int32_t*>(blob + w->zp_off);
   a.sB = reinterpret_cast<const float*>(blob + w->scale_off);
-  a.bias = bias;
   a.sA = sA;
-  a.sOut = sOut;
   a.zA = zA;
+  a.Y = Y;
+  a.ldy = w->N;
+  return a;
+}
+}  // namespace
+
+qp_status launch_conv_implicit(const int8_t* X, const ConvShape& cs, float sA, int32_t zA,
+                               const qp_packed_info* w, const void* packedW,
+                               const int32_t* bias, float sOut, int32_t zp_out, bool out32,
+                               int32_t relu, void* Y, hipStream_t stream) {
+  ConvKArgs a = conv_args(X, cs, sA, zA, w, packedW, Y);
+  a.bias = bias;
+  a.sOut = sOut;
   a.zp_out = zp_out;
   a.lo = relu ? zp_out : -128;
   a.hi = 127;
-  a.Y = Y;
-  a.ldy = w->N;
   if (a.M == 0) return QP_OK;
   const bool rowsum = w->has_zero_points != 0;
   if (out32)
     return rowsum ? launch_sel<true, true>(a, stream) : launch_sel<true, false>(a, stream);
   return rowsum ? launch_sel<false, true>(a, stream) : launch_sel<false, false>(a, stream);
+}
+
+qp_status launch_conv_implicit_blk(const int8_t* X, const ConvShape& cs, float sx, int32_t zx,
+                                   const qp_packed_info* w, const void* packedW,
+                                   const float* bias, float lo, float hi, float* Y,
+                                   hipStream_t stream) {
+  ConvKArgs a = conv_args(X, cs, sx, zx, w, packedW, Y);
+  a.sw_blk = a.sB;  // the block scales, [Npad][Kpad/group]
+  a.nblk = w->Kpad / w->group;
+  a.blk_shift = w->group == 128 ? 1 : 0;
+  a.bias_f = bias;
+  a.clo = lo;
+  a.chi = hi;
+  if (a.M == 0) return QP_OK;
+  return launch_sel<true, false, true>(a, stream);
 }
 
 }  // namespace qp

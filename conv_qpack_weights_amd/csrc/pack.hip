@@ -48,9 +48,10 @@ __global__ void write_header_kernel(BlobHeader h, uint8_t* blob) {
 // one contiguous kilobyte -- plus its scale, zero point and colsum (sum over
 // the real K only).
 // kBlock (format 5, block-quantized int8): instead, the row's block scales
-// scales[n*ldsw + b] (blocks of `group` K) and its weight kernel sum
-// wsum[n] = sum_b sw[n,b] * sum_{k in b} w[n,k] in fp64, from per-block
-// integer sums gathered in LDS.
+// scales[n*ldsw + b % period] (blocks of `group` K; OIHW weights repeat
+// their per-input-channel-block scales over the kernel taps, period =
+// IC/group) and its weight kernel sum wsum[n] = sum_b sw[n,b] * sum_{k in b}
+// w[n,k] in fp64, from per-block integer sums gathered in LDS.
 template <bool kBlock>
 __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__ w, int64_t N,
                                                       int64_t K, int64_t Kpad, int64_t sn, KMap km,
@@ -59,7 +60,8 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
                                                       int32_t zp, uint8_t* __restrict__ blob,
                                                       int64_t data_off, int64_t scale_off,
                                                       int64_t sum_off, int64_t zp_off,
-                                                      int64_t group, int64_t ldsw) {
+                                                      int64_t group, int64_t ldsw,
+                                                      int64_t period) {
   extern __shared__ int32_t block_sum[];  // kBlock: Kpad/group entries
   const int64_t n = blockIdx.x;
   const int t = threadIdx.x;
@@ -97,11 +99,11 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
     const int64_t Greal = (K + group - 1) / group;
     float* srow = reinterpret_cast<float*>(blob + scale_off) + n * nblk;
     for (int64_t b = t; b < nblk; b += 256)
-      srow[b] = (live && b < Greal) ? scales[n * ldsw + b] : 0.0f;
+      srow[b] = (live && b < Greal) ? scales[n * ldsw + b % period] : 0.0f;
     if (t == 0) {
       double acc = 0.0;
       for (int64_t b = 0; b < nblk; ++b)
-        acc = acc + (double)((live && b < Greal) ? scales[n * ldsw + b] : 0.0f) *
+        acc = acc + (double)((live && b < Greal) ? scales[n * ldsw + b % period] : 0.0f) *
                         (double)block_sum[b];
       reinterpret_cast<float*>(blob + sum_off)[n] = live ? (float)acc : 0.0f;
     }
@@ -378,7 +380,7 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     hipLaunchKernelGGL(pack_s8_kernel<false>, dim3((unsigned)g.Npad), dim3(256), 0, stream, src,
                        v.N, v.K, g.Kpad, v.sn, v.km, per_channel ? w->scales : nullptr, w->scale,
                        w->zero_points, w->zero_point, blob, g.data_off, g.scale_off, g.sum_off,
-                       g.zp_off, (int64_t)0, (int64_t)0);
+                       g.zp_off, (int64_t)0, (int64_t)0, (int64_t)1);
     if ((st = check_launch("qpack_weights int8"))) return st;
     g.has_zero_points = has_zp;
     g.scale_min = smin;
@@ -389,10 +391,19 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     if ((st = check_launch("qpack_weights header"))) return st;
     const size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / g.group);
     QP_REQUIRE(lds <= 65536, QP_EUNSUPPORTED, "block-quantized int8 packing: too many blocks");
+    // rank 2: scales [N][ceil(K/group)]; OIHW: [OC][IC/group], blocks of input
+    // channels, the same scale for every kernel tap
+    int64_t ldsw = ceil_div(v.K, g.group), period = ldsw;
+    if (w->rank == 4) {
+      const int64_t IC = w->shape[1];
+      QP_REQUIRE(IC % g.group == 0, QP_EINVAL,
+                 "channel-blocked conv weights: the block (%lld) must divide IC (%lld)",
+                 (long long)g.group, (long long)IC);
+      ldsw = period = IC / g.group;
+    }
     hipLaunchKernelGGL(pack_s8_kernel<true>, dim3((unsigned)g.Npad), dim3(256), lds, stream, src,
                        v.N, v.K, g.Kpad, v.sn, v.km, w->scales, 0.0f, (const int32_t*)nullptr, 0,
-                       blob, g.data_off, g.scale_off, g.sum_off, g.zp_off, g.group,
-                       ceil_div(v.K, g.group));
+                       blob, g.data_off, g.scale_off, g.sum_off, g.zp_off, g.group, ldsw, period);
     if ((st = check_launch("qpack_weights int8 blockwise"))) return st;
     g.has_zero_points = 0;
   } else {

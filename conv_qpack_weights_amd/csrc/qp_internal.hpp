@@ -88,6 +88,12 @@ qp_status launch_conv_implicit(const int8_t* X, const ConvShape& cs, float sA, i
                                const qp_packed_info* w, const void* packedW,
                                const int32_t* bias, float sOut, int32_t zp_out, bool out32,
                                int32_t relu, void* Y, hipStream_t stream);
+// The same gather with channel-blocked weights (a block-quantized int8 blob
+// packed from OIHW weights) and f32 output.
+qp_status launch_conv_implicit_blk(const int8_t* X, const ConvShape& cs, float sx, int32_t zx,
+                                   const qp_packed_info* w, const void* packedW,
+                                   const float* bias, float lo, float hi, float* Y,
+                                   hipStream_t stream);
 qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
                         const int32_t* bias, int64_t max_abs_bias, const qp_qtensor* out,
                         bool* out32);

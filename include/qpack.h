@@ -185,7 +185,10 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  * block-quantized int8 blob (format 5, QP_S8 with QP_BLOCKWISE, group 64 or
  *   128): the int8 sub-tiles of format 1 with Kpad = roundup(K, 128), then
  *   f32 scale[Npad][Kpad/group] (zero past K and N) and f32 wsum[Npad] =
- *   sum_b scale[n,b] * sum_{k in b} w[n,k] (fp64); no zero points.
+ *   sum_b scale[n,b] * sum_{k in b} w[n,k] (fp64); no zero points.  Rank-2
+ *   weights give scales [N][ceil(K/group)], one per K block; OIHW weights
+ *   give [OC][IC/group], one per block of input channels, stored repeated
+ *   for every kernel tap (group must divide IC).
  * All padding bytes are zero.  int4 values outside [-8,7] set the header word
  * at byte 108 to non-zero (it is 0 for valid input).
  *   w_dev        device weights laid out as w->shape / w->stride.
@@ -469,6 +472,29 @@ qp_status qconv2d_s8(const qp_qtensor* x, const int8_t* X, const qp_packed_info*
                      int32_t pad_r, int32_t dil_h, int32_t dil_w, const int32_t* bias_dev,
                      int64_t max_abs_bias, const qp_qtensor* y, int32_t relu, void* Y, void* ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qconv2d_s8_blockwise_f32 -- INT8 NHWC convolution with channel-blocked int8
+ * weights and f32 output ([MNN] _computeReorderQuantInfo and the dynamic-quant
+ * path of DenseConvInt8TiledExecutor with blockNum > 1: one weight scale per
+ * output channel and block of input channels, exact block sums combined in
+ * float):
+ *   Y[b,oy,ox,oc] = clamp(sx * sum_{ky,kx,ic} sw[oc][ic/icb] * (xp - zx) * w
+ *                         + bias[oc], lo, hi)      (xp = zx outside the image)
+ *   x        QP_S8 NHWC, contiguous, 16-byte aligned, per-tensor (sx, zx);
+ *            C a multiple of 16 and of icb.
+ *   w, packedW_dev  a block-quantized int8 blob packed from OIHW weights with
+ *            scheme QP_BLOCKWISE, group_size = icb (64 or 128) and scales
+ *            f32 [OC][IC/icb].
+ *   bias_dev f32 [OC] or NULL; Y device f32 NHWC [N, OH, OW, OC].
+ *   Geometry arguments as qconv2d_s8.  No workspace.  Implicit GEMM.
+ */
+qp_status qconv2d_s8_blockwise_f32(const qp_qtensor* x, const int8_t* X, const qp_packed_info* w,
+                                   const void* packedW_dev, int32_t KH, int32_t KW,
+                                   int32_t stride_h, int32_t stride_w, int32_t pad_t,
+                                   int32_t pad_l, int32_t pad_b, int32_t pad_r, int32_t dil_h,
+                                   int32_t dil_w, const float* bias_dev, float clamp_lo,
+                                   float clamp_hi, float* Y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -88,11 +88,11 @@ def test_a8w8b_unpack_and_conv_weights(qp, orc):
     """A 1x1 convolution's OIHW weights pack as K = C; unpack returns the
     values, the block scales and the dequantized weights (O9)."""
     rng = np.random.default_rng(9)
-    Wt = rng.integers(-128, 128, (24, 200, 1, 1)).astype(np.int8)
+    Wt = rng.integers(-128, 128, (24, 256, 1, 1)).astype(np.int8)
     sw = rng.uniform(1e-4, 1e-3, (24, 4)).astype(np.float32)
     blob, info = qp.pack_s8_blockwise(_dev(Wt), _dev(sw), block=64)
     w, sc, zp, dq = qp.qunpack_weights(blob, info, dequant=True)
-    W = Wt.reshape(24, 200)
+    W = Wt.reshape(24, 256)
     assert zp is None
     assert np.array_equal(_host(w), W) and np.array_equal(_host(sc), sw)
     assert np.array_equal(_host(dq), orc.dequant_weights_s4(W, sw, 64))
