@@ -35,7 +35,7 @@ namespace {
 
 struct W8B {
   const int8_t* data;  // 32x32 sub-tiles, [Npad/32][Kpad/32][32][32]
-  const float* scale;  // [Npad][nblk]
+  const float* scale;  // [nblk][Npad]: a block's scales of all channels side by side
   const float* wsum;   // [Npad]
   int64_t N, Npad, Kpad, kblocks, nblk;
 };
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
   const int64_t n = n0 + (lane & 15);
   const int8_t* wsrc =
       w.data + ((n >> 5) * w.kblocks + (c >> 1)) * 1024 + (n & 31) * 32 + (c & 1) * 16;
-  const float* ssrc = w.scale + n * w.nblk;
+  const float* ssrc = w.scale + n;  // + block * Npad
 
   // ---- activation direct loads (as the A8W4 GEMM) ----
   const int8_t* const a_base = qa + mw * lda;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
 #pragma unroll
     for (int s = 0; s < 2; ++s) wr[u][s] = *reinterpret_cast<const v4i*>(wsrc + b * 4096 + s * 2048);
 #pragma unroll
-    for (int s = 0; s < NSC; ++s) sr[u][s] = ssrc[b * NSC + s];
+    for (int s = 0; s < NSC; ++s) sr[u][s] = ssrc[(b * NSC + s) * w.Npad];
   };
 
   auto step = [&](int u, int64_t j) {

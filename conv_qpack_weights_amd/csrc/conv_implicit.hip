@@ -56,7 +56,8 @@ struct ConvKArgs {
   int64_t ldy;
   int32_t tiles_n;
   // channel-blocked weights (f32 output): scale of channel n and K block kb
-  // at sw_blk[n*nblk + kb], blocks of 64 << blk_shift K
+  // at sw_blk[kb*Npad + n], blocks of 64 << blk_shift K
+  int64_t Npad;
   const float* sw_blk;
   int64_t nblk;
   int32_t blk_shift;
@@ -82,7 +83,7 @@ template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
 __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   constexpr int BM = 4 * FM * 16;  // four waves stacked along the pixels
   constexpr int BN = FN * 16;
-  constexpr int LOADS = FM + FN + (kBlk ? 4 * FN : 0);  // loads per K-step and lane
+  constexpr int LOADS = FM + FN + (kBlk ? FN : 0);  // loads per K-step and lane
   static_assert((P - 1) * LOADS < 64, "vmcnt range");
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
 
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   v4i ar[P][FM], br[P][FN];
   uint32_t vbits[P];  // bit j: fragment j's piece is an in-image load
   int32_t fill[P];    // the pattern of the other pieces: zero point, or 0 past K
-  float swr[kBlk ? P : 1][FN][4];  // kBlk: the step's block scale, channels 4*grp+r
+  float4 swr[kBlk ? P : 1][FN];  // kBlk: the step's block scales of channels 4*grp..+3
   auto issue = [&](int slot, int kt) {
     const int k = kt * 64 + grp * 16;
     const int tap = div_small(k, g.C, g.rcpC);
@@ -171,9 +172,8 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
       const int64_t kb = kc >> g.blk_shift;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          swr[slot][i][r] = g.sw_blk[(n0 + i * 16 + 4 * grp + r) * g.nblk + kb];
+        swr[slot][i] =
+            *reinterpret_cast<const float4*>(g.sw_blk + kb * g.Npad + n0 + i * 16 + 4 * grp);
     }
   };
   float accf[kBlk ? FN : 1][kBlk ? FM : 1][4];
@@ -222,8 +222,10 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
         v4i d[FN][FM], e[FN];
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[i][r] = swr[u][i][r];
+          sc[i][0] = swr[u][i].x;
+          sc[i][1] = swr[u][i].y;
+          sc[i][2] = swr[u][i].z;
+          sc[i][3] = swr[u][i].w;
           e[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], zop, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
           for (int j = 0; j < FM; ++j)
@@ -356,11 +358,11 @@ qp_status launch_depth(const ConvKArgs& a, hipStream_t stream) {
 
 template <bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_sel(const ConvKArgs& a, hipStream_t stream) {
-  if constexpr (kBlk) {
-    // four scale loads per channel quad and step: 32-channel tiles keep the
-    // loads in flight within the wait counter's range
-    if (ceil_div(a.M, 128) * ceil_div(a.N, 32) >= 512)
-      return launch_depth<2, 2, kOut32, kRowSum, kBlk>(a, stream);
+  if constexpr (kBlk) {  // (one more load per fragment and step: the scales)
+    if (ceil_div(a.M, 128) * ceil_div(a.N, 64) >= 512)
+      return launch_depth<2, 4, kOut32, kRowSum, kBlk>(a, stream);
+    if (ceil_div(a.M, 64) * ceil_div(a.N, 64) >= 256 && a.N > 32)
+      return launch_depth<1, 4, kOut32, kRowSum, kBlk>(a, stream);
     return launch_depth<1, 2, kOut32, kRowSum, kBlk>(a, stream);
   } else {
     // Two 128-pixel workgroups per compute unit or more: 32 pixels per wave
@@ -436,7 +438,8 @@ qp_status launch_conv_implicit_blk(const int8_t* X, const ConvShape& cs, float s
                                    const float* bias, float lo, float hi, float* Y,
                                    hipStream_t stream) {
   ConvKArgs a = conv_args(X, cs, sx, zx, w, packedW, Y);
-  a.sw_blk = a.sB;  // the block scales, [Npad][Kpad/group]
+  a.sw_blk = a.sB;  // the block scales, [Kpad/group][Npad]
+  a.Npad = w->Npad;
   a.nblk = w->Kpad / w->group;
   a.blk_shift = w->group == 128 ? 1 : 0;
   a.bias_f = bias;

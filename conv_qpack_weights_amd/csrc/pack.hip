@@ -48,7 +48,8 @@ __global__ void write_header_kernel(BlobHeader h, uint8_t* blob) {
 // one contiguous kilobyte -- plus its scale, zero point and colsum (sum over
 // the real K only).
 // kBlock (format 5, block-quantized int8): instead, the row's block scales
-// scales[n*ldsw + b % period] (blocks of `group` K; OIHW weights repeat
+// scales[n*ldsw + b % period], stored block-major ([nblk][Npad], so a
+// block's scales of consecutive channels are adjacent) (blocks of `group` K; OIHW weights repeat
 // their per-input-channel-block scales over the kernel taps, period =
 // IC/group) and its weight kernel sum wsum[n] = sum_b sw[n,b] * sum_{k in b}
 // w[n,k] in fp64, from per-block integer sums gathered in LDS.
@@ -97,9 +98,10 @@ __global__ __launch_bounds__(256) void pack_s8_kernel(const int8_t* __restrict__
   if constexpr (kBlock) {
     __syncthreads();
     const int64_t Greal = (K + group - 1) / group;
-    float* srow = reinterpret_cast<float*>(blob + scale_off) + n * nblk;
+    const int64_t Npad = gridDim.x;  // one workgroup per padded channel
+    float* scol = reinterpret_cast<float*>(blob + scale_off) + n;  // [nblk][Npad]
     for (int64_t b = t; b < nblk; b += 256)
-      srow[b] = (live && b < Greal) ? scales[n * ldsw + b % period] : 0.0f;
+      scol[b * Npad] = (live && b < Greal) ? scales[n * ldsw + b % period] : 0.0f;
     if (t == 0) {
       double acc = 0.0;
       for (int64_t b = 0; b < nblk; ++b)

@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void unpack_s8_kernel(const uint8_t* __restric
   if (w) w[i * ldw + k] = q;
   if (deq) {
     if (b.format == 5) {  // a scale per block of `group` K, no zero point
-      const float s = reinterpret_cast<const float*>(blob + b.scale_off)[n * (b.Kpad / b.group) +
-                                                                           k / b.group];
+      const float s = reinterpret_cast<const float*>(blob + b.scale_off)[(k / b.group) * b.Npad + n];
       deq[i * ldd + k] = s * (float)q;
     } else {
       const float s = reinterpret_cast<const float*>(blob + b.scale_off)[n];
@@ -101,8 +100,7 @@ __global__ __launch_bounds__(256) void unpack_scales_kernel(const uint8_t* __res
     if (zp) zp[i] = reinterpret_cast<const int32_t*>(blob + b.zp_off)[n];
   } else if (b.format == 5) {
     if (scales)
-      scales[i * lds + g] =
-          reinterpret_cast<const float*>(blob + b.scale_off)[n * (b.Kpad / b.group) + g];
+      scales[i * lds + g] = reinterpret_cast<const float*>(blob + b.scale_off)[g * b.Npad + n];
   } else if (scales) {
     const int64_t Gq = (b.Kpad / b.group + 3) / 4;
     const int64_t e = ((n / 16) * Gq + g / 4) * 64 + (n % 16) * 4 + g % 4;

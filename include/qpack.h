@@ -184,7 +184,7 @@ qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis
  *   [MNN] _computeReorderQuantInfo / BatchAsyDynamicQuant).
  * block-quantized int8 blob (format 5, QP_S8 with QP_BLOCKWISE, group 64 or
  *   128): the int8 sub-tiles of format 1 with Kpad = roundup(K, 128), then
- *   f32 scale[Npad][Kpad/group] (zero past K and N) and f32 wsum[Npad] =
+ *   f32 scale[Kpad/group][Npad] (block-major; zero past K and N) and f32 wsum[Npad] =
  *   sum_b scale[n,b] * sum_{k in b} w[n,k] (fp64); no zero points.  Rank-2
  *   weights give scales [N][ceil(K/group)], one per K block; OIHW weights
  *   give [OC][IC/group], one per block of input channels, stored repeated
