@@ -61,6 +61,7 @@ struct ConvKArgs {
   const float* sw_blk;
   int64_t nblk;
   int32_t blk_shift;
+  int32_t sw_in_lds;  // the workgroup's scale columns are staged in LDS
   const float* bias_f;
   float clo, chi;
 };
@@ -75,17 +76,20 @@ __device__ __forceinline__ int div_small(int k, int d, float rcp) {
 }
 
 // kBlk: channel-blocked weights with f32 output.  Each K-step's products are
-// kept apart: d = MFMA(weights, pieces) and e = MFMA(weights, the input zero
-// point over the real K), so d - e is the step's exact sum of (x - zx)*w,
-// which is scaled by its block's weight scale into an f32 sum; the output
-// is sx * that + bias, clamped.
+// kept apart: e = MFMA(weights, the input zero point), then
+// d = MFMA(weights, pieces) accumulated onto -e, so d is the step's exact
+// sum of (x - zx)*w, which is scaled by its block's weight scale into an
+// f32 sum; the output is sx * that + bias, clamped.  The workgroup's block
+// scales ([nblk][BN]) are copied to LDS once when they fit, else each step
+// reads them from memory.
 template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
 __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   constexpr int BM = 4 * FM * 16;  // four waves stacked along the pixels
   constexpr int BN = FN * 16;
-  constexpr int LOADS = FM + FN + (kBlk ? FN : 0);  // loads per K-step and lane
+  constexpr int LOADS = FM + FN;  // loads per K-step and lane
   static_assert((P - 1) * LOADS < 64, "vmcnt range");
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+  extern __shared__ float sw_tile[];  // kBlk with sw_in_lds: [nblk][BN]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,11 +144,20 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
                (grp & 1) * 16;
   }
   const int32_t zfill = (int32_t)(0x01010101u * (uint32_t)(uint8_t)(int8_t)g.zA);
+  if constexpr (kBlk) {
+    if (g.sw_in_lds) {
+      const float* src = g.sw_blk + n0;
+      for (int t = tid; t < (int)g.nblk * BN; t += 256) {
+        const int kb = t / BN;
+        sw_tile[t] = src[(int64_t)kb * g.Npad + (t - kb * BN)];
+      }
+      __syncthreads();
+    }
+  }
 
   v4i ar[P][FM], br[P][FN];
   uint32_t vbits[P];  // bit j: fragment j's piece is an in-image load
   int32_t fill[P];    // the pattern of the other pieces: zero point, or 0 past K
-  float4 swr[kBlk ? P : 1][FN];  // kBlk: the step's block scales of channels 4*grp..+3
   auto issue = [&](int slot, int kt) {
     const int k = kt * 64 + grp * 16;
     const int tap = div_small(k, g.C, g.rcpC);
@@ -168,13 +181,6 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     const int64_t kc = kt < g.nk ? kt : g.nk - 1;
 #pragma unroll
     for (int i = 0; i < FN; ++i) br[slot][i] = *reinterpret_cast<const v4i*>(b_src[i] + kc * 2048);
-    if constexpr (kBlk) {
-      const int64_t kb = kc >> g.blk_shift;
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        swr[slot][i] =
-            *reinterpret_cast<const float4*>(g.sw_blk + kb * g.Npad + n0 + i * 16 + 4 * grp);
-    }
   };
   float accf[kBlk ? FN : 1][kBlk ? FM : 1][4];
 #pragma unroll
@@ -218,27 +224,38 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
       if constexpr (kBlk) {
         // the input zero point over this lane's real K (0 past K)
         const v4i zop = v4i{fill[u], fill[u], fill[u], fill[u]};
-        float sc[FN][4];
-        v4i d[FN][FM], e[FN];
+        const int kt = kt0 + u;
+        const int kb = (kt < g.nk ? kt : g.nk - 1) >> g.blk_shift;
+        float4 sc[FN];
+        if (g.sw_in_lds) {
+#pragma unroll
+          for (int i = 0; i < FN; ++i)
+            sc[i] = *reinterpret_cast<const float4*>(sw_tile + kb * BN + i * 16 + 4 * grp);
+        } else {
+#pragma unroll
+          for (int i = 0; i < FN; ++i)
+            sc[i] = *reinterpret_cast<const float4*>(g.sw_blk + (int64_t)kb * g.Npad + n0 +
+                                                     i * 16 + 4 * grp);
+        }
+        v4i d[FN][FM];
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-          sc[i][0] = swr[u][i].x;
-          sc[i][1] = swr[u][i].y;
-          sc[i][2] = swr[u][i].z;
-          sc[i][3] = swr[u][i].w;
-          e[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], zop, v4i{0, 0, 0, 0}, 0, 0, 0);
+          v4i e = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], zop, v4i{0, 0, 0, 0}, 0, 0, 0);
+          e = v4i{0, 0, 0, 0} - e;
 #pragma unroll
           for (int j = 0; j < FM; ++j)
-            d[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], a[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+            d[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(br[u][i], a[j], e, 0, 0, 0);
         }
         issue(u, kt0 + u + P);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
-          for (int j = 0; j < FM; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              accf[i][j][r] = __builtin_fmaf(sc[i][r], (float)(d[i][j][r] - e[i][r]), accf[i][j][r]);
+          for (int j = 0; j < FM; ++j) {
+            accf[i][j][0] = __builtin_fmaf(sc[i].x, (float)d[i][j][0], accf[i][j][0]);
+            accf[i][j][1] = __builtin_fmaf(sc[i].y, (float)d[i][j][1], accf[i][j][1]);
+            accf[i][j][2] = __builtin_fmaf(sc[i].z, (float)d[i][j][2], accf[i][j][2]);
+            accf[i][j][3] = __builtin_fmaf(sc[i].w, (float)d[i][j][3], accf[i][j][3]);
+          }
         continue;
       }
 #pragma unroll
@@ -335,14 +352,22 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   }
 }
 
+// Largest LDS copy of a workgroup's block scales.
+constexpr int64_t kScaleTileBytes = 32 * 1024;
+
 template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_cfg(ConvKArgs a, hipStream_t stream) {
   constexpr int BM = 4 * FM * 16, BN = FN * 16;
   a.tiles_n = (int32_t)ceil_div(a.N, BN);
   const int64_t blocks = ceil_div(a.M, BM) * a.tiles_n;
   QP_REQUIRE(blocks < (INT64_C(1) << 31), QP_EUNSUPPORTED, "qconv2d: too many tiles");
+  size_t lds = 0;
+  if (kBlk && a.nblk * BN * 4 <= kScaleTileBytes) {
+    a.sw_in_lds = 1;
+    lds = (size_t)(a.nblk * BN * 4);
+  }
   hipLaunchKernelGGL((conv_implicit_kernel<FM, FN, P, kOut32, kRowSum, kBlk>), dim3((unsigned)blocks),
-                     dim3(256), 0, stream, a);
+                     dim3(256), lds, stream, a);
   return check_launch("qconv2d implicit kernel");
 }
 
@@ -350,19 +375,22 @@ qp_status launch_cfg(ConvKArgs a, hipStream_t stream) {
 // steps fall past the end of K.
 template <int FM, int FN, bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_depth(const ConvKArgs& a, hipStream_t stream) {
-  if (a.nk <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum, kBlk>(a, stream);
-  if (a.nk % 4 != 0 && a.nk % 3 == 0)
-    return launch_cfg<FM, FN, 3, kOut32, kRowSum, kBlk>(a, stream);
-  return launch_cfg<FM, FN, 4, kOut32, kRowSum, kBlk>(a, stream);
+  if constexpr (kBlk) {  // (the per-step rescaling holds more registers: depth 2)
+    return launch_cfg<FM, FN, 2, kOut32, kRowSum, kBlk>(a, stream);
+  } else {
+    if (a.nk <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum>(a, stream);
+    if (a.nk % 4 != 0 && a.nk % 3 == 0) return launch_cfg<FM, FN, 3, kOut32, kRowSum>(a, stream);
+    return launch_cfg<FM, FN, 4, kOut32, kRowSum>(a, stream);
+  }
 }
 
 template <bool kOut32, bool kRowSum, bool kBlk = false>
 qp_status launch_sel(const ConvKArgs& a, hipStream_t stream) {
-  if constexpr (kBlk) {  // (one more load per fragment and step: the scales)
-    if (ceil_div(a.M, 128) * ceil_div(a.N, 64) >= 512)
-      return launch_depth<2, 4, kOut32, kRowSum, kBlk>(a, stream);
-    if (ceil_div(a.M, 64) * ceil_div(a.N, 64) >= 256 && a.N > 32)
-      return launch_depth<1, 4, kOut32, kRowSum, kBlk>(a, stream);
+  if constexpr (kBlk) {
+    // The per-step rescaling holds FN*FM*4 more registers: 32-channel tiles
+    // keep the occupancy (measured faster than 64-channel ones).
+    if (ceil_div(a.M, 128) * ceil_div(a.N, 32) >= 512)
+      return launch_depth<2, 2, kOut32, kRowSum, kBlk>(a, stream);
     return launch_depth<1, 2, kOut32, kRowSum, kBlk>(a, stream);
   } else {
     // Two 128-pixel workgroups per compute unit or more: 32 pixels per wave
