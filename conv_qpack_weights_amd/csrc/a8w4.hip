@@ -331,8 +331,9 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
                                                         int64_t ldy, int64_t ldsz) {
   static_assert(!kBQ || kKind != 2, "per-block activations take symmetric weights");
   static_assert(RW * CW * KS == 4, "four waves");
-  // weight prefetch depth in blocks (kBQ holds more per block: two)
-  constexpr int P = kBQ ? 2 : (FM * FN >= 4 ? 3 : 5);
+  // weight prefetch depth in blocks (kBQ holds more per block: two); a
+  // deeper ring measured slower (more registers, lower occupancy)
+  constexpr int P = kBQ ? 2 : 3;
   constexpr int R = 4;                      // activation ring stages
   constexpr int MT = 16 * FM * RW;          // rows per workgroup
   constexpr int SLOTS = KS * MT * 8;        // 16-byte pieces per stage
@@ -794,7 +795,7 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                       float hi, float* Y, int64_t ldy, hipStream_t stream, int64_t ldsz = 0) {
   // <FM, FN, RW, CW, KS>: rows per workgroup 16*FM*RW, channels 16*FN*CW.
   // Small M splits K over the waves (enough waves stream the weights); larger
-  // M shares each staged activation row among four channel groups.
+  // M shares each staged activation row among several channel groups.
   if (M <= 16)
     return launch_gemm_cfg<1, 1, 1, 1, 4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
@@ -802,7 +803,10 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   if (M <= 32 || ldsz > 0)
     return launch_gemm_cfg<2, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
-  return launch_gemm_cfg<4, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
+  // 64 rows x 32 channels a workgroup (two row and two channel groups):
+  // measured faster than 64 x 64 with four channel groups, whose 256-VGPR
+  // waves fit two a SIMD
+  return launch_gemm_cfg<2, 1, 2, 2, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
                                         stream);
 }
 
