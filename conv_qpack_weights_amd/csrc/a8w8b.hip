@@ -276,7 +276,8 @@ qp_status launch_a8w8b(const int8_t* qa, int64_t lda, const float* sa, const int
   // small M: four K ranges per 16-channel fragment; otherwise four channel
   // fragments share the staged rows
   if (M <= 16) return launch_cfg<1, 1, 4>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
-  if (M <= 32) return launch_cfg<2, 4, 1>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
+  // (32-row workgroups up to M = 128: more of them, measured faster there)
+  if (M <= 128) return launch_cfg<2, 4, 1>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
   return launch_cfg<4, 4, 1>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
 }
 
