@@ -82,13 +82,19 @@ __device__ __forceinline__ int div_small(int k, int d, float rcp) {
 // f32 sum; the output is sx * that + bias, clamped.  The workgroup's block
 // scales ([nblk][BN]) are copied to LDS once when they fit, else each step
 // reads them from memory.
-template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
+// KSP == 4 (few output tiles): the four waves share one tile of pixels and
+// take every fourth K-step each (wave w: steps w, w+4, ...); their sums are
+// added through LDS and wave 0 writes the tile.
+template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false, int KSP = 1>
 __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
-  constexpr int BM = 4 * FM * 16;  // four waves stacked along the pixels
+  static_assert(KSP == 1 || KSP == 4, "K split over 1 or 4 waves");
+  constexpr int BM = (KSP == 1 ? 4 : 1) * FM * 16;  // four waves stacked along the pixels, or one tile
   constexpr int BN = FN * 16;
   constexpr int LOADS = FM + FN;  // loads per K-step and lane
   static_assert((P - 1) * LOADS < 64, "vmcnt range");
+  constexpr int NRED = FN * FM * 4 + FM;  // a lane's partial sums (and row sums)
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+  __shared__ int32_t red[KSP > 1 ? KSP - 1 : 1][KSP > 1 ? NRED : 1][64];
   extern __shared__ float sw_tile[];  // kBlk with sw_in_lds: [nblk][BN]
 
   const int tid = threadIdx.x;
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   // channel tiles fastest, so neighbouring workgroups read the same pixels
   const int tile_n = (int)(blockIdx.x % (unsigned)g.tiles_n);
   const int64_t tile_m = blockIdx.x / (unsigned)g.tiles_n;
-  const int64_t m0 = tile_m * BM + wave * FM * 16;
+  const int64_t m0 = tile_m * BM + (KSP == 1 ? wave * FM * 16 : 0);
   const int64_t n0 = (int64_t)tile_n * BN;
 
   // ---- per-column epilogue constants (read after the main loop) ----
@@ -158,7 +164,8 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   v4i ar[P][FM], br[P][FN];
   uint32_t vbits[P];  // bit j: fragment j's piece is an in-image load
   int32_t fill[P];    // the pattern of the other pieces: zero point, or 0 past K
-  auto issue = [&](int slot, int kt) {
+  auto issue = [&](int slot, int j) {  // j: this wave's step -> K-step kt
+    const int kt = KSP == 1 ? j : j * KSP + wave;
     const int k = kt * 64 + grp * 16;
     const int tap = div_small(k, g.C, g.rcpC);
     const int ic = k - tap * g.C;
@@ -201,7 +208,8 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
 
 #pragma unroll
   for (int p = 0; p < P; ++p) issue(p, p);
-  const int nsteps = (g.nk + P - 1) / P * P;
+  const int nloc = (g.nk + KSP - 1) / KSP;  // steps of one wave (the last may be past K)
+  const int nsteps = (nloc + P - 1) / P * P;
   for (int kt0 = 0; kt0 < nsteps; kt0 += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
       if constexpr (kBlk) {
         // the input zero point over this lane's real K (0 past K)
         const v4i zop = v4i{fill[u], fill[u], fill[u], fill[u]};
-        const int kt = kt0 + u;
+        const int kt = KSP == 1 ? kt0 + u : (kt0 + u) * KSP + wave;
         const int kb = (kt < g.nk ? kt : g.nk - 1) >> g.blk_shift;
         float4 sc[FN];
         if (g.sw_in_lds) {
@@ -267,6 +275,38 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     }
   }
   wait_vmcnt<0>();
+  if constexpr (KSP > 1) {  // add the waves' partial sums (this barrier also publishes
+                            // the column constants)
+    if (wave > 0) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            red[wave - 1][(i * FM + j) * 4 + r][lane] =
+                kBlk ? __builtin_bit_cast(int32_t, accf[i][j][r]) : acc[i][j][r];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) red[wave - 1][FN * FM * 4 + j][lane] = rsum[j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KSP - 1; ++w) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int32_t v = red[w][(i * FM + j) * 4 + r][lane];
+            if constexpr (kBlk) accf[i][j][r] = accf[i][j][r] + __builtin_bit_cast(float, v);
+            else acc[i][j][r] = acc[i][j][r] + v;
+          }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) rsum[j] += red[w][FN * FM * 4 + j][lane];
+    }
+  }
   if constexpr (kBlk) {  // y = sx * sum + bias, clamped; lane: channels 4*grp+r of row r16
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -288,7 +328,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     }
     return;
   }
-  __syncthreads();  // the column constants
+  if constexpr (KSP == 1) __syncthreads();  // the column constants
 
   // Row sums: the four lanes of a pixel hold the four K pieces.
   int32_t rs[FM];
@@ -355,9 +395,9 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
 // Largest LDS copy of a workgroup's block scales.
 constexpr int64_t kScaleTileBytes = 32 * 1024;
 
-template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false>
+template <int FM, int FN, int P, bool kOut32, bool kRowSum, bool kBlk = false, int KSP = 1>
 qp_status launch_cfg(ConvKArgs a, hipStream_t stream) {
-  constexpr int BM = 4 * FM * 16, BN = FN * 16;
+  constexpr int BM = (KSP == 1 ? 4 : 1) * FM * 16, BN = FN * 16;
   a.tiles_n = (int32_t)ceil_div(a.N, BN);
   const int64_t blocks = ceil_div(a.M, BM) * a.tiles_n;
   QP_REQUIRE(blocks < (INT64_C(1) << 31), QP_EUNSUPPORTED, "qconv2d: too many tiles");
@@ -366,21 +406,22 @@ qp_status launch_cfg(ConvKArgs a, hipStream_t stream) {
     a.sw_in_lds = 1;
     lds = (size_t)(a.nblk * BN * 4);
   }
-  hipLaunchKernelGGL((conv_implicit_kernel<FM, FN, P, kOut32, kRowSum, kBlk>), dim3((unsigned)blocks),
-                     dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((conv_implicit_kernel<FM, FN, P, kOut32, kRowSum, kBlk, KSP>),
+                     dim3((unsigned)blocks), dim3(256), lds, stream, a);
   return check_launch("qconv2d implicit kernel");
 }
 
 // The K loop runs in whole groups of P steps; P is picked so that few
 // steps fall past the end of K.
-template <int FM, int FN, bool kOut32, bool kRowSum, bool kBlk = false>
+template <int FM, int FN, bool kOut32, bool kRowSum, bool kBlk = false, int KSP = 1>
 qp_status launch_depth(const ConvKArgs& a, hipStream_t stream) {
   if constexpr (kBlk) {  // (the per-step rescaling holds more registers: depth 2)
-    return launch_cfg<FM, FN, 2, kOut32, kRowSum, kBlk>(a, stream);
+    return launch_cfg<FM, FN, 2, kOut32, kRowSum, kBlk, KSP>(a, stream);
   } else {
-    if (a.nk <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum>(a, stream);
-    if (a.nk % 4 != 0 && a.nk % 3 == 0) return launch_cfg<FM, FN, 3, kOut32, kRowSum>(a, stream);
-    return launch_cfg<FM, FN, 4, kOut32, kRowSum>(a, stream);
+    const int64_t n = ceil_div((int64_t)a.nk, KSP);  // steps per wave
+    if (n <= 2) return launch_cfg<FM, FN, 2, kOut32, kRowSum, false, KSP>(a, stream);
+    if (n % 4 != 0 && n % 3 == 0) return launch_cfg<FM, FN, 3, kOut32, kRowSum, false, KSP>(a, stream);
+    return launch_cfg<FM, FN, 4, kOut32, kRowSum, false, KSP>(a, stream);
   }
 }
 
@@ -391,6 +432,8 @@ qp_status launch_sel(const ConvKArgs& a, hipStream_t stream) {
     // keep the occupancy (measured faster than 64-channel ones).
     if (ceil_div(a.M, 128) * ceil_div(a.N, 32) >= 512)
       return launch_depth<2, 2, kOut32, kRowSum, kBlk>(a, stream);
+    if (ceil_div(a.M, 64) * ceil_div(a.N, 32) < 256 && a.nk >= 4)
+      return launch_depth<1, 2, kOut32, kRowSum, kBlk, 4>(a, stream);
     return launch_depth<1, 2, kOut32, kRowSum, kBlk>(a, stream);
   } else {
     // Two 128-pixel workgroups per compute unit or more: 32 pixels per wave
@@ -400,6 +443,10 @@ qp_status launch_sel(const ConvKArgs& a, hipStream_t stream) {
       return launch_depth<2, 4, kOut32, kRowSum>(a, stream);
     if (ceil_div(a.M, 64) * ceil_div(a.N, 64) >= 256 && a.N > 32)
       return launch_depth<1, 4, kOut32, kRowSum>(a, stream);
+    // Few tiles (a small image): the four waves of a workgroup split the
+    // K-steps of one 16-pixel tile, four times the workgroups.
+    if (ceil_div(a.M, 64) * ceil_div(a.N, 32) < 256 && a.nk >= 4)
+      return launch_depth<1, 2, kOut32, kRowSum, false, 4>(a, stream);
     return launch_depth<1, 2, kOut32, kRowSum>(a, stream);
   }
 }
