@@ -64,6 +64,7 @@ SIGNATURES = {
     "qp_last_error": (C.c_char_p, []),
     "qpack_weights_size": (C.c_int, [_QT, _I32, _I32, _SZ, _SZ]),
     "qpack_weights": (C.c_int, [_QT, _P, _I32, _I32, _P, C.c_size_t, _PI, _P]),
+    "qrepack_weights": (C.c_int, [_QT, _P, _I32, _I32, _P, _PI, _P]),
     "qp_packed_info_from_header": (C.c_int, [_P, _PI]),
     "qunpack_weights": (C.c_int, [_PI, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I64, _P]),
     "qquantize_rows_s8": (C.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P]),
@@ -182,8 +183,15 @@ def qpack_weights_size(desc: QTensor, k_axis: int, n_axis: int):
     return nb.value, al.value
 
 
-def qpack_weights(w: torch.Tensor, desc: QTensor, k_axis: int, n_axis: int):
-    """Pack device weights ``w`` described by ``desc``; returns (blob, PackedInfo)."""
+def qpack_weights(w: torch.Tensor, desc: QTensor, k_axis: int, n_axis: int, into=None):
+    """Pack device weights ``w`` described by ``desc``; returns (blob, PackedInfo).
+    ``into=(blob, info)``: refill that existing blob in place instead
+    (qrepack_weights; same shape and format required), returning it."""
+    if into is not None:
+        blob, info = into
+        _check(_lib.qrepack_weights(C.byref(desc), _ptr(w), k_axis, n_axis, _ptr(blob),
+                                    C.byref(info), _stream(w.device)), "qrepack_weights")
+        return blob, info
     nbytes, _ = qpack_weights_size(desc, k_axis, n_axis)
     blob = _alloc_bytes(nbytes, w.device)
     info = PackedInfo()
@@ -193,8 +201,9 @@ def qpack_weights(w: torch.Tensor, desc: QTensor, k_axis: int, n_axis: int):
 
 
 def pack_s8(w: torch.Tensor, scales=None, scale=1.0, zero_points=None, zero_point=0,
-            k_axis=None, n_axis=None):
-    """Pack int8 weights: rank 2 ([N,K] by default) or rank 4 OIHW."""
+            k_axis=None, n_axis=None, into=None):
+    """Pack int8 weights: rank 2 ([N,K] by default) or rank 4 OIHW.
+    ``into=(blob, info)`` refills an existing blob of the same shape."""
     if w.dim() == 4:
         k_axis, n_axis = 1, 0
     elif k_axis is None:
@@ -202,25 +211,26 @@ def pack_s8(w: torch.Tensor, scales=None, scale=1.0, zero_points=None, zero_poin
     scheme = QP_PER_CHANNEL if scales is not None else QP_PER_TENSOR
     desc = qtensor(QP_S8, list(w.shape), [s for s in w.stride()], scheme=scheme, scale=scale,
                    scales=scales, zero_point=zero_point, zero_points=zero_points, axis=n_axis)
-    return qpack_weights(w, desc, k_axis, n_axis)
+    return qpack_weights(w, desc, k_axis, n_axis, into)
 
 
-def pack_s8_blockwise(w: torch.Tensor, scales: torch.Tensor, block=128):
+def pack_s8_blockwise(w: torch.Tensor, scales: torch.Tensor, block=128, into=None):
     """Pack int8 weights with one f32 scale per channel and block: rank 2
     [N, K] with scales [N, ceil(K/block)] (blocks of K), or OIHW with scales
     [OC, IC/block] (blocks of input channels, every kernel tap)."""
     k_axis, n_axis = 1, 0
     desc = qtensor(QP_S8, list(w.shape), list(w.stride()), scheme=QP_BLOCKWISE, scales=scales,
                    group_size=block, axis=n_axis)
-    return qpack_weights(w, desc, k_axis, n_axis)
+    return qpack_weights(w, desc, k_axis, n_axis, into)
 
 
 def pack_s4(w: torch.Tensor, scales: torch.Tensor, group_size=32, scale_dtype="f32",
-            offsets=None):
+            offsets=None, into=None):
     """Pack int4 values (one per int8 byte, in [-8,7]) given as [N, K] with
     f32 group scales [N, ceil(K/group)]; scale_dtype "bf16" stores the
     scales rounded to bf16; `offsets` [N, ceil(K/group)] makes the weights
-    asymmetric (real weight = scale*q + offset)."""
+    asymmetric (real weight = scale*q + offset).  ``into=(blob, info)``
+    refills an existing blob of the same shape and format."""
     scheme = {"f32": QP_BLOCKWISE, "bf16": QP_BLOCKWISE_BF16}[scale_dtype]
     if offsets is not None:
         assert scale_dtype == "f32", "asymmetric int4 keeps f32 scales"
@@ -228,7 +238,7 @@ def pack_s4(w: torch.Tensor, scales: torch.Tensor, group_size=32, scale_dtype="f
         scales = torch.stack((offsets.float(), scales.float()), dim=-1).contiguous()
     desc = qtensor(QP_S4, list(w.shape), list(w.stride()), scheme=scheme, scales=scales,
                    group_size=group_size, axis=0)
-    return qpack_weights(w, desc, 1, 0)
+    return qpack_weights(w, desc, 1, 0, into)
 
 
 def qp_packed_info_from_header(header: bytes) -> PackedInfo:

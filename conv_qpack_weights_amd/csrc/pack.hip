@@ -433,3 +433,36 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
   *info = g;
   return QP_OK;
 }
+
+extern "C" qp_status qrepack_weights(const qp_qtensor* w, const void* w_dev, int32_t k_axis,
+                                     int32_t n_axis, void* packed_dev, qp_packed_info* info,
+                                     hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  QP_REQUIRE(w && info, QP_EINVAL, "qrepack_weights: null argument");
+  WeightView v;
+  qp_status st = weight_view(w, k_axis, n_axis, &v);
+  if (st) return st;
+  int32_t format = 0;
+  if ((st = format_of(w, &format))) return st;
+  qp_packed_info g;
+  if ((st = blob_geometry(format, w->scheme, v.N, v.K, format != 1 ? w->group_size : 0, &g)))
+    return st;
+  QP_REQUIRE(g.format == info->format && g.scheme == info->scheme && g.N == info->N &&
+                 g.K == info->K && g.group == info->group && g.Npad == info->Npad &&
+                 g.Kpad == info->Kpad && g.data_off == info->data_off &&
+                 g.scale_off == info->scale_off && g.sum_off == info->sum_off &&
+                 g.zp_off == info->zp_off && g.total_bytes == info->total_bytes,
+             QP_EINVAL,
+             "qrepack_weights: the buffer holds format %d (scheme %d) N=%lld K=%lld group=%lld; "
+             "these weights need format %d (scheme %d) N=%lld K=%lld group=%lld",
+             info->format, info->scheme, (long long)info->N, (long long)info->K,
+             (long long)info->group, g.format, g.scheme, (long long)g.N, (long long)g.K,
+             (long long)g.group);
+  qp_packed_info out;
+  st = qpack_weights(w, w_dev, k_axis, n_axis, packed_dev, (size_t)info->total_bytes, &out,
+                     stream);
+  if (st) return st;
+  *info = out;
+  return QP_OK;
+}

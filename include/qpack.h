@@ -201,6 +201,25 @@ qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32_t k_axis, 
                         void* packed_dev, size_t packed_bytes, qp_packed_info* info,
                         hipStream_t stream);
 
+/*
+ * qrepack_weights -- refill an existing packed blob in place with new weights
+ * of the same shape and format ([TRACT] PackedFormat::new_packed_buffer /
+ * repack_tensor_view: an operand that changes between calls but keeps its
+ * shape reuses its packed buffer instead of reallocating one).
+ *   w, w_dev, k_axis, n_axis  as for qpack_weights.
+ *   packed_dev   the blob `info` describes (at least info->total_bytes,
+ *                256-byte aligned); its old contents are overwritten.
+ *   info         in: the description of that blob (from qpack_weights or
+ *                qp_packed_info_from_header); out: the refilled blob's
+ *                description (zero points and scale extremes may change).
+ * Fails with QP_EINVAL, leaving buffer and `info` untouched, unless the new
+ * weights give the same format, scheme, N, K, group and region layout as
+ * `info`.  Same synchronization as qpack_weights.  The caller must not use
+ * the blob on another stream while it is being refilled.
+ */
+qp_status qrepack_weights(const qp_qtensor* w, const void* w_dev, int32_t k_axis, int32_t n_axis,
+                          void* packed_dev, qp_packed_info* info, hipStream_t stream);
+
 /* Parse a blob header copied to host memory (256 bytes) into `info`. */
 qp_status qp_packed_info_from_header(const void* header_host, qp_packed_info* info);
 

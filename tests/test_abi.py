@@ -286,3 +286,21 @@ def test_conv_routes_and_workspace(qp):
     assert st == qp.QP_OK and b >= 128 * 64
     assert ws(16, 3, (1, 1, 1, 1), (0, 1))[0] == qp.QP_EINVAL
     assert ws(16, 3, (0, 0, 0, 0), (4, 4))[0] == qp.QP_EINVAL       # span 9 > 8
+
+
+def test_repack_checks_the_buffer_before_any_launch(qp):
+    """qrepack_weights refuses weights whose blob geometry differs from the
+    buffer's description (host-side check; nothing is launched)."""
+    L = qp.lib()
+    i8 = _info8(qp)                                  # int8, N=70, K=129
+    for N, K in [(70, 130), (71, 129)]:
+        d = _w8_desc(qp, N, K, scheme=qp.QP_PER_CHANNEL)
+        _expect(qp, L.qrepack_weights(C.byref(d), C.c_void_p(FAKE), 1, 0, C.c_void_p(FAKE),
+                                      C.byref(i8), None), qp.QP_EINVAL,
+                "qrepack_weights: the buffer holds")
+    d4 = qp.qtensor(qp.QP_S4, [70, 129], [129, 1], scheme=qp.QP_BLOCKWISE, group_size=32)
+    _expect(qp, L.qrepack_weights(C.byref(d4), C.c_void_p(FAKE), 1, 0, C.c_void_p(FAKE),
+                                  C.byref(i8), None), qp.QP_EINVAL, "format 1")
+    _expect(qp, L.qrepack_weights(C.byref(d4), C.c_void_p(FAKE), 1, 0, C.c_void_p(FAKE),
+                                  None, None), qp.QP_EINVAL, "null argument")
+    assert i8.N == 70 and i8.K == 129 and i8.format == 1   # untouched
