@@ -194,7 +194,8 @@ def main():
                    "M": M, "N": N, "K": K, "out": "int8", "zp_a": 0, "scale_a": 0.01,
                    "scale_out": 1.0},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     # 10^12 dense int8 operations (2 per multiply-add) per second
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
                      "traffic": None, "kernel_ms": round(kern_ms, 4),
                      "traffic_detail": None,
                      "algorithmic": "2*M*N*K = %.4e int8 ops per launch" % ops},
