@@ -279,14 +279,27 @@ def main():
             i = idx[0] = (idx[0] + 1) % copies
             qp.qgemm_a8w4_prequant_f32(q, sa, za, blobs[i], info4, bg, -6.0, 6.0, out=Yg)
         ms_pre = graph_time(gemv_pre_cold, copies)
+        # context for the latency floor: a device-to-device copy of the same
+        # blob bytes (read + write), in the same graph-replay harness and
+        # weight rotation
+        cdst = torch.empty_like(blob4)
+
+        def copy_cold():
+            i = idx[0] = (idx[0] + 1) % copies
+            cdst.copy_(blobs[i])
+        ms_copy = graph_time(copy_cold, copies)
         gbs = nbytes_alg / ms_cold / 1e6
         workloads["a8w4_gemv_1x4096x4096"] = {
             "quantize_plus_gemv_cold_us": round(ms_cold * 1e3, 3),
             "GBps_cold": round(gbs, 1), "frac_hbm_peak_cold": round(gbs / PEAK_HBM_GBS, 4),
             "gemv_only_cold_us": round(ms_pre * 1e3, 3),
             "warm_cache_resident_us": round(ms_warm * 1e3, 3),
+            "blob_copy_cold_us": round(ms_copy * 1e3, 3),
             "algorithmic_bytes": nbytes_alg, "weight_copies_rotated": copies,
-            "note": "per-launch average, HIP graph replay of back-to-back launches (events)"}
+            "note": "per-launch average, HIP graph replay of back-to-back launches (events); "
+                    "blob_copy_cold_us: torch copy of the same %d-byte blob (read and write) "
+                    "in the same harness" % blob4.numel()}
+        del cdst
         del blobs
 
         # the same GEMV with the group scales stored as bf16 (blob format 3)
@@ -530,7 +543,7 @@ def main():
     # ------------------------------------------------------------ CPU baseline
     if not a.no_cpu_baseline:
         import oracle
-        rows = int(os.environ.get("QP_CPU_SAMPLE_ROWS", "256"))
+        rows = int(os.environ.get("QP_CPU_SAMPLE_ROWS", "384"))
         Ah, Wh = g["A"], g["W"]
         t0 = time.perf_counter()
         acc = oracle.gemm_affine(Ah[:rows], 0, Wh, 0, None, b_is_nk=True)
