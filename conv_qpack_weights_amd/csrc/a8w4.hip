@@ -309,7 +309,10 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 // p ^ ((r >> 1) & 7) so that the 16-byte fragment reads are conflict-free.
 // With kPerm the activations were written permuted inside each 128-K block
 // (piece (t, c) at 32c + 8t) and a lane's four operands are 32 contiguous
-// bytes; otherwise they are four 8-byte pieces.  One barrier per block: past
+// bytes; otherwise they are four 8-byte pieces.  When a workgroup is one
+// row and one channel group (its waves split K), each wave fills and reads
+// only its own rows of a stage and the loop has no barrier.  Otherwise one
+// barrier per block: past
 // it every wave has left the previous block (its ring stage may be
 // refilled) and this block's rows have landed.  Weights and scales of the
 // next P blocks are in registers in flight; a block's MFMAs are issued
@@ -340,6 +343,11 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   constexpr int ND = SLOTS / 256;           // direct loads per thread per stage
   constexpr int STAGE = SLOTS * 16;         // bytes per stage
   static_assert(SLOTS % 256 == 0, "a stage must split evenly over the workgroup");
+  // Each wave its own K range (one row and one channel group): a wave loads
+  // and reads only its own rows of a stage, so the waves need no barrier in
+  // the K loop and run decoupled (a late weight block stalls only its wave).
+  constexpr bool kPrivA = RW * CW == 1;
+  static_assert(!kPrivA || MT * 8 == 64 * ND, "a wave's rows of a stage: ND loads per lane");
   __shared__ __attribute__((aligned(16))) int8_t ring[R * STAGE];
   __shared__ float red[KS > 1 ? (KS - 1) * RW * CW : 1][FM][FN][4][64];
   const int tid = threadIdx.x;
@@ -399,9 +407,9 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   int a_rng[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
-    const int s = tid + 256 * i;
+    const int s = kPrivA ? wave * (MT * 8) + 64 * i + lane : tid + 256 * i;
     const int r = (s >> 3) % MT;
-    a_rng[i] = (32 * i + 8 * wave) / MT;  // == (s >> 3) / MT: a wave's 8 rows share it
+    a_rng[i] = kPrivA ? wave : (32 * i + 8 * wave) / MT;  // == (s >> 3) / MT
     const int p = (s & 7) ^ ((r >> 1) & 7);
     int64_t m = mw + r;
     m = m < M ? m : M - 1;
@@ -412,7 +420,8 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int64_t b = range_block(a_rng[i], j);
-      dma16_to_lds(a_base, (lds_void_t*)(st + (256 * i + 64 * wave) * 16), a_voff[i],
+      const int s0 = kPrivA ? wave * (MT * 8) + 64 * i : 256 * i + 64 * wave;  // lane 0's slot
+      dma16_to_lds(a_base, (lds_void_t*)(st + s0 * 16), a_voff[i],
                    (uint32_t)(b * 128));
     }
   };
@@ -626,7 +635,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       // (past the last step the body still runs, with zero scales, so that
       // every iteration issues the same loads)
       wait_vmcnt<A_WAIT>();
-      asm volatile("s_barrier" ::: "memory");
+      if constexpr (!kPrivA) asm volatile("s_barrier" ::: "memory");
       issue_stage(j + R - 1);
       step(u, j);
       __builtin_amdgcn_sched_barrier(0);
