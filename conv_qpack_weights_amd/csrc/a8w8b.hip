@@ -69,6 +69,10 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
   constexpr int STAGE = SLOTS * 16;
   constexpr int NSC = 128 / BS;        // block scales per step
   static_assert(SLOTS % 256 == 0, "a stage must split evenly over the workgroup");
+  // One channel fragment split over the four waves' K ranges: each wave
+  // loads and reads only its own rows of a stage, no barrier in the loop.
+  constexpr bool kPrivA = CW == 1;
+  static_assert(!kPrivA || MT * 8 == 64 * ND, "a wave's rows of a stage: ND loads per lane");
   __shared__ __attribute__((aligned(16))) int8_t ring[R * STAGE];
   __shared__ float red[KS > 1 ? (KS - 1) * CW : 1][FM][4][64];
   const int tid = threadIdx.x;
@@ -102,9 +106,9 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
   int a_rng[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
-    const int s = tid + 256 * i;
+    const int s = kPrivA ? wave * (MT * 8) + 64 * i + lane : tid + 256 * i;
     const int r = (s >> 3) % MT;
-    a_rng[i] = (32 * i + 8 * wave) / MT;
+    a_rng[i] = kPrivA ? wave : (32 * i + 8 * wave) / MT;
     const int p = (s & 7) ^ ((r >> 1) & 7);
     int64_t m = mw + r;
     m = m < M ? m : M - 1;
@@ -115,7 +119,8 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int64_t b = range_step(a_rng[i], j);
-      dma16_to_lds(a_base, (lds_void_t*)(st + (256 * i + 64 * wave) * 16), a_voff[i],
+      const int s0 = kPrivA ? wave * (MT * 8) + 64 * i : 256 * i + 64 * wave;  // lane 0's slot
+      dma16_to_lds(a_base, (lds_void_t*)(st + s0 * 16), a_voff[i],
                    (uint32_t)(b * 128));
     }
   };
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
     for (int u = 0; u < P; ++u) {
       const int64_t j = j0 + u;
       wait_vmcnt<A_WAIT>();
-      asm volatile("s_barrier" ::: "memory");
+      if constexpr (!kPrivA) asm volatile("s_barrier" ::: "memory");
       issue_stage(j + R - 1);
       step(u, j);
       __builtin_amdgcn_sched_barrier(0);
