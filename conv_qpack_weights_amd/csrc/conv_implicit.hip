@@ -19,11 +19,13 @@
 // one 16-byte load from X, or the zero-point pattern when the tap falls
 // outside the image, or zeros past the real K (the packed weights are zero
 // there too).  The weight piece is read from the int8 blob's 32x32 sub-tiles
-// exactly as in the GEMM.  No LDS is used in the main loop: a wave owns its
-// rows, loads its own operands, and keeps P K-steps of loads in flight in
-// registers; every step runs the same branch-free body (the loads past the
-// end read clamped, in-bounds addresses and are zeroed), so one constant
-// wait count covers all of them.  The epilogue is the GEMM's: zero-point
+// exactly as in the GEMM.  The operands do not pass through LDS: a wave owns
+// its rows, loads its own operands, and keeps P K-steps of loads in flight
+// in registers; every step runs the same branch-free body (the loads past
+// the end read clamped, in-bounds addresses and are zeroed), so one constant
+// wait count covers all of them.  (LDS holds only per-column constants, the
+// channel-blocked variant's scale columns, and the partial sums of the
+// K-split configuration.)  The epilogue is the GEMM's: zero-point
 // corrections, bias and the Q31 requantization (or the raw int32), with the
 // activation row sums, needed when the weights have zero points, summed
 // from the same operand pieces.
