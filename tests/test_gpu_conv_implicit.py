@@ -77,6 +77,10 @@ def test_conv3x3_workload_implicit(qp, orc):
     dict(NB=2, H=8, W=8, C=64, OC=64, KH=5, KW=5, stride=(1, 1), pad=(2, 2, 2, 2), dil=(1, 1)),
     dict(NB=1, H=7, W=7, C=80, OC=96, KH=7, KW=7, stride=(1, 1), pad=(3, 3, 3, 3), dil=(1, 1)),
     dict(NB=1, H=5, W=6, C=16, OC=5, KH=1, KW=1, stride=(2, 2), pad=(1, 0, 1, 0), dil=(1, 1)),
+    # K = 32832, just under the int32 bound K*65025 < 2^31 (513 K-steps);
+    # and pads and dilations much larger than the image
+    dict(NB=1, H=3, W=4, C=3648, OC=16, KH=3, KW=3, stride=(1, 1), pad=(1, 1, 1, 1), dil=(1, 1)),
+    dict(NB=1, H=4, W=3, C=16, OC=8, KH=2, KW=2, stride=(1, 1), pad=(40, 30, 0, 0), dil=(20, 15)),
     # 1x1 fastway (the GEMM on x itself), K a multiple of 64 and not
     dict(NB=2, H=7, W=9, C=64, OC=40, KH=1, KW=1, stride=(1, 1), pad=(0, 0, 0, 0), dil=(1, 1)),
     dict(NB=1, H=6, W=5, C=24, OC=17, KH=1, KW=1, stride=(1, 1), pad=(0, 0, 0, 0), dil=(2, 3)),
