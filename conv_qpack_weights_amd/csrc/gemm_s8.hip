@@ -27,6 +27,7 @@
 //   sum (a-zA)(b-zB) = sum ab - zB*rowsum(a) - zA*colsum(b) + K*zA*zB,
 // evaluated in wrapping 32-bit arithmetic, which is exact whenever the true
 // result fits INT32 (checked on the host with the K*65025+|bias| bound).
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -91,12 +92,17 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
   const size_t lds = (size_t)SA * BM * BK;
   auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32>;
-  static bool lds_attr_set = false;  // once per instantiation; repeating it is harmless
-  if (!lds_attr_set) {
+  // The LDS limit is raised once per instantiation and device (threads may
+  // race to set it; repeating it is harmless).
+  static std::atomic<uint64_t> lds_attr_devices{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) QP_FAIL(QP_EHIP, "qgemm: hipGetDevice failed");
+  const uint64_t bit = dev >= 0 && dev < 64 ? (UINT64_C(1) << dev) : 0;
+  if (bit == 0 || (lds_attr_devices.load(std::memory_order_acquire) & bit) == 0) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       QP_FAIL(QP_EHIP, "qgemm: cannot reserve %zu bytes of LDS", lds);
-    lds_attr_set = true;
+    lds_attr_devices.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, a);
   return check_launch("qgemm_s8s8 kernel");
