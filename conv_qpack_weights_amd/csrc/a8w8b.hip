@@ -50,7 +50,7 @@ __device__ __forceinline__ float finish_w8(float S, float sa, int32_t za, float 
   return y;
 }
 
-template <int FM, int CW, int KS, int BS>
+template <int FM, int CW, int KS, int BS, int P>
 __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restrict__ qa,
                                                          int64_t lda,
                                                          const float* __restrict__ sa_g,
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
                                                          float* __restrict__ Y, int64_t ldy) {
   static_assert(CW * KS == 4, "four waves");
   static_assert(BS == 64 || BS == 128, "block of 64 or 128 K");
-  constexpr int P = 3;                 // weight steps in flight
+  // P: weight steps in flight
   constexpr int R = 4;                 // activation ring stages
   constexpr int MT = 16 * FM;          // rows per workgroup
   constexpr int SLOTS = KS * MT * 8;   // 16-byte pieces per stage
@@ -258,7 +258,7 @@ qp_status validate_w8b(const qp_packed_info* b, int64_t K) {
   return QP_OK;
 }
 
-template <int FM, int CW, int KS>
+template <int FM, int CW, int KS, int P = 3>
 qp_status launch_cfg(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za, int64_t M,
                      const W8B& w, int64_t bs, const float* bias, float lo, float hi, float* Y,
                      int64_t ldy, hipStream_t stream) {
@@ -267,10 +267,10 @@ qp_status launch_cfg(const int8_t* qa, int64_t lda, const float* sa, const int32
   QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w8 blockwise: M too large");
   const dim3 grid(bx, (unsigned)by);
   if (bs == 64)
-    hipLaunchKernelGGL((a8w8b_gemm_kernel<FM, CW, KS, 64>), grid, dim3(256), 0, stream, qa, lda,
+    hipLaunchKernelGGL((a8w8b_gemm_kernel<FM, CW, KS, 64, P>), grid, dim3(256), 0, stream, qa, lda,
                        sa, za, M, w, bias, lo, hi, Y, ldy);
   else
-    hipLaunchKernelGGL((a8w8b_gemm_kernel<FM, CW, KS, 128>), grid, dim3(256), 0, stream, qa, lda,
+    hipLaunchKernelGGL((a8w8b_gemm_kernel<FM, CW, KS, 128, P>), grid, dim3(256), 0, stream, qa, lda,
                        sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w8 blockwise gemm");
 }
@@ -280,7 +280,14 @@ qp_status launch_a8w8b(const int8_t* qa, int64_t lda, const float* sa, const int
                        float* Y, int64_t ldy, hipStream_t stream) {
   // small M: four K ranges per 16-channel fragment; otherwise four channel
   // fragments share the staged rows
-  if (M <= 16) return launch_cfg<1, 1, 4>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
+  if (M <= 16) {
+    // At most one wave per SIMD (up to 256 16-channel fragments): nothing
+    // else hides the weights' latency, so each wave keeps eight steps in
+    // flight; larger grids keep three (more resident waves instead).
+    if (ceil_div(w.N, 16) <= 256)
+      return launch_cfg<1, 1, 4, 8>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
+    return launch_cfg<1, 1, 4>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
+  }
   // (32-row workgroups up to M = 128: more of them, measured faster there)
   if (M <= 128) return launch_cfg<2, 4, 1>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
   return launch_cfg<4, 4, 1>(qa, lda, sa, za, M, w, bs, bias, lo, hi, Y, ldy, stream);
