@@ -233,6 +233,8 @@ def test_a8w4_blockq_gemm_workload(qp, orc, M):
 
 @pytest.mark.parametrize("M,N,K,prequant,sdt", [(1, 70, 96, False, "f32"),
                                                 (1, 33, 1000, True, "bf16"),
+                                                (1, 40, 1000, False, "bf16"),
+                                                (1, 16, 53248, False, "f32"),
                                                 (2, 130, 200, False, "f32"),
                                                 (5, 77, 1000, True, "f32"),
                                                 (17, 100, 256, False, "bf16"),
