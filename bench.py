@@ -572,6 +572,22 @@ def main():
             "kind": "oracle",
             "sample": "%d of 8192 rows of the 8192^3 GEMM (O1 integer GEMM + O3 requant, "
                       "scalar C, one thread), %.1f s" % (rows, cpu_s)}
+        # the same oracle calls on the host's threads, the rows split evenly
+        # (the C library runs with the interpreter lock released)
+        from concurrent.futures import ThreadPoolExecutor
+        T = max(1, min(os.cpu_count() or 1, 16))
+        cuts = [rows * i // T for i in range(T + 1)]
+
+        def part(i):
+            acc_i = oracle.gemm_affine(Ah[cuts[i]:cuts[i + 1]], 0, Wh, 0, None, b_is_nk=True)
+            oracle.requant_matrix(acc_i, g["sA"], g["s_w"], g["s_out"], g["zp_out"], False)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=T) as ex:
+            list(ex.map(part, range(T)))
+        cpu_t = time.perf_counter() - t0
+        out["cpu_baseline"]["all_threads"] = {
+            "value": round(2.0 * rows * N * K / cpu_t / 1e12, 6), "unit": "TOPS", "cores": T,
+            "seconds": round(cpu_t, 2)}
     print(json.dumps(out))
 
 
