@@ -377,6 +377,8 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     QP_REQUIRE(w->zero_point >= -128 && w->zero_point <= 127, QP_EINVAL,
                "weight zero point %d outside int8", w->zero_point);
     h.has_zp = has_zp;
+    h.scale_min = smin;
+    h.scale_max = smax;
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
     if ((st = check_launch("qpack_weights header"))) return st;
     hipLaunchKernelGGL(pack_s8_kernel<false>, dim3((unsigned)g.Npad), dim3(256), 0, stream, src,

@@ -47,7 +47,11 @@ struct alignas(16) BlobHeader {
   int64_t data_off, data_bytes, scale_off, sum_off, zp_off, total_bytes;
   int32_t has_zp;
   int32_t invalid_values;
-  uint8_t zero[256 - 112];
+  // int8 (format 1): extremes of the per-channel weight scales, so that a
+  // blob restored from its bytes validates requantization multipliers and
+  // picks the epilogue exactly as the freshly packed one does.  0 elsewhere.
+  float scale_min, scale_max;
+  uint8_t zero[256 - 120];
 };
 static_assert(sizeof(BlobHeader) == 256, "header is 256 bytes");
 

@@ -1,4 +1,5 @@
 // status.cpp -- error strings, version, blob geometry.
+#include <cmath>
 #include <cstdarg>
 #include <cstring>
 
@@ -102,8 +103,19 @@ qp_status qp_packed_info_from_header(const void* header_host, qp_packed_info* in
              QP_EINVAL, "blob header is inconsistent with its own geometry");
   QP_REQUIRE(h.invalid_values == 0, QP_EINVAL, "blob was packed from out-of-range int4 values");
   g.has_zero_points = h.has_zp;
-  g.scale_min = 0.0f;
-  g.scale_max = 0.0f;
+  if (g.format == 1) {
+    // The scale range drives the multiplier validation of the GEMM entry
+    // points; a blob without a valid one is refused rather than run unchecked.
+    QP_REQUIRE(std::isfinite(h.scale_min) && std::isfinite(h.scale_max) && h.scale_min > 0.0f &&
+                   h.scale_min <= h.scale_max,
+               QP_EINVAL, "blob header holds no valid weight-scale range (%g, %g)",
+               (double)h.scale_min, (double)h.scale_max);
+    g.scale_min = h.scale_min;
+    g.scale_max = h.scale_max;
+  } else {
+    g.scale_min = 0.0f;
+    g.scale_max = 0.0f;
+  }
   *info = g;
   return QP_OK;
 }

@@ -694,7 +694,9 @@ int orc_a8w4_blockwise_asym(int64_t M, int64_t N, int64_t K, int64_t group, cons
  *   u32 magic 0x4B505149, u32 version 1, u32 format (1 int8, 2 int4),
  *   u32 scheme (0 per-tensor, 1 per-channel, 2 blockwise),
  *   i64 N, K, Npad, Kpad, group, data_off, data_bytes, scale_off, sum_off,
- *   zp_off, total_bytes; i32 has_zero_points; zero to byte 256.
+ *   zp_off, total_bytes; i32 has_zero_points; i32 invalid-int4 flag (0);
+ *   int8 format: f32 smallest and f32 largest weight scale of the real
+ *   channels (bytes 112 and 116; 0 for the other formats); zero to byte 256.
  * int8 format:  Npad = roundup(N,64), Kpad = roundup(K,64);
  *   data: 32x32 sub-tiles, [Npad/32][Kpad/32][32 rows][32 bytes] -- W[n,k]
  *   at ((n/32)*(Kpad/32) + k/32)*1024 + (n%32)*32 + k%32, zero beyond N, K;
@@ -763,6 +765,13 @@ int orc_pack_s8_ref(int64_t N, int64_t K, const int8_t* Wt, int64_t w_sn, int64_
   }
   orc_header(blob, 1u, per_channel ? 1u : 0u, N, K, Npad, Kpad, 0, data_bytes, scale_off,
              sum_off, zp_off, total, has_zp);
+  float smin = scales[0], smax = scales[0];
+  for (int64_t n = 0; per_channel && n < N; ++n) {
+    if (scales[n] < smin) smin = scales[n];
+    if (scales[n] > smax) smax = scales[n];
+  }
+  memcpy(blob + 112, &smin, 4);
+  memcpy(blob + 116, &smax, 4);
   for (int64_t n = 0; n < N; ++n) {
     int64_t cs = 0;
     for (int64_t k = 0; k < K; ++k) {

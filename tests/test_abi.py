@@ -67,6 +67,13 @@ def test_header_parser_reads_the_reference_blob(qp, orc):
     info = qp.qp_packed_info_from_header(blob[:256].tobytes())
     assert (info.format, info.N, info.K, info.Npad, info.Kpad) == (1, 70, 129, 128, 192)
     assert info.total_bytes == blob.size and info.has_zero_points == 1
+    # the weight-scale range travels in the header, so a restored blob
+    # validates requantization multipliers like a freshly packed one
+    assert (info.scale_min, info.scale_max) == (np.float32(0.01), np.float32(0.01))
+    norange = bytearray(blob[:256].tobytes())
+    norange[112:120] = bytes(8)
+    with pytest.raises(qp.QPackError):
+        qp.qp_packed_info_from_header(bytes(norange))
     W4 = rng.integers(-8, 8, (5, 100)).astype(np.int8)
     blob4 = orc.pack_s4_ref(W4, np.ones((5, 4), np.float32))
     info4 = qp.qp_packed_info_from_header(blob4[:256].tobytes())

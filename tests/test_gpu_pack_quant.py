@@ -103,7 +103,7 @@ def test_blob_header_round_trip(qp):
     blob, info = qp.pack_s8(_dev(W), scales=_dev(np.full(70, 0.01, np.float32)))
     back = qp.qp_packed_info_from_header(_host(blob)[:256].tobytes())
     for f in ["format", "N", "K", "Npad", "Kpad", "data_off", "scale_off", "sum_off", "zp_off",
-              "total_bytes"]:
+              "total_bytes", "has_zero_points", "scale_min", "scale_max"]:
         assert getattr(back, f) == getattr(info, f), f
 
 
@@ -112,7 +112,8 @@ def _quant_rows_cases():
     rng = np.random.default_rng(9)
     d3 = synth.a8w4_gemv()
     d4 = synth.a8w4_gemm(16)
-    rows = [d3["X"], d4["X"],
+    d5 = synth.a8w4_gemm(128)
+    rows = [d3["X"], d4["X"], d5["X"],
             rng.standard_normal((3, 777)).astype(np.float32),
             np.zeros((2, 64), np.float32),
             np.abs(rng.standard_normal((2, 100))).astype(np.float32),
@@ -122,7 +123,7 @@ def _quant_rows_cases():
     return rows
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(9))
 def test_quantize_rows_bit_exact(qp, orc, case):
     X = _quant_rows_cases()[case]
     q, s, z = qp.qquantize_rows_s8(_dev(X))

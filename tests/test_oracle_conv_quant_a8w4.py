@@ -328,7 +328,10 @@ def _hdr(blob):
     d = dict(zip(keys, (int(v) for v in i64)))
     d.update(magic=int(u32[0]), version=int(u32[1]), format=int(u32[2]), scheme=int(u32[3]),
              has_zp=int(h[104:108].view(np.int32)[0]))
-    assert not h[108:].any()
+    d["scale_min"], d["scale_max"] = (float(v) for v in h[112:120].view(np.float32))
+    assert not h[108:112].any() and not h[120:].any()
+    if d["format"] != 1:
+        assert d["scale_min"] == d["scale_max"] == 0.0
     return d
 
 
@@ -356,6 +359,7 @@ def test_o7_s8_blob_decodes_back(orc, N, K):
     assert np.array_equal(cs[:N], W.astype(np.int64).sum(1)) and not cs[N:].any()
     zz = blob[h["zp_off"]:h["zp_off"] + 4 * h["Npad"]].view(np.int32)
     assert np.array_equal(zz[:N], zp) and h["has_zp"] == int(zp.any())
+    assert (h["scale_min"], h["scale_max"]) == (float(sc.min()), float(sc.max()))
     # same blob from a [K, N] source view
     assert np.array_equal(orc.pack_s8_ref(np.ascontiguousarray(W.T).T, sc, zp), blob)
 
