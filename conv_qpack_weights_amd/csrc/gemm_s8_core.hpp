@@ -54,10 +54,13 @@ struct GemmArgs {
 // 2^31 -> 2^30 with e+1; shift = 31 - e.
 // The kernel's rounding step needs 1 <= shift <= 62, so the two edge cases
 // are mapped to equivalent pairs: shift >= 63 (|acc*M| < 1/2 for every
-// acc, result 0) becomes (m0 = 0, shift = 1); shift == 0 (M >= 2^30, every
-// non-zero acc saturates, acc = 0 gives 0) becomes (2^31-1, 1), which
-// saturates the same way.  A column whose multiplier is not positive and
-// finite (the zero-scale padding columns) gets (0, 1).
+// acc, result 0) becomes (m0 = 0, shift = 32), which both rounding forms
+// (the 64-bit one and the one in 32-bit pieces, used when every shift is
+// >= 32) turn into 0; shift == 0 (M >= 2^30, every non-zero acc saturates,
+// acc = 0 gives 0) becomes (2^31-1, 1), which saturates the same way and
+// only occurs in launches with the 64-bit rounding.  A column whose
+// multiplier is not positive and finite (the zero-scale padding columns)
+// gets (0, 1).
 __device__ __forceinline__ void derive_mult(float sA, float sB, float sOut, int32_t* m0,
                                             int32_t* sh) {
 #pragma clang fp contract(off)
@@ -80,7 +83,7 @@ __device__ __forceinline__ void derive_mult(float sA, float sB, float sOut, int3
     s = 1;
     q = 0x7fffffff;
   } else if (s >= 63) {
-    s = 1;
+    s = 32;
     q = 0;
   }
   *m0 = (int32_t)q;
