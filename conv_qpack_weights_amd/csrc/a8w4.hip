@@ -317,8 +317,12 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 // refilled) and this block's rows have landed.  Weights and scales of the
 // next P blocks are in registers in flight; a block's MFMAs are issued
 // before their results are rescaled, two group slots at a time, into two
-// f32 chains (even and odd slots) per output.  K-range partial sums are
-// added in wave order through LDS.
+// f32 chains (even and odd slots) per output.  Asymmetric weights make each
+// group's term (scale * dot + offset * activation sum) large next to the
+// output, so there the chains hold one block's four groups only and are
+// added into an f64 sum after every block: an f32 sum over all of K would
+// round by more than the output tolerance.  K-range partial sums are added
+// in wave order through LDS.
 // kBQ (activations quantized per block of 32: sa, za are [M][ldsz]): the
 // MFMA is issued the other way round, (weights, activations), so a lane
 // holds channels 4*(l/16)+i of row l%16 and needs one row's group
@@ -428,6 +432,13 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 
   // ---- accumulators ----
   float acc[2][FM][FN][4];
+  double accd[kAsym ? FM : 1][kAsym ? FN : 1][4];
+#pragma unroll
+  for (int f = 0; f < (kAsym ? FM : 1); ++f)
+#pragma unroll
+    for (int q = 0; q < (kAsym ? FN : 1); ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accd[f][q][i] = 0.0;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -609,6 +620,18 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
           }
         }
     }
+    if constexpr (kAsym) {  // the block's sum into the f64 one
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int q = 0; q < FN; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            accd[f][q][i] = accd[f][q][i] + (double)(acc[0][f][q][i] + acc[1][f][q][i]);
+            acc[0][f][q][i] = 0.0f;
+            acc[1][f][q][i] = 0.0f;
+          }
+    }
   };
 
   // ---- prologue: stages 0..R-2 and weights of blocks 0..P-1, all drained ----
@@ -649,7 +672,12 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
     for (int q = 0; q < FN; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[f][q][i] = acc[0][f][q][i] + acc[1][f][q][i];
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (kAsym)
+          out[f][q][i] = (float)accd[f][q][i];
+        else
+          out[f][q][i] = acc[0][f][q][i] + acc[1][f][q][i];
+      }
   if constexpr (KS > 1) {
     if (ks > 0) {
 #pragma unroll

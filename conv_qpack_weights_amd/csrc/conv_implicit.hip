@@ -80,8 +80,10 @@ __device__ __forceinline__ int div_small(int k, int d, float rcp) {
 // kBlk: channel-blocked weights with f32 output.  Each K-step's products are
 // kept apart: e = MFMA(weights, the input zero point), then
 // d = MFMA(weights, pieces) accumulated onto -e, so d is the step's exact
-// sum of (x - zx)*w, which is scaled by its block's weight scale into an
-// f32 sum; the output is sx * that + bias, clamped.  The workgroup's block
+// sum of (x - zx)*w.  Its block's f32 weight scale times d (|d| < 2^22) is
+// exact in f64, and the running sum over the blocks is kept in f64: with
+// hundreds of blocks an f32 running sum would round by more than the output
+// tolerance.  The output is f32(sx * that) + bias, clamped.  The workgroup's block
 // scales ([nblk][BN]) are copied to LDS once when they fit, else each step
 // reads them from memory.
 // KSP == 4 (few output tiles): the four waves share one tile of pixels and
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   constexpr int BN = FN * 16;
   constexpr int LOADS = FM + FN;  // loads per K-step and lane
   static_assert((P - 1) * LOADS < 64, "vmcnt range");
-  constexpr int NRED = FN * FM * 4 + FM;  // a lane's partial sums (and row sums)
+  // a lane's partial sums (f64 ones in two words) and row sums
+  constexpr int NRED = FN * FM * 4 * (kBlk ? 2 : 1) + FM;
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
   __shared__ int32_t red[KSP > 1 ? KSP - 1 : 1][KSP > 1 ? NRED : 1][64];
   extern __shared__ float sw_tile[];  // kBlk with sw_in_lds: [nblk][BN]
@@ -191,13 +194,13 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
 #pragma unroll
     for (int i = 0; i < FN; ++i) br[slot][i] = *reinterpret_cast<const v4i*>(b_src[i] + kc * 2048);
   };
-  float accf[kBlk ? FN : 1][kBlk ? FM : 1][4];
+  double accd[kBlk ? FN : 1][kBlk ? FM : 1][4];
 #pragma unroll
   for (int i = 0; i < (kBlk ? FN : 1); ++i)
 #pragma unroll
     for (int j = 0; j < (kBlk ? FM : 1); ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) accd[i][j][r] = 0.0;
 
   v4i acc[FN][FM];
   int32_t rsum[FM];
@@ -258,14 +261,16 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
         }
         issue(u, kt0 + u + P);
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
+        for (int i = 0; i < FN; ++i) {
+          const double s0 = sc[i].x, s1 = sc[i].y, s2 = sc[i].z, s3 = sc[i].w;
 #pragma unroll
           for (int j = 0; j < FM; ++j) {
-            accf[i][j][0] = __builtin_fmaf(sc[i].x, (float)d[i][j][0], accf[i][j][0]);
-            accf[i][j][1] = __builtin_fmaf(sc[i].y, (float)d[i][j][1], accf[i][j][1]);
-            accf[i][j][2] = __builtin_fmaf(sc[i].z, (float)d[i][j][2], accf[i][j][2]);
-            accf[i][j][3] = __builtin_fmaf(sc[i].w, (float)d[i][j][3], accf[i][j][3]);
+            accd[i][j][0] = __builtin_fma(s0, (double)d[i][j][0], accd[i][j][0]);
+            accd[i][j][1] = __builtin_fma(s1, (double)d[i][j][1], accd[i][j][1]);
+            accd[i][j][2] = __builtin_fma(s2, (double)d[i][j][2], accd[i][j][2]);
+            accd[i][j][3] = __builtin_fma(s3, (double)d[i][j][3], accd[i][j][3]);
           }
+        }
         continue;
       }
 #pragma unroll
@@ -285,11 +290,18 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            red[wave - 1][(i * FM + j) * 4 + r][lane] =
-                kBlk ? __builtin_bit_cast(int32_t, accf[i][j][r]) : acc[i][j][r];
+          for (int r = 0; r < 4; ++r) {
+            const int q = (i * FM + j) * 4 + r;
+            if constexpr (kBlk) {
+              const uint64_t v = __builtin_bit_cast(uint64_t, accd[i][j][r]);
+              red[wave - 1][2 * q][lane] = (int32_t)(uint32_t)v;
+              red[wave - 1][2 * q + 1][lane] = (int32_t)(uint32_t)(v >> 32);
+            } else {
+              red[wave - 1][q][lane] = acc[i][j][r];
+            }
+          }
 #pragma unroll
-      for (int j = 0; j < FM; ++j) red[wave - 1][FN * FM * 4 + j][lane] = rsum[j];
+      for (int j = 0; j < FM; ++j) red[wave - 1][NRED - FM + j][lane] = rsum[j];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -301,12 +313,17 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
         for (int j = 0; j < FM; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int32_t v = red[w][(i * FM + j) * 4 + r][lane];
-            if constexpr (kBlk) accf[i][j][r] = accf[i][j][r] + __builtin_bit_cast(float, v);
-            else acc[i][j][r] = acc[i][j][r] + v;
+            const int q = (i * FM + j) * 4 + r;
+            if constexpr (kBlk) {
+              const uint64_t v = (uint64_t)(uint32_t)red[w][2 * q][lane] |
+                                 ((uint64_t)(uint32_t)red[w][2 * q + 1][lane] << 32);
+              accd[i][j][r] = accd[i][j][r] + __builtin_bit_cast(double, v);
+            } else {
+              acc[i][j][r] = acc[i][j][r] + red[w][q][lane];
+            }
           }
 #pragma unroll
-      for (int j = 0; j < FM; ++j) rsum[j] += red[w][FN * FM * 4 + j][lane];
+      for (int j = 0; j < FM; ++j) rsum[j] += red[w][NRED - FM + j][lane];
     }
   }
   if constexpr (kBlk) {  // y = sx * sum + bias, clamped; lane: channels 4*grp+r of row r16
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (n + r >= g.N) continue;
-          float y = g.sA * accf[i][j][r] + (g.bias_f ? g.bias_f[n + r] : 0.0f);
+          float y = (float)((double)g.sA * accd[i][j][r]) + (g.bias_f ? g.bias_f[n + r] : 0.0f);
           y = y < g.clo ? g.clo : y;
           y = y > g.chi ? g.chi : y;
           row[n + r] = y;

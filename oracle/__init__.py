@@ -1,9 +1,12 @@
 """Python view of the scalar C oracle (``oracle.c``).
 
 Test infrastructure: only the tests, ``__graft_entry__.smoke()`` and the
-benchmark's CPU-baseline leg import this package.  It is marshalling only --
-every step of the reference arithmetic is in ``oracle.c`` -- and it never
-imports the GPU library.
+benchmark's CPU-baseline leg import this package.  It is marshalling for the
+C oracle (``oracle.c``) plus two small numpy definitions that are not in C:
+O9, the dequantized weight values (one IEEE f32 product, plus the group
+offset for asymmetric int4), and ``matmul_f64.py``, a second formulation of
+O1 through an fp64 library matmul for full-size checks.  It never imports
+the GPU library.
 """
 from __future__ import annotations
 
@@ -122,6 +125,22 @@ def _check(rc, what):
 
 def _elem_strides(a):
     return tuple(s // a.itemsize for s in a.strides)
+
+
+def rows_in_threads(fn, X, *args, threads=None, chunk=None, **kw):
+    """``fn(X[r0:r1], *args, **kw)`` over row ranges of ``X`` on host threads,
+    concatenated along the first axis.  Every oracle function used this way
+    treats rows independently, so the result is identical to one call; the
+    C code runs without the interpreter lock, so the ranges run in
+    parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = X.shape[0]
+    threads = threads or min(16, os.cpu_count() or 1)
+    chunk = chunk or max(1, -(-n // (4 * threads)))
+    starts = range(0, n, chunk)
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda r0: fn(X[r0:r0 + chunk], *args, **kw), starts))
+    return np.concatenate(parts, axis=0)
 
 
 # ---------------------------------------------------------------- O1 / O2

@@ -17,3 +17,16 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def large_gemm():
+    """The 8192^3 per-channel workload and its exact int32 accumulators from
+    the fp64-matmul formulation of the oracle (computed once per session;
+    shared by the int8, int32 and f32 full-size checks)."""
+    import synth
+    from oracle.matmul_f64 import gemm_affine_f64
+    d = synth.gemm_large()
+    print("computing the 8192^3 reference accumulators", flush=True)
+    acc = gemm_affine_f64(d["A"], d["zA"], d["W"], 0)
+    return d, acc

@@ -43,7 +43,8 @@ def _case(qp, orc, d, rows=None):
     Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
                                           d["clamp_lo"], d["clamp_hi"]))
     X = d["X"] if rows is None else d["X"][rows]
-    want = orc.a8w4_forward(X, d["W"], d["sw"], d["bias"], d["clamp_lo"], d["clamp_hi"])
+    want = orc.rows_in_threads(orc.a8w4_forward, X, d["W"], d["sw"], d["bias"], d["clamp_lo"],
+                               d["clamp_hi"])
     got = Y if rows is None else Y[rows]
     return _check_close(got, want, "a8w4 f32 output")
 
@@ -54,8 +55,7 @@ def test_a8w4_gemv_workload(qp, orc):
 
 @pytest.mark.parametrize("M", [16, 128])
 def test_a8w4_gemm_workload(qp, orc, M):
-    rows = None if M == 16 else np.r_[0:8, 60:68, 120:128]
-    _case(qp, orc, synth.a8w4_gemm(M), rows)
+    _case(qp, orc, synth.a8w4_gemm(M))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 70, 96), (1, 1, 32), (2, 130, 200), (3, 64, 4096),
@@ -110,7 +110,8 @@ def _case_bf16(qp, orc, d, rows=None, prequant=False):
         Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
                                               d["clamp_lo"], d["clamp_hi"]))
     X = d["X"] if rows is None else d["X"][rows]
-    want = orc.a8w4_forward(X, d["W"], sw16, d["bias"], d["clamp_lo"], d["clamp_hi"])
+    want = orc.rows_in_threads(orc.a8w4_forward, X, d["W"], sw16, d["bias"], d["clamp_lo"],
+                               d["clamp_hi"])
     _check_close(Y if rows is None else Y[rows], want, "a8w4 bf16-scale output")
     return blob, info, sw16
 
@@ -125,8 +126,7 @@ def test_a8w4_bf16_scales_gemv_workload(qp, orc):
 
 @pytest.mark.parametrize("M", [16, 128])
 def test_a8w4_bf16_scales_gemm_workload(qp, orc, M):
-    rows = None if M == 16 else np.r_[0:8, 120:128]
-    _case_bf16(qp, orc, synth.a8w4_gemm(M), rows)
+    _case_bf16(qp, orc, synth.a8w4_gemm(M))
 
 
 @pytest.mark.parametrize("M,N,K,prequant", [(1, 70, 96, False), (3, 64, 4096, True),
@@ -156,8 +156,8 @@ def _case_asym(qp, orc, d, bw, rows=None, prequant=False):
         Y = _host(qp.qgemm_a8w4_blockwise_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
                                               d["clamp_lo"], d["clamp_hi"]))
     X = d["X"] if rows is None else d["X"][rows]
-    want = orc.a8w4_forward_asym(X, d["W"], d["sw"], bw, d["bias"], d["clamp_lo"],
-                                 d["clamp_hi"])
+    want = orc.rows_in_threads(orc.a8w4_forward_asym, X, d["W"], d["sw"], bw, d["bias"],
+                               d["clamp_lo"], d["clamp_hi"])
     _check_close(Y if rows is None else Y[rows], want, "asymmetric a8w4 output")
     return blob, info
 
@@ -175,8 +175,7 @@ def test_a8w4_asym_gemv_workload(qp, orc):
 @pytest.mark.parametrize("M", [16, 128])
 def test_a8w4_asym_gemm_workload(qp, orc, M):
     d = synth.a8w4_gemm(M)
-    rows = None if M == 16 else np.r_[0:8, 120:128]
-    _case_asym(qp, orc, d, _offsets(d, M), rows)
+    _case_asym(qp, orc, d, _offsets(d, M))
 
 
 @pytest.mark.parametrize("M,N,K,prequant", [(1, 70, 96, False), (1, 33, 1000, False),
@@ -217,7 +216,8 @@ def _case_bq(qp, orc, d, rows=None, prequant=False, scale_dtype="f32"):
         Y = _host(qp.qgemm_a8w4_blockq_f32(_dev(d["X"]), blob, info, _dev(d["bias"]),
                                            d["clamp_lo"], d["clamp_hi"]))
     X = d["X"] if rows is None else d["X"][rows]
-    want = orc.a8w4_forward_blockq(X, d["W"], sw, d["bias"], d["clamp_lo"], d["clamp_hi"])
+    want = orc.rows_in_threads(orc.a8w4_forward_blockq, X, d["W"], sw, d["bias"], d["clamp_lo"],
+                               d["clamp_hi"])
     _check_close(Y if rows is None else Y[rows], want, "per-block a8w4 output")
 
 
@@ -227,8 +227,7 @@ def test_a8w4_blockq_gemv_workload(qp, orc):
 
 @pytest.mark.parametrize("M", [16, 128])
 def test_a8w4_blockq_gemm_workload(qp, orc, M):
-    rows = None if M == 16 else np.r_[0:8, 120:128]
-    _case_bq(qp, orc, synth.a8w4_gemm(M), rows)
+    _case_bq(qp, orc, synth.a8w4_gemm(M))
 
 
 @pytest.mark.parametrize("M,N,K,prequant,sdt", [(1, 70, 96, False, "f32"),
