@@ -91,6 +91,8 @@ SIGNATURES = {
                                            _P, C.c_size_t, _P]),
     "qgemm_a8w4_prequant_f32": (C.c_int, [_P, _I64, _I64, _P, _P, _PI, _P, _P, _F, _F, _P, _I64,
                                           _P]),
+    "qgemm_a8w4_blockwise_f32_noalloc": (C.c_int, [_P, _I64, _I64, _I64, _PI, _P, _P, _F, _F, _P,
+                                                   _I64, _P]),
     "qim2col_s8": (C.c_int, [_P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
                              _I32, _I32, _I32, _P, _I64, _P]),
     "qconv2d_s8_im2col_ws_size": (C.c_int, [_QT, _PI, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -381,6 +383,22 @@ def qgemm_a8w4_blockwise_f32(X: torch.Tensor, blob: torch.Tensor, info: PackedIn
                                          _ptr(bias), clamp_lo, clamp_hi, _ptr(out), out.stride(0),
                                          _ptr(ws), ws.numel(), _stream(X.device)),
            "qgemm_a8w4_blockwise_f32")
+    return out
+
+
+def qgemm_a8w4_blockwise_f32_noalloc(X: torch.Tensor, blob: torch.Tensor, info: PackedInfo,
+                                     bias=None, clamp_lo=-float("inf"), clamp_hi=float("inf"),
+                                     out=None):
+    """qgemm_a8w4_blockwise_f32 without a workspace: the library's own
+    per-GPU scratch array holds the quantized rows (at most 4 MiB)."""
+    assert X.dtype == torch.float32 and X.dim() == 2 and X.stride(1) == 1
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, info.N), dtype=torch.float32, device=X.device)
+    _check(_lib.qgemm_a8w4_blockwise_f32_noalloc(_ptr(X), M, K, X.stride(0), C.byref(info),
+                                                 _ptr(blob), _ptr(bias), clamp_lo, clamp_hi,
+                                                 _ptr(out), out.stride(0), _stream(X.device)),
+           "qgemm_a8w4_blockwise_f32_noalloc")
     return out
 
 

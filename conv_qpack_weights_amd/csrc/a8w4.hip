@@ -21,6 +21,7 @@
 // int8 MFMA consume them with no sign fix-up; the factor 16 is removed
 // exactly (a power of two) in the epilogue.  One 16-byte load (chunk c of a
 // block) carries the same 8 K of four consecutive groups.
+#include <atomic>
 #include <cstring>
 #include <type_traits>
 
@@ -888,6 +889,69 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32(const float* X, int64_t M, int64_t
   st = launch_quantize_rows(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, true, stream);
   if (st) return st;
   return launch_gemm(qa, w->Kpad, true, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
+}
+
+// ---- the same product with no workspace argument -------------------------
+// For callers that cannot allocate device memory.  The quantized rows live in
+// a library-owned array in device memory, one per GPU, held until the process
+// ends; every call on a GPU reuses that GPU's copy.  The array's host-side
+// name is only a stand-in for it: its device address (one per GPU) comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is ever handed to a kernel.
+namespace qp {
+namespace {
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::atomic<void*> scratch_dev_ptr[kNoAllocMaxDevices];
+
+qp_status scratch_of_current_device(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess)
+    QP_FAIL(QP_EHIP, "a8w4 (no allocation): hipGetDevice failed");
+  QP_REQUIRE(dev >= 0 && dev < kNoAllocMaxDevices, QP_EUNSUPPORTED,
+             "a8w4 (no allocation): device %d beyond the %d supported", dev, kNoAllocMaxDevices);
+  void* p = scratch_dev_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Threads may race here; each gets the same address.
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      QP_FAIL(QP_EHIP, "a8w4 (no allocation): hipGetSymbolAddress failed: %s",
+              hipGetErrorString(e));
+    scratch_dev_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = static_cast<uint8_t*>(p);
+  return QP_OK;
+}
+}  // namespace
+}  // namespace qp
+
+extern "C" qp_status qgemm_a8w4_blockwise_f32_noalloc(const float* X, int64_t M, int64_t K,
+                                                      int64_t ldx, const qp_packed_info* w,
+                                                      const void* packedW_dev, const float* bias,
+                                                      float clamp_lo, float clamp_hi, float* Y,
+                                                      int64_t ldy, hipStream_t stream) {
+  using namespace qp;
+  clear_error();
+  qp_status st = validate_w4(w, K);
+  if (st) return st;
+  QP_REQUIRE(M >= 0 && ldx >= K && ldy >= w->N, QP_EINVAL, "a8w4: bad M/ldx/ldy");
+  QP_REQUIRE(!(clamp_lo > clamp_hi), QP_EINVAL, "a8w4: clamp_lo > clamp_hi");
+  if (M == 0) return QP_OK;
+  QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
+  size_t need = 0;
+  qgemm_a8w4_blockwise_f32_ws_size(M, w, &need);
+  QP_REQUIRE(need <= kNoAllocScratchBytes, QP_ESIZE,
+             "a8w4 (no allocation): M=%lld rows of Kpad=%lld need %zu bytes of scratch, "
+             "more than the %zu available",
+             (long long)M, (long long)w->Kpad, need, kNoAllocScratchBytes);
+  if (M == 1)  // the fused GEMV keeps the quantized row in LDS: no scratch
+    return qgemm_a8w4_blockwise_f32(X, M, K, ldx, w, packedW_dev, bias, clamp_lo, clamp_hi, Y,
+                                    ldy, nullptr, 0, stream);
+  uint8_t* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  return qgemm_a8w4_blockwise_f32(X, M, K, ldx, w, packedW_dev, bias, clamp_lo, clamp_hi, Y, ldy,
+                                  ws, need, stream);
 }
 
 extern "C" qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_t lda,

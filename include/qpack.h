@@ -369,6 +369,26 @@ qp_status qgemm_a8w4_blockwise_f32(const float* X, int64_t M, int64_t K, int64_t
                                    int64_t ldy, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qgemm_a8w4_blockwise_f32_noalloc -- qgemm_a8w4_blockwise_f32 with no
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as
+ * qgemm_a8w4_blockwise_f32, whose kernels it runs; it calls no allocator.
+ * The quantized activations go to a 4 MiB array in device memory that the
+ * library owns, one per GPU, held until the process ends:
+ * round_up(M*Kpad, 256) + round_up(8*M, 256) must not exceed 4 MiB (else
+ * QP_ESIZE, nothing launched), e.g. M <= 1022 for K = 4096.  Every call on a
+ * GPU shares that GPU's array and leaves its contents behind; calls that
+ * overlap on one GPU (concurrent streams, several host threads) race on it,
+ * so serialize them.  Nothing in it needs clearing: each call rewrites what
+ * it reads.
+ */
+qp_status qgemm_a8w4_blockwise_f32_noalloc(const float* X, int64_t M, int64_t K, int64_t ldx,
+                                           const qp_packed_info* w, const void* packedW_dev,
+                                           const float* bias, float clamp_lo, float clamp_hi,
+                                           float* Y, int64_t ldy, hipStream_t stream);
+
+/*
  * qgemm_a8w4_prequant_f32 -- the same product on activations already
  * quantized by qquantize_rows_s8 (the matmul step alone).
  *   qa       device int8 [M][lda]; lda >= Kpad, 16-byte aligned rows, and
