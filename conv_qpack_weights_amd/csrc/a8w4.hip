@@ -107,37 +107,219 @@ __device__ __forceinline__ float4 load_scale4(const uint8_t* p) {
   }
 }
 
-// ---- GEMV: a workgroup per 16-channel tile, waves split the 128-K blocks ----
+// The four group scales (f32 or bf16) of one channel and 128-K block through
+// a buffer resource bounded by the tile's scale region: offsets past it
+// read as zeros, so blocks past the end of K contribute nothing without a
+// select (which the compiler may turn into a branch around the load, whose
+// join then waits for it).
+template <bool kBf16>
+__device__ __forceinline__ float4 load_scale4_bounded(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (kBf16) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const uint32_t lo = v[0], hi = v[1];
+    return make_float4(__builtin_bit_cast(float, lo << 16),
+                       __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                       __builtin_bit_cast(float, hi << 16),
+                       __builtin_bit_cast(float, hi & 0xFFFF0000u));
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const uint32_t a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+    return make_float4(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1),
+                       __builtin_bit_cast(float, a2), __builtin_bit_cast(float, a3));
+  }
+}
+
+// The dot products of one 128-K block for lane (channel l/4, chunk c = l%4):
+// wq holds the chunk's 8-K piece of four groups, a[t] the activations of
+// group t's piece (bytes k..k+3 in .x, k+4..k+7 in .y), sv / ov the group
+// scales / offsets.  Adds the block's four group terms to `part`.
+template <int kKind>
+__device__ __forceinline__ void gemv_block_terms(const uint4& wq, const uint2 (&a)[4],
+                                                 const float4& sv, const float4& ov,
+                                                 float& part) {
+  const float d0 = (float)word_dot16(wq.x, a[0].x, a[0].y);
+  const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
+  const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
+  const float d3 = (float)word_dot16(wq.w, a[3].x, a[3].y);
+  if constexpr (kKind == 2) {
+    // a group piece's term scale*d + offset*(16 * activation sum) is
+    // formed first, so the running sum takes one addition per piece
+    const float e0 = (float)word_sum16(a[0].x, a[0].y);
+    const float e1 = (float)word_sum16(a[1].x, a[1].y);
+    const float e2 = (float)word_sum16(a[2].x, a[2].y);
+    const float e3 = (float)word_sum16(a[3].x, a[3].y);
+    part = part + __builtin_fmaf(ov.x, e0, sv.x * d0);
+    part = part + __builtin_fmaf(ov.y, e1, sv.y * d1);
+    part = part + __builtin_fmaf(ov.z, e2, sv.z * d2);
+    part = part + __builtin_fmaf(ov.w, e3, sv.w * d3);
+  } else {
+    part = part + sv.x * d0;
+    part = part + sv.y * d1;
+    part = part + sv.z * d2;
+    part = part + sv.w * d3;
+  }
+}
+
+// ---- GEMV with the row's dynamic quantization (M = 1) ---------------------
+// One workgroup per 16-channel tile, two kinds of waves:
+//  * NQ quantizer waves load the f32 row (branch-free, bounded loads) and
+//    quantize it with the steps of qquantize_rows_s8 into LDS, permuted so
+//    that the 32 activation bytes of a chunk are contiguous;
+//  * NWW weight waves issue all their weight and scale loads at once and
+//    only then wait.  Lane l handles channel l/4 of the tile and 16-byte
+//    chunk c = l%4 of each of its blocks (the 8-K piece c of four groups), so
+//    one load instruction reads one tile-block: 1 KiB in one piece.
+// Loads complete in issue order within a wave, so a wave that both waited
+// for the row and streamed weights would either hold its weight loads back
+// until the row arrived or see the row arrive behind its weights; with the
+// two jobs in different waves neither waits for the other.  After the codes
+// are in LDS the weight waves form the exact int32 group dots and the f32
+// scaled sum, reduce over the four lanes of a channel (DPP) and then over
+// the weight waves through LDS in a fixed order.
+template <int NQ, int NWW, int BB, int kKind>
+__global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
+    const float* __restrict__ X, int64_t K, W4 w, const float* __restrict__ bias, float lo,
+    float hi, float* __restrict__ Y) {
+  constexpr int QT = NQ * 64;  // quantizer threads
+  constexpr int QE = 8;        // row values a quantizer thread handles per pass
+  constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
+  constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
+  extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];  // [Kpad] codes
+  __shared__ float red[2 * NQ];
+  __shared__ float part_w[NWW][16];
+  __shared__ float row_param[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile = blockIdx.x;
+  const int64_t nb = w.nblk;
+  const int64_t n_out = tile * 16 + (lane & 15);  // the final step's channel (weight wave 0)
+  float wsum_c = 0.0f, bias_c = 0.0f;
+  if (wave < NQ) {
+    const bool xvec = (((uintptr_t)X) & 15) == 0;
+    const RowFirst xf = quantize_row_first<QT, QE>(X, K, xvec);
+    // one pass of whole vectors (e.g. K = 4096) runs without the loops and
+    // fallbacks of the general case
+    const bool one = xvec && K == (int64_t)QT * QE && w.Kpad == K;
+    float4 first[4];
+    if (one)
+      row_extremes_partial<QT, QE, false, true>(X, K, xvec, red, first, &xf);
+    else
+      row_extremes_partial<QT, QE, false>(X, K, xvec, red, first, &xf);
+    __syncthreads();  // (1) the waves' extremes
+    float s;
+    int32_t z;
+    row_params<QT, false>(red, &s, &z);
+    if (tid == 0) {
+      row_param[0] = s;
+      row_param[1] = __builtin_bit_cast(float, z);
+    }
+    if (one)
+      row_codes<QT, QE, true, false, true>(X, K, w.Kpad, xvec, true, qa_lds, s, z, first);
+    else
+      row_codes<QT, QE, true, false>(X, K, w.Kpad, xvec, true, qa_lds, s, z, first);
+    __syncthreads();  // (2) the codes
+    __syncthreads();  // (3) the partial sums
+  } else {
+    const int ww = wave - NQ;
+    const int ch = lane >> 2, c = lane & 3;
+    const uint8_t* wbase = w.data + tile * nb * 1024 + lane * 16;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(w.scale + tile * nb * 64 * ES), 0, (uint32_t)(nb * 64 * ES),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kAsym ? w.offs + tile * nb * 256 : w.scale), 0,
+        (uint32_t)(kAsym ? nb * 256 : 0), 0x00020000);
+    // batches of BB blocks per wave: block (j*BB + u)*NWW + ww; past the end
+    // the weights are re-read from the last block (clamped) and the scales
+    // read as zeros
+    const int64_t nbatch = (nb + (int64_t)NWW * BB - 1) / ((int64_t)NWW * BB);
+    uint4 wv[BB];
+    float4 sv[BB], ov[BB];
+    int64_t blk[BB];
+    auto load_batch = [&](int64_t j) {
+#pragma unroll
+      for (int u = 0; u < BB; ++u) {
+        const int64_t b = (j * BB + u) * NWW + ww;
+        blk[u] = b < nb ? b : nb - 1;
+        wv[u] = *reinterpret_cast<const uint4*>(wbase + blk[u] * 1024);
+        sv[u] = load_scale4_bounded<kBf16>(srs, (uint32_t)((b * 64 + ch * 4) * ES));
+        if constexpr (kAsym)
+          ov[u] = load_scale4_bounded<false>(ors, (uint32_t)((b * 64 + ch * 4) * 4));
+        else
+          ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    float part = 0.0f;
+    auto compute_batch = [&]() {
+#pragma unroll
+      for (int u = 0; u < BB; ++u) {
+        const int8_t* ab = qa_lds + blk[u] * 128 + c * 32;
+        const uint4 p0 = *reinterpret_cast<const uint4*>(ab);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 16);
+        const uint2 a[4] = {make_uint2(p0.x, p0.y), make_uint2(p0.z, p0.w),
+                            make_uint2(p1.x, p1.y), make_uint2(p1.z, p1.w)};
+        gemv_block_terms<kKind>(wv[u], a, sv[u], ov[u], part);
+      }
+    };
+    load_batch(0);
+    // weight wave 0 also fetches the epilogue operands of the tile's channels
+    // (after its weights: they are needed last)
+    if (ww == 0 && lane < 16) {
+      wsum_c = w.wsum[n_out];
+      bias_c = (bias && n_out < w.N) ? bias[n_out] : 0.0f;
+    }
+    __syncthreads();  // (1)
+    __syncthreads();  // (2): the codes are in LDS
+    compute_batch();
+    for (int64_t j = 1; j < nbatch; ++j) {
+      load_batch(j);
+      compute_batch();
+    }
+    // the four lanes of a channel: quad_perm [1,0,3,2] then [2,3,0,1]
+    float p = part;
+    p = p + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p),
+                                                                  0xB1, 0xF, 0xF, false));
+    p = p + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p),
+                                                                  0x4E, 0xF, 0xF, false));
+    if (c == 0) part_w[ww][ch] = p;
+    __syncthreads();  // (3)
+  }
+  if (wave == NQ && lane < 16) {  // weight wave 0 writes the tile
+    float S = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NWW; ++v) S = S + part_w[v][lane];
+    const float sa = row_param[0];
+    const int32_t za = __builtin_bit_cast(int32_t, row_param[1]);
+    if (n_out < w.N) Y[n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
+  }
+}
+
+// ---- GEMV on quantized rows: a workgroup per 16-channel tile --------------
 // Lane l handles channel l/4 of the tile and 16-byte chunk c = l%4 of each
 // of its wave's blocks (the 8-K piece c of four groups), so one wave load
 // instruction reads one tile-block: 1 KiB in one piece.  Its four group
-// scales are 16 bytes shared by the four lanes of the channel.  All of a
-// wave's weight and scale loads are issued first; while they are in flight
-// the workgroup quantizes the activation row (kFused, M = 1: the same device
-// steps as qquantize_rows_s8) into LDS, permuted so that the 32 activation
-// bytes of a chunk are contiguous; otherwise it reads the quantized rows
-// from memory (row-major).  Partial sums are reduced across the four lanes
-// of a channel with DPP and then across the waves through LDS, in a fixed
-// order.  Rows m > 0 reuse the weights held in registers.
+// scales are 16 bytes shared by the four lanes of the channel.  The
+// quantized rows (M <= 4, row-major) are read from memory.  Partial sums
+// are reduced across the four lanes of a channel with DPP and then across
+// the waves through LDS, in a fixed order.  Rows m > 0 reuse the weights
+// held in registers.
 // kBQ: the activations were quantized per block of 32 (one scale and zero
 // point per row and group, [M][ldsz]); one row.  Each group piece then
 // contributes sa[g]*sw[g] * (dot - za[g] * sum q), exactly in integers up to
 // that product.
-template <int NT, bool kFused, int kKind, bool kBQ = false>
-__global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__ X, int64_t K,
-                                                       const int8_t* __restrict__ qa_g,
+template <int NT, int kKind, bool kBQ = false, int BB = 4>
+__global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const int8_t* __restrict__ qa_g,
                                                        int64_t lda, const float* __restrict__ sa_g,
                                                        const int32_t* __restrict__ za_g,
                                                        int64_t M, W4 w,
                                                        const float* __restrict__ bias, float lo,
                                                        float hi, float* __restrict__ Y,
                                                        int64_t ldy) {
-  static_assert(!kBQ || (!kFused && kKind != 2), "per-block activations: prequantized, symmetric");
+  static_assert(!kBQ || kKind != 2, "per-block activations: symmetric weights");
   constexpr int NW = NT / 64;
-  constexpr int BB = 4;      // blocks a wave holds in registers per batch
-  constexpr int MR = 4;      // rows per call (M = 1 fused, M <= 4 prequantized)
-  extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];
-  __shared__ float red[2 * NW];
+  // BB: blocks a wave holds in registers per batch
+  constexpr int MR = 4;      // rows per call (M <= 4)
   __shared__ float part_w[NW][16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -161,15 +343,9 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
   float part[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) part[m] = 0.0f;
-  float sa = 0.0f;
-  int32_t za = 0;
-  const bool xvec = (((uintptr_t)X) & 15) == 0;
-  RowFirst xfirst;
   float sa_m[MR];
   int32_t za_m[MR];
-  if constexpr (kFused) {
-    xfirst = quantize_row_first<NT, 8>(X, K, xvec);  // before the weights
-  } else if constexpr (!kBQ) {
+  if constexpr (!kBQ) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       sa_m[m] = m < M ? sa_g[m] : 0.0f;
@@ -194,16 +370,12 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
       if constexpr (kAsym) {
         const float4 o4 = load_scale4<false>(obase + blk[u] * 64 * 4);
         ov[u] = b < nb ? o4 : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if constexpr (kBQ) {  // the row's four group parameters of this block
         saq[u] = *reinterpret_cast<const float4*>(sa_g + 4 * blk[u]);
         zaq[u] = *reinterpret_cast<const int4*>(za_g + 4 * blk[u]);
-      }
-    }
-    if constexpr (kFused) {
-      if (j == 0) {  // quantize the row while the first loads are in flight
-        quantize_row_wg<NT, true, 8>(X, K, w.Kpad, xvec, true, qa_lds, red, &sa, &za, &xfirst);
-        __syncthreads();
       }
     }
 #pragma unroll
@@ -212,19 +384,9 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
 #pragma unroll
         for (int u = 0; u < BB; ++u) {
           uint2 a[4];
-          if constexpr (kFused) {
-            const int8_t* ab = qa_lds + blk[u] * 128 + c * 32;
-            const uint4 p0 = *reinterpret_cast<const uint4*>(ab);
-            const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 16);
-            a[0] = make_uint2(p0.x, p0.y);
-            a[1] = make_uint2(p0.z, p0.w);
-            a[2] = make_uint2(p1.x, p1.y);
-            a[3] = make_uint2(p1.z, p1.w);
-          } else {
-            const int8_t* ab = qa_g + m * lda + blk[u] * 128 + c * 8;
+          const int8_t* ab = qa_g + m * lda + blk[u] * 128 + c * 8;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint2*>(ab + 32 * t);
-          }
+          for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const uint2*>(ab + 32 * t);
           const uint4 wq = wv[u];
           if constexpr (kBQ) {
             const int32_t z0 = zaq[u].x, z1 = zaq[u].y, z2 = zaq[u].z, z3 = zaq[u].w;
@@ -236,28 +398,8 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
             part[m] = part[m] + (saq[u].y * sv[u].y) * (float)e1;
             part[m] = part[m] + (saq[u].z * sv[u].z) * (float)e2;
             part[m] = part[m] + (saq[u].w * sv[u].w) * (float)e3;
-            continue;
-          }
-          const float d0 = (float)word_dot16(wq.x, a[0].x, a[0].y);
-          const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
-          const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
-          const float d3 = (float)word_dot16(wq.w, a[3].x, a[3].y);
-          if constexpr (kAsym) {
-            // a group piece's term scale*d + offset*(16 * activation sum) is
-            // formed first, so the running sum takes one addition per piece
-            const float e0 = (float)word_sum16(a[0].x, a[0].y);
-            const float e1 = (float)word_sum16(a[1].x, a[1].y);
-            const float e2 = (float)word_sum16(a[2].x, a[2].y);
-            const float e3 = (float)word_sum16(a[3].x, a[3].y);
-            part[m] = part[m] + __builtin_fmaf(ov[u].x, e0, sv[u].x * d0);
-            part[m] = part[m] + __builtin_fmaf(ov[u].y, e1, sv[u].y * d1);
-            part[m] = part[m] + __builtin_fmaf(ov[u].z, e2, sv[u].z * d2);
-            part[m] = part[m] + __builtin_fmaf(ov[u].w, e3, sv[u].w * d3);
           } else {
-            part[m] = part[m] + sv[u].x * d0;
-            part[m] = part[m] + sv[u].y * d1;
-            part[m] = part[m] + sv[u].z * d2;
-            part[m] = part[m] + sv[u].w * d3;
+            gemv_block_terms<kKind>(wq, a, sv[u], ov[u], part[m]);
           }
         }
       }
@@ -276,17 +418,17 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const float* __restrict__
       float S = 0.0f;
 #pragma unroll
       for (int v = 0; v < NW; ++v) S = S + part_w[v][tid];
-      if constexpr (!kFused) {
+      if constexpr (kBQ) {
+        if (n_out < w.N) Y[m * ldy + n_out] = finish_bq(S, bias_c, lo, hi);
+      } else {
+        float sa = 0.0f;
+        int32_t za = 0;
 #pragma unroll
         for (int r = 0; r < MR; ++r)
           if (r == m) {
             sa = sa_m[r];
             za = za_m[r];
           }
-      }
-      if constexpr (kBQ) {
-        if (n_out < w.N) Y[m * ldy + n_out] = finish_bq(S, bias_c, lo, hi);
-      } else {
         if (n_out < w.N) Y[m * ldy + n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
       }
     }
@@ -748,35 +890,46 @@ qp_status validate_w4(const qp_packed_info* b, int64_t K) {
   return QP_OK;
 }
 
-template <int NT>
-qp_status launch_gemv_cfg(const float* X, int64_t K, const int8_t* qa, int64_t lda,
-                          const float* sa, const int32_t* za, int64_t M, const W4& w,
-                          const float* bias, float lo, float hi, float* Y, int64_t ldy,
-                          bool fused, hipStream_t stream) {
+// Largest Kpad of the fused GEMV: its codes live in the workgroup's LDS,
+// which stays within the 64 KiB a launch gets without raising its limit.
+constexpr int64_t kFusedGemvMaxKpad = 32768;
+
+// M = 1 from f32: the wave-specialized kernel (8 quantizer + 8 weight waves,
+// four blocks per weight wave and batch).
+qp_status launch_gemv_fused(const float* X, int64_t K, const W4& w, const float* bias, float lo,
+                            float hi, float* Y, hipStream_t stream) {
   const unsigned blocks = (unsigned)(w.Npad / 16);
-  const size_t lds = fused ? (size_t)w.Kpad : 0;
-#define QP_GEMV(F, KIND)                                                                      \
-  hipLaunchKernelGGL((a8w4_gemv_kernel<NT, F, KIND>), dim3(blocks), dim3(NT), lds, stream, X, K, \
-                     qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy)
-  if (fused) {
-    if (w.kind == 1) QP_GEMV(true, 1);
-    else if (w.kind == 2) QP_GEMV(true, 2);
-    else QP_GEMV(true, 0);
-  } else {
-    if (w.kind == 1) QP_GEMV(false, 1);
-    else if (w.kind == 2) QP_GEMV(false, 2);
-    else QP_GEMV(false, 0);
-  }
-#undef QP_GEMV
+  const size_t lds = (size_t)w.Kpad;
+  constexpr int NQ = 8, NWW = 8, BB = 4;
+  if (w.kind == 1)
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 1>), dim3(blocks),
+                       dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
+  else if (w.kind == 2)
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 2>), dim3(blocks),
+                       dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
+  else
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 0>), dim3(blocks),
+                       dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
   return check_launch("a8w4 gemv");
 }
 
-qp_status launch_gemv(const float* X, int64_t K, const int8_t* qa, int64_t lda,
-                      const float* sa, const int32_t* za, int64_t M, const W4& w,
-                      const float* bias, float lo, float hi, float* Y, int64_t ldy, bool fused,
+// M <= 4 quantized rows (row-major, lda >= Kpad).
+qp_status launch_gemv(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za, int64_t M,
+                      const W4& w, const float* bias, float lo, float hi, float* Y, int64_t ldy,
                       hipStream_t stream) {
   QP_REQUIRE(M <= 4, QP_EUNSUPPORTED, "a8w4 gemv: at most 4 rows");
-  return launch_gemv_cfg<512>(X, K, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, fused, stream);
+  constexpr int NT = 512;
+  const unsigned blocks = (unsigned)(w.Npad / 16);
+  if (w.kind == 1)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, 1>), dim3(blocks), dim3(NT), 0, stream, qa, lda, sa,
+                       za, M, w, bias, lo, hi, Y, ldy);
+  else if (w.kind == 2)
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, 2>), dim3(blocks), dim3(NT), 0, stream, qa, lda, sa,
+                       za, M, w, bias, lo, hi, Y, ldy);
+  else
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, 0>), dim3(blocks), dim3(NT), 0, stream, qa, lda, sa,
+                       za, M, w, bias, lo, hi, Y, ldy);
+  return check_launch("a8w4 gemv");
 }
 
 // One row quantized per block: sa, za hold the row's group parameters.
@@ -785,11 +938,11 @@ qp_status launch_gemv_bq(const int8_t* qa, const float* sa, const int32_t* za, c
   constexpr int NT = 512;
   const unsigned blocks = (unsigned)(w.Npad / 16);
   if (w.kind == 1)
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, 1, true>), dim3(blocks), dim3(NT), 0, stream,
-                       nullptr, w.Kpad, qa, w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, 1, true>), dim3(blocks), dim3(NT), 0, stream, qa,
+                       w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
   else
-    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, false, 0, true>), dim3(blocks), dim3(NT), 0, stream,
-                       nullptr, w.Kpad, qa, w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
+    hipLaunchKernelGGL((a8w4_gemv_kernel<NT, 0, true>), dim3(blocks), dim3(NT), 0, stream, qa,
+                       w.Kpad, sa, za, 1, w, bias, lo, hi, Y, w.N);
   return check_launch("a8w4 gemv (per-block activations)");
 }
 
@@ -855,7 +1008,9 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32_ws_size(int64_t M, const qp_packed
                                                       size_t* bytes) {
   using namespace qp;
   QP_REQUIRE(w && bytes && M >= 0, QP_EINVAL, "qgemm_a8w4_blockwise_f32_ws_size: bad argument");
-  *bytes = M <= 1 ? 0 : (size_t)(round_up(M * w->Kpad, 256) + round_up(8 * M, 256));
+  // one row with its codes fitting the fused GEMV's LDS needs no workspace
+  const bool fused = M <= 1 && w->Kpad <= kFusedGemvMaxKpad;
+  *bytes = fused ? 0 : (size_t)(round_up(M * w->Kpad, 256) + round_up(8 * M, 256));
   return QP_OK;
 }
 
@@ -873,9 +1028,8 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32(const float* X, int64_t M, int64_t
   if (M == 0) return QP_OK;
   QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
   const W4 wv = w4_of(w, packedW_dev);
-  if (M == 1)
-    return launch_gemv(X, K, nullptr, 0, nullptr, nullptr, 1, wv, bias, clamp_lo, clamp_hi, Y, ldy,
-                       true, stream);
+  if (M == 1 && w->Kpad <= kFusedGemvMaxKpad)
+    return launch_gemv_fused(X, K, wv, bias, clamp_lo, clamp_hi, Y, stream);
   size_t need = 0;
   qgemm_a8w4_blockwise_f32_ws_size(M, w, &need);
   QP_REQUIRE(ws_bytes >= need, QP_ESIZE, "a8w4: workspace holds %zu bytes, needs %zu", ws_bytes,
@@ -886,6 +1040,11 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32(const float* X, int64_t M, int64_t
   int8_t* qa = reinterpret_cast<int8_t*>(p);
   float* sa = reinterpret_cast<float*>(p + round_up(M * w->Kpad, 256));
   int32_t* za = reinterpret_cast<int32_t*>(sa + M);
+  if (M == 1) {  // codes too long for the fused GEMV's LDS: quantize, then the GEMV
+    st = launch_quantize_rows(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, false, stream);
+    if (st) return st;
+    return launch_gemv(qa, w->Kpad, sa, za, 1, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
+  }
   st = launch_quantize_rows(X, M, K, ldx, qa, w->Kpad, w->Kpad, sa, za, true, stream);
   if (st) return st;
   return launch_gemm(qa, w->Kpad, true, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
@@ -945,7 +1104,7 @@ extern "C" qp_status qgemm_a8w4_blockwise_f32_noalloc(const float* X, int64_t M,
              "a8w4 (no allocation): M=%lld rows of Kpad=%lld need %zu bytes of scratch, "
              "more than the %zu available",
              (long long)M, (long long)w->Kpad, need, kNoAllocScratchBytes);
-  if (M == 1)  // the fused GEMV keeps the quantized row in LDS: no scratch
+  if (need == 0)  // one row in the fused GEMV, which keeps its codes in LDS: no scratch
     return qgemm_a8w4_blockwise_f32(X, M, K, ldx, w, packedW_dev, bias, clamp_lo, clamp_hi, Y,
                                     ldy, nullptr, 0, stream);
   uint8_t* ws = nullptr;
@@ -972,8 +1131,7 @@ extern "C" qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_
   QP_REQUIRE(lda <= (INT64_C(1) << 24), QP_EUNSUPPORTED, "a8w4: lda above 2^24 bytes");
   const W4 wv = w4_of(w, packedW_dev);
   if (M <= 4)
-    return launch_gemv(nullptr, w->K, qa, lda, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy,
-                       false, stream);
+    return launch_gemv(qa, lda, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
   return launch_gemm(qa, lda, false, sa, za, M, wv, bias, clamp_lo, clamp_hi, Y, ldy, stream);
 }
 

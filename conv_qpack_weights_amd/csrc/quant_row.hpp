@@ -90,41 +90,72 @@ __device__ __forceinline__ uint32_t quantize_one(float x, float s, int32_t z) {
 // offset 32c + 8t, so the four pieces one lane needs are 32 contiguous
 // bytes (requires kfill % 128 == 0 and a 16-byte aligned dst).
 // The thread's first E values, loaded ahead (quantize_row_first) so that a
-// caller can put the row's loads in flight before other traffic.
+// caller can put the row's loads in flight before other traffic.  The loads
+// are unconditional buffer loads bounded by the row (past its end they
+// return zeros and touch no memory), so no branch joins their results: a
+// join would make the compiler wait for them right away.  quantize_row_wg
+// uses them only where a whole aligned vector lies inside the row.
 struct RowFirst {
   float4 v[4];
 };
 template <int NT, int E = 16>
 __device__ __forceinline__ RowFirst quantize_row_first(const float* __restrict__ x, int64_t K,
                                                        bool vec) {
+  static_assert(E == 16 || E == 8 || E == 4, "4, 8 or 16 values per thread");
   RowFirst f;
   const int64_t k0 = (int64_t)threadIdx.x * E;
-  if (vec && k0 + E <= K) {
+  const uint32_t bytes = (uint32_t)(K < (INT64_C(1) << 29) ? 4 * K : (INT64_C(1) << 31));
+  const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x), 0, bytes, 0x00020000);
+  const uint32_t off = (uint32_t)(k0 < (INT64_C(1) << 29) ? 4 * k0 : (INT64_C(1) << 31));
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) f.v[q] = *reinterpret_cast<const float4*>(x + k0 + 4 * q);
+  for (int q = 0; q < E / 4; ++q) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16 * q, 0, 0);
+    // (bit_cast of a vector element would read element 0: copy them out first)
+    const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+    f.v[q] = make_float4(__builtin_bit_cast(float, v0), __builtin_bit_cast(float, v1),
+                         __builtin_bit_cast(float, v2), __builtin_bit_cast(float, v3));
   }
+  (void)vec;
   return f;
 }
 
-// E: values per thread per pass (16, or 8 to spread a short row over more
-// threads).  kSym: symmetric variant -- scale = max|x| / 127 (1 for an
-// all-zero row), zero point 0, codes clamp(rint(x/scale), -127, 127).
-template <int NT, bool kChunkMajor = false, int E = 16, bool kSym = false>
-__device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
-                                                int64_t kfill, bool vec, bool dst_vec,
-                                                int8_t* __restrict__ dst, float* red,
-                                                float* s_out, int32_t* z_out,
-                                                const RowFirst* pre = nullptr) {
-  static_assert(E == 16 || E == 8, "8 or 16 values per thread");
+// The steps of one row's quantization, for NT threads (threadIdx.x < NT
+// take part; NT a multiple of 64) and E values per thread per pass (16, or
+// 8 or 4 to spread a short row over more threads).  kSym: the symmetric
+// variant -- scale = max|x| / 127 (1 for an all-zero row), zero point 0,
+// codes clamp(rint(x/scale), -127, 127).
+//
+// Step 1, row_extremes_partial: each thread's extremes over its values, a
+// wave reduction, and the wave's pair written to red[wave], red[NT/64 +
+// wave].  A thread's first E values stay in `first` for step 3 (rows of up
+// to E*NT values are read once); `pre` optionally holds them already loaded.
+// kOne: the caller guarantees K == NT*E, a 16-byte aligned x and `pre`
+// (one pass of whole vectors, no fallbacks).
+template <int NT, int E, bool kSym, bool kOne = false>
+__device__ __forceinline__ void row_extremes_partial(const float* __restrict__ x, int64_t K,
+                                                     bool vec, float* red, float4 (&first)[4],
+                                                     const RowFirst* pre) {
+  static_assert(E == 16 || E == 8 || E == 4, "4, 8 or 16 values per thread");
   constexpr int NW = NT / 64;
   constexpr int Q = E / 4;
   const int t = threadIdx.x;
   float lo = 0.0f, hi = 0.0f;
-  // pass 1: extremes; a thread's first E values stay in registers for pass
-  // 2 (rows of up to E*NT values are read once)
-  float4 first[Q];
-  const bool keep = vec && (int64_t)t * E + E <= K;
-  for (int64_t k0 = (int64_t)t * E; k0 < K; k0 += NT * E) {
+  if constexpr (kOne) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float4 v = pre->v[q];
+      first[q] = v;
+      if constexpr (kSym) {
+        hi = qp_max(qp_max(qp_max(qp_max(hi, __builtin_fabsf(v.x)), __builtin_fabsf(v.y)),
+                           __builtin_fabsf(v.z)),
+                    __builtin_fabsf(v.w));
+      } else {
+        lo = qp_min(qp_min(qp_min(qp_min(lo, v.x), v.y), v.z), v.w);
+        hi = qp_max(qp_max(qp_max(qp_max(hi, v.x), v.y), v.z), v.w);
+      }
+    }
+  }
+  for (int64_t k0 = (int64_t)t * E; !kOne && k0 < K; k0 += NT * E) {
     if (vec && k0 + E <= K) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
@@ -161,27 +192,48 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
     red[wave] = lo;
     red[NW + wave] = hi;
   }
-  __syncthreads();
-  lo = red[0];
-  hi = red[NW];
+}
+
+// Step 2 (after a barrier that makes step 1's writes visible): the row's
+// scale and zero point from the waves' pairs, combined in wave order.
+template <int NT, bool kSym>
+__device__ __forceinline__ void row_params(const float* red, float* s_out, int32_t* z_out) {
+  constexpr int NW = NT / 64;
+  float lo = red[0], hi = red[NW];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     lo = qp_min(lo, red[w]);
     hi = qp_max(hi, red[NW + w]);
   }
-  float s;
-  int32_t z;
   if constexpr (kSym) {
-    s = hi / 127.0f;
+    float s = hi / 127.0f;
     if (s == 0.0f) s = 1.0f;
-    z = 0;
+    *s_out = s;
+    *z_out = 0;
   } else {
-    params_from_range(lo, hi, &s, &z);
+    params_from_range(lo, hi, s_out, z_out);
   }
-  // pass 2: codes (beyond the first E per thread, x is read again)
-  for (int64_t k0 = (int64_t)t * E; k0 < kfill; k0 += NT * E) {
+}
+
+// Step 3: the codes of the thread's values into dst[0, kfill) (zeros past
+// K); beyond the first E values per thread, x is read again.  Codes are
+// written 16 bytes at a time when `dst_vec` (dst 16-byte aligned), else
+// byte by byte.
+// kChunkMajor: dst receives the codes permuted for the A8W4 GEMV -- within
+// each 128-K block the 8-byte piece (t, c) holding k = 32t + 8c .. +8 goes to
+// offset 32c + 8t, so the four pieces one lane needs are 32 contiguous
+// bytes (requires kfill % 128 == 0 and a 16-byte aligned dst).
+// kOne: as for step 1, and kfill == K (the thread's E values, once).
+template <int NT, int E, bool kChunkMajor, bool kSym, bool kOne = false>
+__device__ __forceinline__ void row_codes(const float* __restrict__ x, int64_t K, int64_t kfill,
+                                          bool vec, bool dst_vec, int8_t* __restrict__ dst,
+                                          float s, int32_t z, const float4 (&first)[4]) {
+  constexpr int Q = E / 4;
+  const int t = threadIdx.x;
+  const bool keep = kOne || (vec && (int64_t)t * E + E <= K);
+  for (int64_t k0 = (int64_t)t * E; kOne || k0 < kfill; k0 += NT * E) {
     uint32_t w[Q];
-    if (vec && k0 + E <= K) {
+    if (kOne || (vec && k0 + E <= K)) {
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const float4 v = (keep && k0 == (int64_t)t * E)
@@ -204,21 +256,49 @@ __device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int
     }
     if constexpr (kChunkMajor) {
       // the 8-byte piece holding k = 128b + 32g + 8c .. +8 goes to 128b + 32c + 8g
+      if constexpr (E == 4) {  // half a piece: k0 % 8 is 0 or 4
+        const int64_t b = k0 >> 7, g = (k0 >> 5) & 3, cc = (k0 >> 3) & 3;
+        *reinterpret_cast<uint32_t*>(dst + b * 128 + cc * 32 + g * 8 + (k0 & 4)) = w[0];
+      } else {
 #pragma unroll
-      for (int h = 0; h < Q / 2; ++h) {
-        const int64_t kk = k0 + 8 * h;
-        const int64_t b = kk >> 7, g = (kk >> 5) & 3, cc = (kk >> 3) & 3;
-        *reinterpret_cast<uint2*>(dst + b * 128 + cc * 32 + g * 8) = make_uint2(w[2 * h], w[2 * h + 1]);
+        for (int h = 0; h < Q / 2; ++h) {
+          const int64_t kk = k0 + 8 * h;
+          const int64_t b = kk >> 7, g = (kk >> 5) & 3, cc = (kk >> 3) & 3;
+          *reinterpret_cast<uint2*>(dst + b * 128 + cc * 32 + g * 8) =
+              make_uint2(w[2 * h], w[2 * h + 1]);
+        }
       }
     } else if (dst_vec && k0 + E <= kfill) {
       if constexpr (E == 16)
         *reinterpret_cast<uint4*>(dst + k0) = make_uint4(w[0], w[1], w[2], w[3]);
-      else
+      else if constexpr (E == 8)
         *reinterpret_cast<uint2*>(dst + k0) = make_uint2(w[0], w[1]);
+      else
+        *reinterpret_cast<uint32_t*>(dst + k0) = w[0];
     } else {
       for (int j = 0; j < E && k0 + j < kfill; ++j) dst[k0 + j] = (int8_t)(w[j >> 2] >> (8 * (j & 3)));
     }
+    if constexpr (kOne) break;
   }
+}
+
+// Workgroup quantization of one row of K floats into `dst` (LDS or global):
+// the three steps with a barrier between the first two.  Every thread of
+// the workgroup (blockDim.x == NT) takes part; `red` is LDS scratch of 2
+// floats per wave.
+template <int NT, bool kChunkMajor = false, int E = 16, bool kSym = false>
+__device__ __forceinline__ void quantize_row_wg(const float* __restrict__ x, int64_t K,
+                                                int64_t kfill, bool vec, bool dst_vec,
+                                                int8_t* __restrict__ dst, float* red,
+                                                float* s_out, int32_t* z_out,
+                                                const RowFirst* pre = nullptr) {
+  float4 first[4];
+  row_extremes_partial<NT, E, kSym>(x, K, vec, red, first, pre);
+  __syncthreads();
+  float s;
+  int32_t z;
+  row_params<NT, kSym>(red, &s, &z);
+  row_codes<NT, E, kChunkMajor, kSym>(x, K, kfill, vec, dst_vec, dst, s, z, first);
   *s_out = s;
   *z_out = z;
 }
