@@ -133,14 +133,34 @@ __device__ __forceinline__ float4 load_scale4_bounded(__amdgpu_buffer_rsrc_t r, 
 // wq holds the chunk's 8-K piece of four groups, a[t] the activations of
 // group t's piece (bytes k..k+3 in .x, k+4..k+7 in .y), sv / ov the group
 // scales / offsets.  Adds the block's four group terms to `part`.
+// The nibbles of the four weight words come unpacked (nibble_ops): low
+// nibbles shifted up in nl[t], high ones masked in nh[t], each as int8 16*q.
+struct Nibbles {
+  uint32_t lo[4], hi[4];
+};
+__device__ __forceinline__ Nibbles nibble_ops(const uint4& wq) {
+  Nibbles n;
+  const uint32_t w4[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    n.lo[t] = nib_lo16(w4[t]);
+    n.hi[t] = nib_hi16(w4[t]);
+  }
+  return n;
+}
+__device__ __forceinline__ int32_t nib_dot16(uint32_t lo, uint32_t hi, uint32_t a0, uint32_t a1) {
+  return __builtin_amdgcn_sdot4((int)a1, (int)hi, __builtin_amdgcn_sdot4((int)a0, (int)lo, 0, false),
+                                false);
+}
+
 template <int kKind>
-__device__ __forceinline__ void gemv_block_terms(const uint4& wq, const uint2 (&a)[4],
+__device__ __forceinline__ void gemv_block_terms(const Nibbles& nb, const uint2 (&a)[4],
                                                  const float4& sv, const float4& ov,
                                                  float& part) {
-  const float d0 = (float)word_dot16(wq.x, a[0].x, a[0].y);
-  const float d1 = (float)word_dot16(wq.y, a[1].x, a[1].y);
-  const float d2 = (float)word_dot16(wq.z, a[2].x, a[2].y);
-  const float d3 = (float)word_dot16(wq.w, a[3].x, a[3].y);
+  const float d0 = (float)nib_dot16(nb.lo[0], nb.hi[0], a[0].x, a[0].y);
+  const float d1 = (float)nib_dot16(nb.lo[1], nb.hi[1], a[1].x, a[1].y);
+  const float d2 = (float)nib_dot16(nb.lo[2], nb.hi[2], a[2].x, a[2].y);
+  const float d3 = (float)nib_dot16(nb.lo[3], nb.hi[3], a[3].x, a[3].y);
   if constexpr (kKind == 2) {
     // a group piece's term scale*d + offset*(16 * activation sum) is
     // formed first, so the running sum takes one addition per piece
@@ -161,6 +181,8 @@ __device__ __forceinline__ void gemv_block_terms(const uint4& wq, const uint2 (&
 }
 
 // ---- GEMV with the row's dynamic quantization (M = 1) ---------------------
+// (NQ quantizer waves, NWW weight waves, BB blocks per weight wave and
+// batch, QE row values per quantizer thread and pass)
 // One workgroup per 16-channel tile, two kinds of waves:
 //  * NQ quantizer waves load the f32 row (branch-free, bounded loads) and
 //    quantize it with the steps of qquantize_rows_s8 into LDS, permuted so
@@ -176,12 +198,11 @@ __device__ __forceinline__ void gemv_block_terms(const uint4& wq, const uint2 (&
 // are in LDS the weight waves form the exact int32 group dots and the f32
 // scaled sum, reduce over the four lanes of a channel (DPP) and then over
 // the weight waves through LDS in a fixed order.
-template <int NQ, int NWW, int BB, int kKind>
+template <int NQ, int NWW, int BB, int QE, int kKind>
 __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
     const float* __restrict__ X, int64_t K, W4 w, const float* __restrict__ bias, float lo,
     float hi, float* __restrict__ Y) {
   constexpr int QT = NQ * 64;  // quantizer threads
-  constexpr int QE = 8;        // row values a quantizer thread handles per pass
   constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
   extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];  // [Kpad] codes
@@ -251,15 +272,25 @@ __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
       }
     };
     float part = 0.0f;
+    // Nothing may wait for the weights before the barriers, where the
+    // quantizer waves wait for every wave: each block's fence keeps the first
+    // use of its loads (the unpack) after them, and the blocks are taken in
+    // the order their loads complete.
     auto compute_batch = [&]() {
+      uint4 p0[BB], p1[BB];  // the codes first: their LDS reads need no weights
 #pragma unroll
       for (int u = 0; u < BB; ++u) {
         const int8_t* ab = qa_lds + blk[u] * 128 + c * 32;
-        const uint4 p0 = *reinterpret_cast<const uint4*>(ab);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 16);
-        const uint2 a[4] = {make_uint2(p0.x, p0.y), make_uint2(p0.z, p0.w),
-                            make_uint2(p1.x, p1.y), make_uint2(p1.z, p1.w)};
-        gemv_block_terms<kKind>(wv[u], a, sv[u], ov[u], part);
+        p0[u] = *reinterpret_cast<const uint4*>(ab);
+        p1[u] = *reinterpret_cast<const uint4*>(ab + 16);
+      }
+#pragma unroll
+      for (int u = 0; u < BB; ++u) {
+        asm volatile("" : "+v"(wv[u].x), "+v"(wv[u].y), "+v"(wv[u].z), "+v"(wv[u].w));
+        const Nibbles nb4 = nibble_ops(wv[u]);
+        const uint2 a[4] = {make_uint2(p0[u].x, p0[u].y), make_uint2(p0[u].z, p0[u].w),
+                            make_uint2(p1[u].x, p1[u].y), make_uint2(p1[u].z, p1[u].w)};
+        gemv_block_terms<kKind>(nb4, a, sv[u], ov[u], part);
       }
     };
     load_batch(0);
@@ -399,7 +430,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const int8_t* __restrict_
             part[m] = part[m] + (saq[u].z * sv[u].z) * (float)e2;
             part[m] = part[m] + (saq[u].w * sv[u].w) * (float)e3;
           } else {
-            gemv_block_terms<kKind>(wq, a, sv[u], ov[u], part[m]);
+            gemv_block_terms<kKind>(nibble_ops(wq), a, sv[u], ov[u], part[m]);
           }
         }
       }
@@ -894,21 +925,22 @@ qp_status validate_w4(const qp_packed_info* b, int64_t K) {
 // which stays within the 64 KiB a launch gets without raising its limit.
 constexpr int64_t kFusedGemvMaxKpad = 32768;
 
-// M = 1 from f32: the wave-specialized kernel (8 quantizer + 8 weight waves,
-// four blocks per weight wave and batch).
+// M = 1 from f32: the wave-specialized kernel.  4 quantizer waves of 16
+// values a thread and 8 weight waves of four blocks a batch (768 threads)
+// measured faster than 8 + 8, 4 + 12 or 8 + 4.
 qp_status launch_gemv_fused(const float* X, int64_t K, const W4& w, const float* bias, float lo,
                             float hi, float* Y, hipStream_t stream) {
   const unsigned blocks = (unsigned)(w.Npad / 16);
   const size_t lds = (size_t)w.Kpad;
-  constexpr int NQ = 8, NWW = 8, BB = 4;
+  constexpr int NQ = 4, NWW = 8, BB = 4, QE = 16;
   if (w.kind == 1)
-    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 1>), dim3(blocks),
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, QE, 1>), dim3(blocks),
                        dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
   else if (w.kind == 2)
-    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 2>), dim3(blocks),
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, QE, 2>), dim3(blocks),
                        dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
   else
-    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, 0>), dim3(blocks),
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, QE, 0>), dim3(blocks),
                        dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
   return check_launch("a8w4 gemv");
 }
