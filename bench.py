@@ -97,7 +97,8 @@ def _floors_lib():
     h = C.CDLL(path)
     h.qpf_stream_read.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
                                   C.c_void_p]
-    h.qpf_mfma_loop.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    h.qpf_mfma_loop.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                C.c_void_p]
     h.qpf_empty.argtypes = [C.c_void_p]
     return h
 
@@ -277,23 +278,33 @@ def main():
                      "algorithmic": "2*M*N*K = %.4e int8 ops per launch" % ops},
     }
 
-    # measured int8 MFMA peak: a loop of independent v_mfma_i32_32x32x32_i8
-    # with 1, 2 and 3 waves a SIMD; the best rate
-    best_mfma = None
-    for blocks, nacc in ((256, 16), (512, 8), (768, 8)):
-        iters = 2000
+    # measured int8 MFMA ceilings: loops of independent v_mfma_i32_32x32x32_i8
+    # with 1, 2 and 3 waves a SIMD (the best rate of each kind), fed either
+    # rotating random-looking operands (the power-limited ceiling for
+    # uniform int8 data like this workload's) or small constant operands
+    # (the clock-limited ceiling)
+    def mfma_ceiling(random):
+        best = None
+        for blocks, nacc in ((256, 16), (512, 8), (768, 8)):
+            iters = 2000
 
-        def mloop():
-            rc = F.qpf_mfma_loop(iters, blocks, nacc, C.c_void_p(sinkf.data_ptr()), cur_stream())
-            assert rc == 0
-        mloop()
-        msl = ev_time(mloop, 5)
-        tops = blocks * 4 * iters * nacc * 65536 / (msl * 1e-3) / 1e12
-        if best_mfma is None or tops > best_mfma[0]:
-            best_mfma = (tops, "%d workgroups x 4 waves, %d accumulators a wave" % (blocks, nacc))
+            def mloop():
+                rc = F.qpf_mfma_loop(iters, blocks, nacc, int(random), C.c_void_p(sinkf.data_ptr()),
+                                     cur_stream())
+                assert rc == 0
+            mloop()
+            msl = ev_time(mloop, 5)
+            tops = blocks * 4 * iters * nacc * 65536 / (msl * 1e-3) / 1e12
+            if best is None or tops > best[0]:
+                best = (tops, "%d workgroups x 4 waves, %d accumulators a wave" % (blocks, nacc))
+        return best
+    best_mfma = mfma_ceiling(True)
+    best_mfma_small = mfma_ceiling(False)
     out["roofline"]["measured_peak"] = round(best_mfma[0], 1)
     out["roofline"]["frac_of_measured_peak"] = round(achieved / best_mfma[0], 4)
-    out["roofline"]["measured_peak_kernel"] = "int8 MFMA loop (" + best_mfma[1] + ")"
+    out["roofline"]["measured_peak_kernel"] = ("int8 MFMA loop on random operands (" +
+                                              best_mfma[1] + ")")
+    out["roofline"]["measured_peak_small_operands"] = round(best_mfma_small[0], 1)
     empty_us = graph_time(lambda: F.qpf_empty(cur_stream()), 100) * 1e3
 
     tr = _measured_traffic()
@@ -651,7 +662,9 @@ def main():
             "us": round(mss * 1e3, 2), "TOPS": round(2 * 130 * 70 * 129 / mss / 1e9, 4),
             "note": "A repack + GEMM launches; latency-bound"}
         workloads["machine_floors"] = {
-            "mfma_i8_loop_TOPS": round(best_mfma[0], 1), "mfma_i8_loop_config": best_mfma[1],
+            "mfma_i8_loop_random_operands_TOPS": round(best_mfma[0], 1),
+            "mfma_i8_loop_random_operands_config": best_mfma[1],
+            "mfma_i8_loop_small_operands_TOPS": round(best_mfma_small[0], 1),
             "empty_launch_us": round(empty_us, 3),
             "note": "measured on this GPU in this run (libqpfloors.so): read-only HBM streams "
                     "under each A8W4 workload, an MFMA loop of independent 32x32x32 int8 "

@@ -42,18 +42,35 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
 // Each wave: `iters` rounds of NACC independent v_mfma_i32_32x32x32_i8
 // (65536 int8 operations each).  NACC = 16 holds 256 accumulator registers
 // (one wave per SIMD); NACC = 8 leaves room for two.
-template <int NACC>
+// kRandom: the operands rotate through 8 register pairs of random-looking
+// bytes, like the changing fragments of a GEMM on uniform int8 data; the
+// MFMA's power then depends on the data, and the clock it sustains is the
+// part's real dense-int8 ceiling for such data.  Otherwise the operands are
+// small constant values (the clock-limited ceiling).
+template <int NACC, bool kRandom>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int32_t iters, uint32_t* sink) {
+  constexpr int NOP = kRandom ? 8 : 1;
   const int t = threadIdx.x;
-  const v4i a = v4i{t, t + 1, t + 2, t + 3};
-  const v4i b = v4i{t ^ 5, t ^ 6, t ^ 7, t ^ 9};
+  v4i a[NOP], b[NOP];
+#pragma unroll
+  for (int p = 0; p < NOP; ++p) {
+    if constexpr (kRandom) {
+      const uint32_t s0 = 0x9E3779B9u * (uint32_t)(t + 1 + 131 * p) + blockIdx.x * 0x85EBCA6Bu;
+      a[p] = v4i{(int)s0, (int)(s0 * 3u), (int)(s0 * 5u), (int)(s0 * 7u)};
+      b[p] = v4i{(int)(s0 ^ 0xA5A5A5A5u), (int)(s0 * 11u), (int)(s0 * 13u), (int)(s0 * 17u)};
+    } else {
+      a[p] = v4i{t, t + 1, t + 2, t + 3};
+      b[p] = v4i{t ^ 5, t ^ 6, t ^ 7, t ^ 9};
+    }
+  }
   v16i acc[NACC];
 #pragma unroll
   for (int j = 0; j < NACC; ++j) acc[j] = v16i{} + j;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < NACC; ++j)
-      acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j % NOP], b[(3 * j + it) % NOP], acc[j], 0,
+                                                      0, 0);
   }
   uint32_t x = 0;
 #pragma unroll
@@ -84,14 +101,23 @@ int qpf_stream_read(const void* src, int64_t bytes, int32_t blocks, int32_t unro
 }
 
 // `blocks` workgroups of four waves, each running `iters` rounds of `nacc`
-// (8 or 16) MFMAs.  Operations per launch: blocks * 4 * iters * nacc * 65536.
-int qpf_mfma_loop(int32_t iters, int32_t blocks, int32_t nacc, uint32_t* sink,
+// (8 or 16) MFMAs; `random` selects rotating random-looking operands.
+// Operations per launch: blocks * 4 * iters * nacc * 65536.
+int qpf_mfma_loop(int32_t iters, int32_t blocks, int32_t nacc, int32_t random, uint32_t* sink,
                   hipStream_t stream) {
   if (iters <= 0 || blocks <= 0 || !sink) return -1;
-  if (nacc == 16)
-    hipLaunchKernelGGL(mfma_loop_kernel<16>, dim3(blocks), dim3(256), 0, stream, iters, sink);
+  if (nacc == 16 && random)
+    hipLaunchKernelGGL((mfma_loop_kernel<16, true>), dim3(blocks), dim3(256), 0, stream, iters,
+                       sink);
+  else if (nacc == 16)
+    hipLaunchKernelGGL((mfma_loop_kernel<16, false>), dim3(blocks), dim3(256), 0, stream, iters,
+                       sink);
+  else if (nacc == 8 && random)
+    hipLaunchKernelGGL((mfma_loop_kernel<8, true>), dim3(blocks), dim3(256), 0, stream, iters,
+                       sink);
   else if (nacc == 8)
-    hipLaunchKernelGGL(mfma_loop_kernel<8>, dim3(blocks), dim3(256), 0, stream, iters, sink);
+    hipLaunchKernelGGL((mfma_loop_kernel<8, false>), dim3(blocks), dim3(256), 0, stream, iters,
+                       sink);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -6;

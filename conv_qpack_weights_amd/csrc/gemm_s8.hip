@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ 
 }
 
 template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kHi,
-          bool kF32>
+          bool kF32, int WM = 1>
 qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (int32_t)ceil_div(a.M, BM);
@@ -91,7 +91,7 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   if (blocks == 0) return QP_OK;
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
   const size_t lds = (size_t)SA * BM * BK;
-  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32>;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32, WM>;
   // The LDS limit is raised once per instantiation and device (threads may
   // race to set it; repeating it is harmless).
   static std::atomic<uint64_t> lds_attr_devices{0};
@@ -113,7 +113,7 @@ qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
   const bool k128 = (a.Kpad % 128) == 0;
   const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   if (k128 && big_tiles >= 256)
-    return launch_cfg<256, 256, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
+    return launch_cfg<256, 256, 128, 8, 4, 32, kOut32, kRowSum, kHi, kF32, 2>(a, stream);
   if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
     return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
   return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi, kF32>(a, stream);

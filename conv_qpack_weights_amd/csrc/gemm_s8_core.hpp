@@ -217,12 +217,15 @@ __device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
 //    MFMA operand order, one tile ahead: each wave owns BN/NW columns, so no
 //    B byte is loaded twice and LDS only carries A.
 // kF32 (with kOut32): f32 output y = clamp(sA*sB[n]*acc + bias_f[n], clo, chi).
+// WM: the waves form WM row groups x NW/WM column groups; a wave computes
+// TM = BM/WM rows x TN = BN/(NW/WM) channels (WM = 1: every wave covers all
+// rows of the tile).
 template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kShiftHi,
-          bool kF32 = false>
+          bool kF32 = false, int WM = 1>
 __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   constexpr int CH = BK / 16;  // 16-byte chunks per A tile row
-  constexpr int TM = BM;       // every wave covers all rows of the tile
-  constexpr int TN = BN / NW;
+  constexpr int TM = BM / WM;
+  constexpr int TN = BN / (NW / WM);
   constexpr int FM = TM / MF;
   constexpr int FN = TN / MF;
   constexpr int KSTEP = MF == 16 ? 64 : 32;  // K per MFMA
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   constexpr int STAGE = BM * BK;
   typedef int accv __attribute__((ext_vector_type(NREG)));
   static_assert(BM * CH % (64 * NW) == 0, "A tile must split evenly over the waves");
-  static_assert(TN % MF == 0 && TM % MF == 0 && BK % KSTEP == 0, "tile shape");
+  static_assert(TN % MF == 0 && TM % MF == 0 && BK % KSTEP == 0 && NW % WM == 0, "tile shape");
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(!kF32 || kOut32, "f32 output uses the 4-byte store paths");
   static_assert(SA >= 2 && (SA - 2) * IA + IB < 64, "vmcnt range");
@@ -244,7 +247,8 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave;
+  const int wn = wave % (NW / WM);  // the wave's column group
+  const int wm = wave / (NW / WM);  // and row group
 
   // ---- tile index: XCD-aware (dispatch round-robins over 8 XCDs), then
   // grouped along M so concurrent workgroups share A rows and B rows in L2.
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     for (int j = 0; j < FM; ++j) acc[i][j] = accv{};
 
   // fragment lane mapping of A: row = lane % MF, 16-byte chunk = lane / MF
-  const int frow = lane % MF;
+  const int frow = lane % MF + wm * TM;  // the lane's A row within the tile
   const int fchunk = lane / MF;
   v4i af[FM];
   auto read_a = [&](const int8_t* sa, int sub, int j) {
@@ -408,8 +412,6 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     wait_vmcnt<0>();  // the clamped refills must land before the workgroup ends
   }
 
-  constexpr int WM = 1;
-  const int wm = 0;
   // ---- epilogue ----
   // 16x16 MFMA: register r of a lane is channel 4*(lane/16)+r of row lane%16.
   // 32x32 MFMA: register 4q+r is channel 8q+4*(lane/32)+r of row lane%32.
@@ -510,10 +512,12 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
           uint32_t mask[4];
           column(i, q, &jn, &cc, &mm, &ss, &zb, half, s2, mask);
 #pragma unroll
-          for (int j = p * (PR / MF); j < (p + 1) * (PR / MF); ++j) {
+          for (int j = 0; j < FM; ++j) {
+            const int fr = wm * TM + j * MF;  // the fragment's first row in the tile
+            if (fr < p * PR || fr >= (p + 1) * PR) continue;  // (wave-uniform)
             int32_t out[4];
             outputs(i, q, j, cc, mm, ss, zb, half, s2, mask, out);
-            const int r = j * MF + (lane % MF) - p * PR;  // row inside the pass
+            const int r = fr + (lane % MF) - p * PR;  // row inside the pass
             const int byte = jn * ES;                     // column byte in the row
             int8_t* dst = stg + r * RB + 16 * ((byte >> 4) ^ swz_row(r)) + (byte & 15);
             if constexpr (kOut32) {
