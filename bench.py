@@ -660,7 +660,8 @@ def main():
         mss = graph_time(small, 50)
         workloads["gemm_130x70x129_per_tensor"] = {
             "us": round(mss * 1e3, 2), "TOPS": round(2 * 130 * 70 * 129 / mss / 1e9, 4),
-            "note": "A repack + GEMM launches; latency-bound"}
+            "note": "one launch: the 64x64-tile kernel reads A byte-exact into LDS and "
+                    "forms the row sums there; latency-bound"}
         workloads["machine_floors"] = {
             "mfma_i8_loop_random_operands_TOPS": round(best_mfma[0], 1),
             "mfma_i8_loop_random_operands_config": best_mfma[1],

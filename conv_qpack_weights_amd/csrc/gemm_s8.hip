@@ -79,8 +79,11 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const int8_t* __restrict__ 
   }
 }
 
+// Deepest K the resident-activation kernel holds in LDS (64 rows x Kpad).
+constexpr int64_t kResidentMaxKpad = 960;
+
 template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kHi,
-          bool kF32, int WM = 1>
+          bool kF32, int WM = 1, bool kResident = false>
 qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (int32_t)ceil_div(a.M, BM);
@@ -90,8 +93,11 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks == 0) return QP_OK;
   QP_REQUIRE(blocks < (1LL << 31), QP_EUNSUPPORTED, "qgemm: too many tiles");
-  const size_t lds = (size_t)SA * BM * BK;
-  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32, WM>;
+  // resident activations hold every K tile; the limit is reserved for the
+  // largest depth that mode takes
+  const size_t lds = kResident ? (size_t)(a.Kpad / BK) * BM * BK : (size_t)SA * BM * BK;
+  const size_t lds_max = kResident ? (size_t)kResidentMaxKpad * BM : lds;
+  auto kern = qgemm_s8_kernel<BM, BN, BK, NW, SA, MF, kOut32, kRowSum, kHi, kF32, WM, kResident>;
   // The LDS limit is raised once per instantiation and device (threads may
   // race to set it; repeating it is harmless).
   static std::atomic<uint64_t> lds_attr_devices{0};
@@ -100,23 +106,36 @@ qp_status launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   const uint64_t bit = dev >= 0 && dev < 64 ? (UINT64_C(1) << dev) : 0;
   if (bit == 0 || (lds_attr_devices.load(std::memory_order_acquire) & bit) == 0) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      QP_FAIL(QP_EHIP, "qgemm: cannot reserve %zu bytes of LDS", lds);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max) != hipSuccess)
+      QP_FAIL(QP_EHIP, "qgemm: cannot reserve %zu bytes of LDS", lds_max);
     lds_attr_devices.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), lds, stream, a);
   return check_launch("qgemm_s8s8 kernel");
 }
 
+// Tile configuration: 256x256 (8 waves) when that fills the chip, else
+// 128x128, else 64x64 with one K-step per tile.
+enum GemmCfg { kCfg256, kCfg128, kCfg64 };
+GemmCfg pick_cfg(int64_t M, int64_t N, int64_t Kpad) {
+  const bool k128 = (Kpad % 128) == 0;
+  if (k128 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) return kCfg256;
+  if (k128 && ceil_div(M, 128) * ceil_div(N, 128) >= 256) return kCfg128;
+  return kCfg64;
+}
+
 template <bool kOut32, bool kRowSum, bool kHi, bool kF32 = false>
-qp_status launch_gemm_sel(const GemmArgs& a, hipStream_t stream) {
-  const bool k128 = (a.Kpad % 128) == 0;
-  const int64_t big_tiles = ceil_div(a.M, 256) * ceil_div(a.N, 256);
-  if (k128 && big_tiles >= 256)
-    return launch_cfg<256, 256, 128, 8, 4, 32, kOut32, kRowSum, kHi, kF32, 2>(a, stream);
-  if (k128 && ceil_div(a.M, 128) * ceil_div(a.N, 128) >= 256)
-    return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
-  return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi, kF32>(a, stream);
+qp_status launch_gemm_sel(const GemmArgs& a, bool resident, hipStream_t stream) {
+  switch (pick_cfg(a.M, a.N, a.Kpad)) {
+    case kCfg256:
+      return launch_cfg<256, 256, 128, 8, 4, 32, kOut32, kRowSum, kHi, kF32, 2>(a, stream);
+    case kCfg128:
+      return launch_cfg<128, 128, 128, 4, 4, 32, kOut32, kRowSum, kHi, kF32>(a, stream);
+    default:
+      if (resident)
+        return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi, kF32, 1, true>(a, stream);
+      return launch_cfg<64, 64, 64, 4, 3, 16, kOut32, kRowSum, kHi, kF32>(a, stream);
+  }
 }
 
 }  // namespace
@@ -134,6 +153,7 @@ static bool host_mult_ok(double mr) {
 struct GemmPlan {
   bool copy_a;
   bool rowsum;
+  bool resident;  // one launch: the GEMM reads A byte-exact and sums its rows
   int64_t ws_a, ws_rowsum, ws_total;
 };
 
@@ -145,10 +165,22 @@ static GemmPlan plan_gemm(int64_t M, int64_t K, int64_t lda, const void* A,
   // row, so very wide strides are compacted first as well.
   p.copy_a = (K != b->Kpad) || (lda % 16 != 0) || (((uintptr_t)A) % 16 != 0) ||
              (lda > (INT64_C(1) << 22));
+  p.resident = false;
   p.ws_a = p.copy_a ? round_up(M * b->Kpad, 256) : 0;
   p.ws_rowsum = p.rowsum ? round_up(4 * M, 256) : 0;
   p.ws_total = p.ws_a + p.ws_rowsum;
   return p;
+}
+
+// Small GEMMs (64x64 tiles) that would need the A copy or the row sums take
+// the resident-activation kernel instead: no workspace, one launch.
+static void plan_resident(GemmPlan* p, int64_t M, const qp_packed_info* b) {
+  if ((p->copy_a || p->rowsum) && b->Kpad <= kResidentMaxKpad &&
+      pick_cfg(M, b->N, b->Kpad) == kCfg64) {
+    p->resident = true;
+    p->copy_a = false;
+    p->ws_a = p->ws_rowsum = p->ws_total = 0;
+  }
 }
 
 qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t zA,
@@ -163,15 +195,16 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
     p.ws_a = 0;
     p.ws_total = p.ws_rowsum;
   }
+  plan_resident(&p, M, b);
   QP_REQUIRE(ws_bytes >= (size_t)p.ws_total, QP_ESIZE, "qgemm: workspace holds %zu bytes, needs %lld",
              ws_bytes, (long long)p.ws_total);
   QP_REQUIRE(p.ws_total == 0 || (ws && ((uintptr_t)ws % 256) == 0), QP_EALIGN,
              "qgemm: workspace must be non-null and 256-byte aligned");
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   int8_t* Ap = p.copy_a ? reinterpret_cast<int8_t*>(wsb) : nullptr;
-  int32_t* rs = p.rowsum ? reinterpret_cast<int32_t*>(wsb + p.ws_a) : nullptr;
+  int32_t* rs = p.rowsum && !p.resident ? reinterpret_cast<int32_t*>(wsb + p.ws_a) : nullptr;
   if (M == 0) return QP_OK;
-  if (p.copy_a || p.rowsum) {
+  if (!p.resident && (p.copy_a || p.rowsum)) {
     hipLaunchKernelGGL(prep_a_kernel, dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, stream, A, M,
                        b->K, lda, Ap, b->Kpad, rs);
     qp_status st = check_launch("qgemm prep A");
@@ -205,21 +238,21 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
     a.bias_f = f32->bias;
     a.clo = f32->lo;
     a.chi = f32->hi;
-    return p.rowsum ? launch_gemm_sel<true, true, false, true>(a, stream)
-                    : launch_gemm_sel<true, false, false, true>(a, stream);
+    return p.rowsum ? launch_gemm_sel<true, true, false, true>(a, p.resident, stream)
+                    : launch_gemm_sel<true, false, false, true>(a, p.resident, stream);
   }
   if (out32)
-    return p.rowsum ? launch_gemm_sel<true, true, false>(a, stream)
-                    : launch_gemm_sel<true, false, false>(a, stream);
+    return p.rowsum ? launch_gemm_sel<true, true, false>(a, p.resident, stream)
+                    : launch_gemm_sel<true, false, false>(a, p.resident, stream);
   // All shifts >= 32 <=> every multiplier < 1/2 (with margin for the m0
   // rounding bump); known only when the scales were seen at pack time.
   const bool hi = b->scale_max > 0.0f &&
                   ((double)sA * (double)b->scale_max / (double)sOut) * (1.0 + 1e-6) < 0.5;
   if (hi)
-    return p.rowsum ? launch_gemm_sel<false, true, true>(a, stream)
-                    : launch_gemm_sel<false, false, true>(a, stream);
-  return p.rowsum ? launch_gemm_sel<false, true, false>(a, stream)
-                  : launch_gemm_sel<false, false, false>(a, stream);
+    return p.rowsum ? launch_gemm_sel<false, true, true>(a, p.resident, stream)
+                    : launch_gemm_sel<false, false, true>(a, p.resident, stream);
+  return p.rowsum ? launch_gemm_sel<false, true, false>(a, p.resident, stream)
+                  : launch_gemm_sel<false, false, false>(a, p.resident, stream);
 }
 
 qp_status validate_gemm(const qp_packed_info* b, int64_t K, float sA, int32_t zA,
@@ -268,7 +301,13 @@ extern "C" qp_status qgemm_s8s8_requant_ws_size(const qp_qtensor* a, const qp_pa
   using namespace qp;
   QP_REQUIRE(a && b && bytes, QP_EINVAL, "qgemm_s8s8_requant_ws_size: null argument");
   QP_REQUIRE(a->rank == 2, QP_EINVAL, "qgemm: activations must be rank 2");
-  // The alignment of A is not known here; size for the copying plan.
+  // Small GEMMs need none (direct loads, or the resident-activation
+  // kernel).  Otherwise the alignment of A is not known here: size for the
+  // copying plan.
+  if (b->Kpad <= kResidentMaxKpad && pick_cfg(a->shape[0], b->N, b->Kpad) == kCfg64) {
+    *bytes = 0;
+    return QP_OK;
+  }
   GemmPlan p = plan_gemm(a->shape[0], a->shape[1], a->stride[0], nullptr, b);
   if (!p.copy_a) {
     p.copy_a = true;

@@ -220,8 +220,14 @@ __device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
 // WM: the waves form WM row groups x NW/WM column groups; a wave computes
 // TM = BM/WM rows x TN = BN/(NW/WM) channels (WM = 1: every wave covers all
 // rows of the tile).
+// kResident (one K-step tiles only): the tile's activations for all of K are
+// read once, byte-exact, into LDS -- any row stride and alignment, zeros past
+// K and past M -- and the row sums the weight zero points need are formed on
+// the way (LDS integer atomics); the K loop then reads only LDS.  Small
+// GEMMs with an odd K or stride take this one launch instead of a padded
+// copy of A plus the GEMM.
 template <int BM, int BN, int BK, int NW, int SA, int MF, bool kOut32, bool kRowSum, bool kShiftHi,
-          bool kF32 = false, int WM = 1>
+          bool kF32 = false, int WM = 1, bool kResident = false>
 __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   constexpr int CH = BK / 16;  // 16-byte chunks per A tile row
   constexpr int TM = BM / WM;
@@ -240,9 +246,11 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(!kF32 || kOut32, "f32 output uses the 4-byte store paths");
   static_assert(SA >= 2 && (SA - 2) * IA + IB < 64, "vmcnt range");
+  static_assert(!kResident || SUB == 1, "resident activations: one K-step tiles");
 
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+  __shared__ int32_t row_sum[kResident ? BM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,8 +261,8 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   // ---- tile index: XCD-aware (dispatch round-robins over 8 XCDs), then
   // grouped along M so concurrent workgroups share A rows and B rows in L2.
   const int nblk = gridDim.x;
-  int lin = blockIdx.x;
-  if (g.xcd_remap && (nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
+  const int lin0 = blockIdx.x;
+  const int lin = g.xcd_remap && (nblk & 7) == 0 ? (lin0 & 7) * (nblk >> 3) + (lin0 >> 3) : lin0;
   const int per_group = g.group_m * g.tiles_n;
   const int grp = lin / per_group;
   const int first_m = grp * g.group_m;
@@ -312,31 +320,122 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     for (int i = 0; i < FN; ++i) breg[sub][i] = *reinterpret_cast<const v4i*>(b_src[i] + kb * 1024);
   };
 
-  const int nk = (int)(g.Kpad / BK);
-  // prologue: A(0) .. A(SA-2) into the ring, B(0) into registers
-#pragma unroll
-  for (int p = 0; p < SA - 1; ++p)
-    if (p < nk)
-#pragma unroll
-      for (int j = 0; j < IA; ++j) issue_a(p, p, j);
-#pragma unroll
-  for (int sub = 0; sub < SUB; ++sub) load_b(0, sub);
+  // ---- per-column epilogue inputs, one column per thread.  Every load is
+  // unconditional (the column clamped into range, a stand-in array where
+  // there is no bias) and issued before the A tiles', so that all of them
+  // are in flight at once; the constants are formed after the prologue.
+  static_assert(BN <= NW * 64, "one column per thread");
+  const int64_t col_nc = n0 + tid < g.N ? n0 + tid : g.N - 1;
+  const float sb = g.sB[col_nc];
+  const int32_t zbl = g.zpB[col_nc];
+  const int32_t csl = g.colsum[col_nc];
+  const int32_t bl = (g.bias ? g.bias : g.zpB)[col_nc];
+  float bfl = 0.0f;
+  if constexpr (kF32) bfl = (g.bias_f ? g.bias_f : g.sB)[col_nc];
 
-  // ---- per-column epilogue constants (overlaps the first loads) ----
-  for (int j = tid; j < BN; j += NW * 64) {
+  const int nk = (int)(g.Kpad / BK);
+  // resident mode: B fragments of RU tiles in flight together
+  constexpr int RU = 4;
+  v4i bq[kResident ? RU : 1][FN];
+  // Tiles past the last one load the last tile's fragments and zero them,
+  // so the loads are unconditional and the extra MFMAs add nothing.
+  auto load_bq = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int64_t kb = (int64_t)min(kt0 + u, nk - 1) * (BK / 32);
+      const int keep = kt0 + u < nk ? -1 : 0;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+        bq[u][i] = *reinterpret_cast<const v4i*>(b_src[i] + kb * 1024) & keep;
+    }
+  };
+  if constexpr (kResident) {
+    // All K tiles of A into LDS stages 0..nk-1; slot s of a tile is filled
+    // by lane s%64 of wave (s/64)%NW, as the direct loads would fill it.
+    // A 16-byte chunk at any alignment is five aligned dwords (a dword with
+    // no byte of the chunk in range is read from the chunk's first dword,
+    // which holds one, so no read leaves a page the row lives in) shifted
+    // into place; bytes past K are masked to zero.  No load is conditional,
+    // so all of RU tiles' loads are in flight together.
+    if (kRowSum && tid < BM) row_sum[tid] = 0;
+    load_bq(0);
+    const uintptr_t a_safe = (uintptr_t)g.A & ~(uintptr_t)3;  // A[0,0] lies in this dword
+    for (int kt0 = 0; kt0 < nk; kt0 += RU) {
+      uint32_t dw[RU][IA][5];
+      int nv[RU][IA];
+      uint32_t sh[RU][IA];
+#pragma unroll
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+          const int sl = (j * NW + wave) * 64 + lane;
+          const int row = sl / CH, c = (sl % CH) ^ swz<BK>(sl / CH);
+          const int64_t gm = m0 + row;
+          const int64_t k0 = (int64_t)(kt0 + u) * BK + c * 16;
+          const bool in = gm < g.M && k0 < g.K;
+          const int64_t rem = g.K - k0;
+          nv[u][j] = in ? (int)(rem < 16 ? rem : 16) : 0;
+          const uintptr_t src = in ? (uintptr_t)(g.A + gm * g.lda + k0) : a_safe;
+          sh[u][j] = (uint32_t)(src & 3);
+          const uint32_t* base = reinterpret_cast<const uint32_t*>(src & ~(uintptr_t)3);
+#pragma unroll
+          for (int d = 0; d < 5; ++d)
+            dw[u][j][d] = base[4 * d < nv[u][j] + (int)sh[u][j] ? d : 0];
+        }
+      // the zeroed row sums are visible before the first adds (this waits
+      // for the loads above, which the adds need anyway)
+      if (kRowSum && kt0 == 0) __syncthreads();
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        if (kt0 + u >= nk) break;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+          const int sl = (j * NW + wave) * 64 + lane;
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int vq = nv[u][j] - 4 * q;  // bytes of word q inside K
+            const uint32_t keep = vq >= 4 ? 0xFFFFFFFFu : vq <= 0 ? 0u : (1u << (8 * vq)) - 1u;
+            w[q] = __builtin_amdgcn_alignbyte(dw[u][j][q + 1], dw[u][j][q], sh[u][j]) & keep;
+          }
+          *reinterpret_cast<uint4*>(smem + (int64_t)(kt0 + u) * STAGE + sl * 16) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+          if constexpr (kRowSum) {
+            int32_t rsum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rsum = __builtin_amdgcn_sdot4((int)w[q], 0x01010101, rsum, false);
+            if (rsum != 0) atomicAdd(&row_sum[sl / CH], rsum);
+          }
+        }
+      }
+    }
+  } else {
+    // prologue: A(0) .. A(SA-2) into the ring, B(0) into registers
+#pragma unroll
+    for (int p = 0; p < SA - 1; ++p)
+      if (p < nk)
+#pragma unroll
+        for (int j = 0; j < IA; ++j) issue_a(p, p, j);
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) load_b(0, sub);
+  }
+
+  // ---- per-column epilogue constants from the inputs loaded above ----
+  if (tid < BN) {
+    const int j = tid;
     const int64_t n = n0 + j;
     int32_t mm = 0, ss = 63, cc = 0, zb = 0;
     if (n < g.N) {
       if constexpr (kF32) {
         // f32 output: the columns hold the dequantization scale and the bias
-        mm = __builtin_bit_cast(int32_t, (float)((double)g.sA * (double)g.sB[n]));
-        ss = __builtin_bit_cast(int32_t, g.bias_f ? g.bias_f[n] : 0.0f);
+        mm = __builtin_bit_cast(int32_t, (float)((double)g.sA * (double)sb));
+        ss = __builtin_bit_cast(int32_t, g.bias_f ? bfl : 0.0f);
       } else {
-        derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
+        derive_mult(g.sA, sb, g.sOut, &mm, &ss);
       }
-      zb = g.zpB[n];
-      uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
-      c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
+      zb = zbl;
+      uint32_t c = (uint32_t)(g.bias ? bl : 0);
+      c -= (uint32_t)g.zA * (uint32_t)csl;
       c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
       cc = (int32_t)c;
     }
@@ -364,7 +463,26 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   wait_vmcnt<0>();
   __syncthreads();  // A(0) everywhere; epilogue constants visible
 
-  if constexpr (SUB == 1) {
+  if constexpr (kResident) {
+    // all of A is in LDS: no barriers; B arrives RU tiles at a time
+    for (int kt0 = 0; kt0 < nk; kt0 += RU) {
+      if (kt0 > 0) load_bq(kt0);
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) read_a(smem + min(kt0 + u, nk - 1) * STAGE, 0, j);
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int i = 0; i < FN; ++i) {
+            if constexpr (MF == 16)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bq[u][i], af[j], acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bq[u][i], af[j], acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+  } else if constexpr (SUB == 1) {
     // One K-step per tile (small tiles): barrier at the top of each tile.
     for (int kt = 0; kt < nk; ++kt) {
       if (kt > 0) {
@@ -424,7 +542,10 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
     int64_t m = m0 + wm * TM + j * MF + (lane % MF);
-    rs[j] = (kRowSum && m < g.M) ? g.rowsum[m] : 0;
+    if constexpr (kResident)
+      rs[j] = kRowSum ? row_sum[wm * TM + j * MF + (lane % MF)] : 0;
+    else
+      rs[j] = (kRowSum && m < g.M) ? g.rowsum[m] : 0;
   }
   // The clamp bounds in a VGPR let the clamp be one v_med3 (one scalar
   // operand per instruction).

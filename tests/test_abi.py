@@ -148,17 +148,43 @@ def test_gemm_rejects_overflow_and_bad_arguments(qp):
     _expect(qp, _gemm(qp, a, _info8(qp), wrong), qp.QP_EINVAL, "output shape")
     kstride = qp.qtensor(qp.QP_S8, [130, K], [1, 130], scale=0.02)
     _expect(qp, _gemm(qp, kstride, _info8(qp), out), qp.QP_EUNSUPPORTED, "K-contiguous")
-    # lda=129 forces the padded copy of A: a 0-byte workspace is too small
-    _expect(qp, _gemm(qp, a, _info8(qp), out, ws_bytes=0), qp.QP_ESIZE, "workspace")
+    # 256x256 tiles with lda = K = 1000 take the padded copy of A: a 0-byte
+    # workspace is too small
+    wide = qp.qtensor(qp.QP_S8, [4096, 1000], [1000, 1], scale=0.02, zero_point=3)
+    wout = qp.qtensor(qp.QP_S8, [4096, 4096], [4096, 1], scale=0.5, zero_point=-2)
+    _expect(qp, _gemm(qp, wide, _info8(qp, N=4096, K=1000), wout, ws_bytes=0), qp.QP_ESIZE,
+            "workspace")
+
+
+def test_gemm_workspace_plan(qp):
+    """64x64-tile GEMMs up to K = 960 need no workspace (direct loads, or
+    activations read byte-exact into LDS with their row sums); deeper or
+    larger ones with an odd stride size the padded copy and row sums."""
+    L = qp.lib()
+
+    def ws(M, K, N, lda, zp=0):
+        n = C.c_size_t()
+        a = qp.qtensor(qp.QP_S8, [M, K], [lda, 1])
+        assert L.qgemm_s8s8_requant_ws_size(C.byref(a), C.byref(_info8(qp, N=N, K=K, has_zp=zp)),
+                                            C.byref(n)) == 0
+        return n.value
+
+    assert ws(130, 129, 70, 129) == 0
+    assert ws(130, 129, 70, 129, zp=1) == 0
+    assert ws(1000, 960, 500, 961, zp=1) == 0
+    assert ws(1000, 961, 500, 961) == 1000 * 1024
+    assert ws(1000, 961, 500, 961, zp=1) == 1000 * 1024 + 4096
+    assert ws(4096, 1000, 4096, 1000) == 4096 * 1024
 
 
 def test_gemm_overflow_limit_is_inclusive(qp):
     # the largest allowed bound passes validation and fails only at the workspace check
-    K = 129
-    a = qp.qtensor(qp.QP_S8, [130, K], [K, 1], scale=0.02, zero_point=3)
-    out = qp.qtensor(qp.QP_S8, [130, 70], [70, 1], scale=0.5, zero_point=-2)
+    K = 1000
+    a = qp.qtensor(qp.QP_S8, [4096, K], [K, 1], scale=0.02, zero_point=3)
+    out = qp.qtensor(qp.QP_S8, [4096, 4096], [4096, 1], scale=0.5, zero_point=-2)
     limit = 2 ** 31 - 1 - K * 65025
-    _expect(qp, _gemm(qp, a, _info8(qp), out, C.c_void_p(FAKE), limit, ws_bytes=0), qp.QP_ESIZE)
+    _expect(qp, _gemm(qp, a, _info8(qp, N=4096, K=K), out, C.c_void_p(FAKE), limit, ws_bytes=0),
+            qp.QP_ESIZE)
 
 
 def test_a8w4_quantize_im2col_conv_reject_bad_arguments(qp):
