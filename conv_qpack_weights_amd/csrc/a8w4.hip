@@ -904,6 +904,171 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   }
 }
 
+// ---- GEMM for at most 16 rows and K <= 4096 --------------------------------
+// A workgroup of 8 waves covers 32 channels (two 16-channel tiles) and all
+// of K: wave w takes tile w%2 and K range w/2 (a quarter of the 128-K
+// blocks, at most BPW).  The 16 rows of activation codes go from memory
+// straight into LDS once per workgroup (rows padded by 16 bytes, so that
+// the 16 rows a read instruction touches fall in different banks); every
+// activation read after that is an LDS read.  Reading the codes from
+// memory in every wave instead (16 KiB per wave, the same lines in every
+// workgroup) measured slower than the whole weight stream.  Two tiles a
+// workgroup measured fastest of one, two and four (one: the codes are read
+// twice as often; four: a quarter of the CUs get no workgroup).
+// Each wave issues every weight and scale load of its range before it
+// waits for anything; it then waits only for the codes (issued first, so
+// complete first) and computes block by block as the weights arrive.  The
+// four K ranges of a tile are summed in a fixed order.  The arithmetic per
+// block is that of a8w4_gemm_kernel.
+template <int BPW, bool kPerm, int kKind>
+__global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
+    const int8_t* __restrict__ qa, int64_t lda, const float* __restrict__ sa_g,
+    const int32_t* __restrict__ za_g, int64_t M, W4 w, const float* __restrict__ bias, float lo,
+    float hi, float* __restrict__ Y, int64_t ldy) {
+  constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
+  constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
+  extern __shared__ __attribute__((aligned(16))) int8_t a_lds[];  // [16][Kpad + 16]
+  __shared__ float red[3][2][4][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tq = wave & 1;   // the wave's tile
+  const int ks = wave >> 1;  // and K range
+  const int c = lane >> 4;
+  const int64_t tile = (int64_t)blockIdx.x * 2 + tq;  // < Npad/16 (Npad: multiple of 64)
+  const int64_t nblocks = w.Kpad / 128;
+  const int64_t bpw = (nblocks + 3) / 4;
+  const int64_t b0 = ks * bpw;
+  const int64_t b_end = b0 + bpw < nblocks ? b0 + bpw : nblocks;
+  const int64_t astr = w.Kpad + 16;  // LDS row stride
+
+  // ---- the codes: 16 rows x Kpad bytes straight into LDS, in 1 KiB pieces
+  // (a piece: 64 lanes x 16 bytes of one row); wave w takes pieces
+  // w, w+8, ...  Rows past M repeat row M-1 (their outputs are not written).
+  const int ppr = (int)((w.Kpad + 1023) / 1024);  // pieces per row (<= 4)
+  for (int i = 0; i < 2 * ppr; ++i) {
+    const int pc = wave + 8 * i;
+    const int r = pc / ppr, j = pc - r * ppr;
+    const int64_t rr = r < M ? r : M - 1;
+    if (j * 1024 + lane * 16 < w.Kpad)
+      dma16_to_lds(qa, (lds_void_t*)((lds_i8*)a_lds + r * astr + j * 1024),
+                   (uint32_t)(rr * lda + j * 1024 + lane * 16), 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the codes' loads first
+
+  // ---- every weight and scale load of the range (blocks past the range
+  // read the range's last real block and get zero scales below)
+  const int8_t* const wp =
+      reinterpret_cast<const int8_t*>(w.data) + tile * w.nblk * 1024 + (lane & 15) * 64 + 16 * c;
+  const uint8_t* const sp = w.scale + (tile * w.nblk * 64 + (lane & 15) * 4) * ES;
+  const uint8_t* const op = kAsym ? w.offs + (tile * w.nblk * 64 + (lane & 15) * 4) * 4 : nullptr;
+  uint4 wr[BPW];
+  float4 sr[BPW], orr[kAsym ? BPW : 1];
+#pragma unroll
+  for (int u = 0; u < BPW; ++u) {
+    const int64_t b = b0 + u < nblocks ? b0 + u : nblocks - 1;
+    wr[u] = *reinterpret_cast<const uint4*>(wp + b * 1024);
+    sr[u] = load_scale4<kBf16>(sp + 64 * ES * b);
+    if constexpr (kAsym) orr[u] = load_scale4<false>(op + 256 * b);
+  }
+  // the codes (issued first, so complete first) are in LDS once no more
+  // than the weight loads are outstanding
+  wait_vmcnt<kAsym ? 3 * BPW : 2 * BPW>();
+  __syncthreads();
+
+  float acc[2][4];
+  double accd[kAsym ? 4 : 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[0][i] = acc[1][i] = 0.0f;
+    if constexpr (kAsym) accd[i] = 0.0;
+  }
+  const int8_t* const arow = a_lds + (lane & 15) * astr;
+#pragma unroll
+  for (int u = 0; u < BPW; ++u) {
+    const int64_t b = b0 + u < nblocks ? b0 + u : nblocks - 1;
+    uint2 ar[4];
+    const int8_t* ab = arow + b * 128;
+    if constexpr (kPerm) {  // the 32 bytes of chunk c's four pieces are contiguous
+      const uint4 p0 = *reinterpret_cast<const uint4*>(ab + 32 * c);
+      const uint4 p1 = *reinterpret_cast<const uint4*>(ab + 32 * c + 16);
+      ar[0] = make_uint2(p0.x, p0.y);
+      ar[1] = make_uint2(p0.z, p0.w);
+      ar[2] = make_uint2(p1.x, p1.y);
+      ar[3] = make_uint2(p1.z, p1.w);
+    } else {  // piece t of chunk c: bytes 32t + 8c
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ar[t] = *reinterpret_cast<const uint2*>(ab + 32 * t + 8 * c);
+    }
+    // a block outside the range contributes 0 * (finite dot) = 0
+    const float keep = b0 + u < b_end ? 1.0f : 0.0f;
+    const float4 cs = make_float4(sr[u].x * keep, sr[u].y * keep, sr[u].z * keep, sr[u].w * keep);
+    float4 co = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (kAsym)
+      co = make_float4(orr[u].x * keep, orr[u].y * keep, orr[u].z * keep, orr[u].w * keep);
+#pragma unroll
+    for (int t2 = 0; t2 < 4; t2 += 2) {
+      v4i d[2], e[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = t2 + h;
+        const uint32_t wd = t == 0 ? wr[u].x : (t == 1 ? wr[u].y : (t == 2 ? wr[u].z : wr[u].w));
+        const long bop = (long)(((uint64_t)nib_hi16(wd) << 32) | nib_lo16(wd));
+        const long aop = (long)(((uint64_t)ar[t].y << 32) | ar[t].x);
+        d[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, v4i{0, 0, 0, 0}, 0, 0, 0);
+        if constexpr (kAsym)
+          e[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, (long)0x1010101010101010LL,
+                                                       v4i{0, 0, 0, 0}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = t2 + h;
+        const float sc = t == 0 ? cs.x : (t == 1 ? cs.y : (t == 2 ? cs.z : cs.w));
+        if constexpr (kAsym) {
+          const float oc = t == 0 ? co.x : (t == 1 ? co.y : (t == 2 ? co.z : co.w));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[h][i] = acc[h][i] + __builtin_fmaf(oc, (float)e[h][i], sc * (float)d[h][i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[h][i] = __builtin_fmaf(sc, (float)d[h][i], acc[h][i]);
+        }
+      }
+    }
+    if constexpr (kAsym) {  // the block's sum into the f64 one
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accd[i] = accd[i] + (double)(acc[0][i] + acc[1][i]);
+        acc[0][i] = acc[1][i] = 0.0f;
+      }
+    }
+  }
+  float out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = kAsym ? (float)accd[kAsym ? i : 0] : acc[0][i] + acc[1][i];
+
+  // ---- the four K ranges of each tile, summed in a fixed order
+  if (ks > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[ks - 1][tq][i][lane] = out[i];
+  }
+  __syncthreads();
+  if (ks != 0) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 3; ++r) out[i] = out[i] + red[r][tq][i][lane];
+  const int64_t n = tile * 16 + (lane & 15);
+  if (n >= w.N) return;
+  const float ws = w.wsum[n];
+  const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = 4 * c + i;
+    if (m < M) Y[m * ldy + n] = finish(out[i], sa_g[m], za_g[m], ws, bn, lo, hi);
+  }
+}
+
 W4 w4_of(const qp_packed_info* b, const void* blob) {
   const uint8_t* p = static_cast<const uint8_t*>(blob);
   return W4{p + b->data_off, p + b->scale_off, reinterpret_cast<const float*>(p + b->sum_off),
@@ -1010,12 +1175,62 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   return check_launch("a8w4 gemm");
 }
 
+template <int BPW, bool kPerm, int kKind>
+qp_status launch_gemm_m16_one(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
+                              int64_t M, const W4& w, const float* bias, float lo, float hi,
+                              float* Y, int64_t ldy, hipStream_t stream) {
+  auto kern = a8w4_gemm_m16_kernel<BPW, kPerm, kKind>;
+  // The LDS limit is raised once per instantiation and device, for the
+  // deepest K the instantiation takes (threads may race to set it;
+  // repeating it is harmless).
+  constexpr int kLdsMax = 16 * (BPW * 4 * 128 + 16);
+  static std::atomic<uint64_t> lds_attr_devices{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) QP_FAIL(QP_EHIP, "a8w4: hipGetDevice failed");
+  const uint64_t bit = dev >= 0 && dev < 64 ? (UINT64_C(1) << dev) : 0;
+  if (bit == 0 || (lds_attr_devices.load(std::memory_order_acquire) & bit) == 0) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
+      QP_FAIL(QP_EHIP, "a8w4: cannot reserve %d bytes of LDS", kLdsMax);
+    lds_attr_devices.fetch_or(bit, std::memory_order_release);
+  }
+  const size_t lds = (size_t)16 * (w.Kpad + 16);
+  hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(w.N, 32)), dim3(512), lds, stream, qa, lda,
+                     sa, za, M, w, bias, lo, hi, Y, ldy);
+  return check_launch("a8w4 gemm (up to 16 rows)");
+}
+
+template <int BPW>
+qp_status launch_gemm_m16(const int8_t* qa, int64_t lda, bool perm, const float* sa,
+                          const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
+                          float hi, float* Y, int64_t ldy, hipStream_t stream) {
+#define QP_M16(PERM, KIND) \
+  return launch_gemm_m16_one<BPW, PERM, KIND>(qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, stream)
+  if (perm) {
+    if (w.kind == 1) QP_M16(true, 1);
+    if (w.kind == 2) QP_M16(true, 2);
+    QP_M16(true, 0);
+  }
+  if (w.kind == 1) QP_M16(false, 1);
+  if (w.kind == 2) QP_M16(false, 2);
+  QP_M16(false, 0);
+#undef QP_M16
+}
+
 // perm: the activations are permuted inside each 128-K block (as written by
 // the fused quantization); otherwise plain row-major.  ldsz > 0: sa, za are
 // per-block parameters [M][ldsz] (row-major activations).
 qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                       const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
                       float hi, float* Y, int64_t ldy, hipStream_t stream, int64_t ldsz = 0) {
+  // Up to 16 rows and 32 blocks of K: every load of a wave at once.
+  const int64_t nblocks = w.Kpad / 128;
+  if (M <= 16 && ldsz == 0 && nblocks <= 32) {
+    const int64_t bpw = (nblocks + 3) / 4;
+    if (bpw <= 2) return launch_gemm_m16<2>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, stream);
+    if (bpw <= 4) return launch_gemm_m16<4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, stream);
+    return launch_gemm_m16<8>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, stream);
+  }
   // <FM, FN, RW, CW, KS>: rows per workgroup 16*FM*RW, channels 16*FN*CW.
   // Small M splits K over the waves (enough waves stream the weights); larger
   // M shares each staged activation row among several channel groups.
