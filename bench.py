@@ -43,8 +43,11 @@ def _args():
                    help="only run a plain device copy of COPY_BYTES (to scale the FETCH_SIZE / "
                         "WRITE_SIZE counters) and exit")
     p.add_argument("--a8w4-only", type=int, default=0, metavar="M",
-                   help="only run the A8W4 path (per-row quantization + GEMM) on M x 11008 x "
+                   help="only run the A8W4 path (per-row quantization + GEMM) on M x N x "
                         "4096 five times and exit (for counter runs)")
+    p.add_argument("--a8w4-n", type=int, default=11008, metavar="N",
+                   help="output channels of the --a8w4-only run (11008; 4096 for the GEMV "
+                        "workload)")
     return p.parse_args()
 
 
@@ -131,17 +134,18 @@ def main():
 
     if a.a8w4_only > 0:
         Mo = a.a8w4_only
-        go = synth.a8w4(synth.BASE_SEED + 3, Mo, 11008, 4096)
+        No = a.a8w4_n
+        go = synth.a8w4(synth.BASE_SEED + 3, Mo, No, 4096)
         bo, io = qp.pack_s4(torch.from_numpy(go["W"]).to(dev), torch.from_numpy(go["sw"]).to(dev))
         Xo = torch.from_numpy(go["X"]).to(dev)
         bias_o = torch.from_numpy(go["bias"]).to(dev)
-        Yo = torch.empty((Mo, 11008), dtype=torch.float32, device=dev)
+        Yo = torch.empty((Mo, No), dtype=torch.float32, device=dev)
         wso = torch.empty(max(qp.qgemm_a8w4_blockwise_f32_ws_size(Mo, io), 256),
                           dtype=torch.uint8, device=dev)
         for _ in range(5):
             qp.qgemm_a8w4_blockwise_f32(Xo, bo, io, bias_o, -6.0, 6.0, out=Yo, ws=wso)
         torch.cuda.synchronize()
-        print(json.dumps({"a8w4_only_M": Mo, "launches": 5}))
+        print(json.dumps({"a8w4_only_M": Mo, "N": No, "launches": 5}))
         return
 
     def d(x):

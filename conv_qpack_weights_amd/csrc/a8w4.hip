@@ -502,7 +502,11 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const int8_t* __restrict_
 // holds channels 4*(l/16)+i of row l%16 and needs one row's group
 // parameters; a second MFMA against the row's zero point replicated over K
 // gives za*sum q, and each group adds sa*sw * (d - that) per output.
-template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind, bool kBQ = false>
+// PW: weight prefetch depth in blocks.  kExact: every K range holds a
+// multiple of PW blocks (the host checks), so no step runs past its range
+// and the per-step range test and zeroed scales drop out.
+template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind, bool kBQ = false,
+          int PW = 3, bool kExact = false>
 __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict__ qa,
                                                         int64_t lda, const float* __restrict__ sa_g,
                                                         const int32_t* __restrict__ za_g,
@@ -512,9 +516,8 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
                                                         int64_t ldy, int64_t ldsz) {
   static_assert(!kBQ || kKind != 2, "per-block activations take symmetric weights");
   static_assert(RW * CW * KS == 4, "four waves");
-  // weight prefetch depth in blocks (kBQ holds more per block: two); a
-  // deeper ring measured slower (more registers, lower occupancy)
-  constexpr int P = kBQ ? 2 : 3;
+  // weight prefetch depth in blocks (kBQ holds more per block: two)
+  constexpr int P = kBQ ? 2 : PW;
   constexpr int R = 4;                      // activation ring stages
   constexpr int MT = 16 * FM * RW;          // rows per workgroup
   constexpr int SLOTS = KS * MT * 8;        // 16-byte pieces per stage
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     }
     uint4 cw4[FN];
     float4 cs[FN], co[FN];
-    const bool live = ks * bpw + j < my_end;
+    const bool live = kExact || ks * bpw + j < my_end;
     if constexpr (kBQ) {
       // per output (channel 4c+i, row): sa[row, g] * sw[channel, g], with
       // the row scales zeroed past the end of the K range
@@ -1143,7 +1146,7 @@ qp_status launch_gemv_bq(const int8_t* qa, const float* sa, const int32_t* za, c
   return check_launch("a8w4 gemv (per-block activations)");
 }
 
-template <int FM, int FN, int RW, int CW, int KS>
+template <int FM, int FN, int RW, int CW, int KS, int PW = 3, bool kExact = false>
 qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                           const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
                           float hi, float* Y, int64_t ldy, int64_t ldsz, hipStream_t stream) {
@@ -1153,7 +1156,8 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w4: M too large");
   const dim3 grid(bx, (unsigned)by);
 #define QP_GEMM(PERM, KIND)                                                                \
-  hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, PERM, KIND>), grid, dim3(256), 0, \
+  hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, PERM, KIND, false, PW, kExact>), grid, \
+                     dim3(256), 0, \
                      stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, (int64_t)0)
 #define QP_GEMM_BQ(KIND)                                                                      \
   hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, KIND, true>), grid, dim3(256), \
@@ -1244,6 +1248,10 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   // 64 rows x 32 channels a workgroup (two row and two channel groups):
   // measured faster than 64 x 64 with four channel groups, whose 256-VGPR
   // waves fit two a SIMD
+  // K a multiple of four blocks: four blocks in flight and no range tests
+  if (nblocks % 4 == 0)
+    return launch_gemm_cfg<2, 1, 2, 2, 1, 4, true>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y,
+                                                   ldy, ldsz, stream);
   return launch_gemm_cfg<2, 1, 2, 2, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
                                         stream);
 }
