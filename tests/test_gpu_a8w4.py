@@ -62,7 +62,8 @@ def test_a8w4_gemm_workload(qp, orc, M):
                                    (5, 77, 1000), (17, 100, 256), (40, 33, 64), (1, 4096, 33),
                                    (33, 48, 160), (65, 40, 256), (130, 48, 320),
                                    (1, 40, 32768), (1, 37, 40000), (7, 50, 1500),
-                                   (16, 64, 2048), (12, 200, 3000), (4, 40, 5000)])
+                                   (16, 64, 2048), (12, 200, 3000), (4, 40, 5000),
+                                   (48, 96, 512), (100, 33, 1536), (128, 64, 1024)])
 def test_a8w4_small_shapes_and_tails(qp, orc, M, N, K):
     _case(qp, orc, synth.a8w4(synth.BASE_SEED + 7 * M + N + K, M, N, K))
 
@@ -134,7 +135,8 @@ def test_a8w4_bf16_scales_gemm_workload(qp, orc, M):
 @pytest.mark.parametrize("M,N,K,prequant", [(1, 70, 96, False), (3, 64, 4096, True),
                                             (5, 77, 1000, False), (33, 48, 160, True),
                                             (130, 48, 320, False), (9, 40, 1800, True),
-                                            (14, 33, 2500, False)])
+                                            (14, 33, 2500, False), (64, 40, 1024, False),
+                                            (33, 70, 512, True)])
 def test_a8w4_bf16_scales_shapes(qp, orc, M, N, K, prequant):
     _case_bf16(qp, orc, synth.a8w4(synth.BASE_SEED + 11 * M + N + K, M, N, K), prequant=prequant)
 
@@ -185,7 +187,8 @@ def test_a8w4_asym_gemm_workload(qp, orc, M):
                                             (3, 64, 4096, True), (5, 77, 1000, False),
                                             (33, 48, 160, True), (40, 33, 64, False),
                                             (130, 48, 320, False), (9, 40, 1800, True),
-                                            (14, 33, 2500, False)])
+                                            (14, 33, 2500, False), (64, 40, 1024, False),
+                                            (33, 70, 512, True)])
 def test_a8w4_asym_shapes(qp, orc, M, N, K, prequant):
     d = synth.a8w4(synth.BASE_SEED + 13 * M + N + K, M, N, K)
     _case_asym(qp, orc, d, _offsets(d, M + N + K), prequant=prequant)
