@@ -503,7 +503,7 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const int8_t* __restrict_
 // parameters; a second MFMA against the row's zero point replicated over K
 // gives za*sum q, and each group adds sa*sw * (d - that) per output.
 // PW: weight prefetch depth in blocks.  kExact: every K range holds a
-// multiple of PW blocks (the host checks), so no step runs past its range
+// multiple of 2*PW blocks (the host checks), so no step runs past its range
 // and the per-step range test and zeroed scales drop out.
 template <int FM, int FN, int RW, int CW, int KS, bool kPerm, int kKind, bool kBQ = false,
           int PW = 3, bool kExact = false>
@@ -541,18 +541,20 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   const int c = lane >> 4;
   const int64_t n0 = ((int64_t)blockIdx.x * CW + cw) * 16 * FN;  // n0 + 16*FN <= Npad
   const int64_t mw = (int64_t)blockIdx.y * MT;                    // workgroup's first row
-  const int64_t nblocks = w.Kpad / 128;
-  const int64_t bpw = (nblocks + KS - 1) / KS;  // blocks per K range
+  // (block indices in 32 bits, wave-uniform: the clamps below are scalar
+  // compares; the host keeps Kpad <= 2^24)
+  const int nblocks = (int)(w.Kpad / 128);
+  const int bpw = (nblocks + KS - 1) / KS;  // blocks per K range
   // every K range runs bpw steps; steps past its end are clamped to its last
   // block and contribute with zero scales
-  auto range_block = [&](int r, int64_t j) {
-    const int64_t b_begin = r * bpw;
-    int64_t last = (b_begin + bpw < nblocks ? b_begin + bpw : nblocks) - 1;
+  auto range_block = [&](int r, int j) {
+    const int b_begin = r * bpw;
+    int last = (b_begin + bpw < nblocks ? b_begin + bpw : nblocks) - 1;
     if (last < b_begin) last = nblocks - 1;  // empty range: park on a real block
-    const int64_t b = b_begin + j;
-    return b < last ? b : last;
+    const int b = b_begin + j;
+    return (int64_t)(b < last ? b : last);
   };
-  const int64_t my_end = (ks * bpw + bpw < nblocks ? ks * bpw + bpw : nblocks);
+  const int my_end = (ks * bpw + bpw < nblocks ? ks * bpw + bpw : nblocks);
 
   // ---- weight/scale sources (tile-contiguous blob) ----
   constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
@@ -590,13 +592,15 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   for (int i = 0; i < ND; ++i) {
     const int s = kPrivA ? wave * (MT * 8) + 64 * i + lane : tid + 256 * i;
     const int r = (s >> 3) % MT;
-    a_rng[i] = kPrivA ? wave : (32 * i + 8 * wave) / MT;  // == (s >> 3) / MT
+    // (wave-uniform: kept in a scalar register, so the range clamps of the
+    // direct loads are scalar compares)
+    a_rng[i] = __builtin_amdgcn_readfirstlane(kPrivA ? wave : (32 * i + 8 * wave) / MT);
     const int p = (s & 7) ^ ((r >> 1) & 7);
     int64_t m = mw + r;
     m = m < M ? m : M - 1;
     a_voff[i] = (uint32_t)((m - mw) * lda + 16 * p);
   }
-  auto issue_stage = [&](int64_t j) {
+  auto issue_stage = [&](int j) {
     lds_i8* st = (lds_i8*)ring + (int)(j % R) * STAGE;
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -625,8 +629,12 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[h][f][q][i] = 0.0f;
 
-  uint4 wr[P][FN];
-  float4 sr[P][FN], orr[P][FN];
+  // The weight ring holds PR = 2P slots when K ranges are exact: step u
+  // consumes slot u and refills slot (u + P) % PR, which nothing reads any
+  // more, so the refill needs no register copies at the loop's back edge.
+  constexpr int PR = (kExact && !kBQ) ? 2 * P : P;
+  uint4 wr[PR][FN];
+  float4 sr[PR][FN], orr[PR][FN];
   float4 sr4[kBQ ? P : 1][FN][4];     // kBQ: [channel 4c+i] x 4 groups
   float4 sar[kBQ ? P : 1][FM];        // kBQ: the row's 4 group scales
   int4 zar[kBQ ? P : 1][FM];          //      and zero points
@@ -653,7 +661,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   };
 
   // one block: activation operands from the stage, MFMAs, refill, rescale
-  auto step = [&](int u, int64_t j) {
+  auto step = [&](int u, int j) {
     const lds_i8* st = (const lds_i8*)ring + (int)(j % R) * STAGE + ks * MT * 128;
     uint2 ca[FM][4];
 #pragma unroll
@@ -746,7 +754,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       cs[q] = live ? sr[u][q] : make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (kAsym) co[q] = live ? orr[u][q] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    load_w(u, range_block(ks, j + P));
+    load_w((u + P) % PR, range_block(ks, j + P));
 #pragma unroll
     for (int t2 = 0; t2 < 4; t2 += 2) {
       v4i d[2][FM][FN];
@@ -827,11 +835,11 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   constexpr int LW = kBQ ? 5 * FN + 2 * FM : (kAsym ? 3 * FN : 2 * FN);
   constexpr int A_WAIT = LW + (R - 2) * (ND + LW);
   static_assert(A_WAIT < 64, "vmcnt range");
-  // The step loop is unrolled by P so the weight ring index is static.
-  for (int64_t j0 = 0; j0 < bpw; j0 += P) {
+  // The step loop is unrolled by PR so the weight ring index is static.
+  for (int j0 = 0; j0 < bpw; j0 += PR) {
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int64_t j = j0 + u;
+    for (int u = 0; u < PR; ++u) {
+      const int j = j0 + u;
       // (past the last step the body still runs, with zero scales, so that
       // every iteration issues the same loads)
       wait_vmcnt<A_WAIT>();
@@ -1248,8 +1256,8 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   // 64 rows x 32 channels a workgroup (two row and two channel groups):
   // measured faster than 64 x 64 with four channel groups, whose 256-VGPR
   // waves fit two a SIMD
-  // K a multiple of four blocks: four blocks in flight and no range tests
-  if (nblocks % 4 == 0)
+  // K a multiple of eight blocks: four blocks in flight and no range tests
+  if (nblocks % 8 == 0)
     return launch_gemm_cfg<2, 1, 2, 2, 1, 4, true>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y,
                                                    ldy, ldsz, stream);
   return launch_gemm_cfg<2, 1, 2, 2, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
