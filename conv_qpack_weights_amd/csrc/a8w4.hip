@@ -931,7 +931,9 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 // complete first) and computes block by block as the weights arrive.  The
 // four K ranges of a tile are summed in a fixed order.  The arithmetic per
 // block is that of a8w4_gemm_kernel.
-template <int BPW, bool kPerm, int kKind>
+// kExact: K is exactly four ranges of BPW blocks, so every block of every
+// range is real and the scales need no zeroing.
+template <int BPW, bool kPerm, int kKind, bool kExact = false>
 __global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
     const int8_t* __restrict__ qa, int64_t lda, const float* __restrict__ sa_g,
     const int32_t* __restrict__ za_g, int64_t M, W4 w, const float* __restrict__ bias, float lo,
@@ -1012,11 +1014,14 @@ __global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
       for (int t = 0; t < 4; ++t) ar[t] = *reinterpret_cast<const uint2*>(ab + 32 * t + 8 * c);
     }
     // a block outside the range contributes 0 * (finite dot) = 0
-    const float keep = b0 + u < b_end ? 1.0f : 0.0f;
-    const float4 cs = make_float4(sr[u].x * keep, sr[u].y * keep, sr[u].z * keep, sr[u].w * keep);
+    float4 cs = sr[u];
     float4 co = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (kAsym)
-      co = make_float4(orr[u].x * keep, orr[u].y * keep, orr[u].z * keep, orr[u].w * keep);
+    if constexpr (kAsym) co = orr[u];
+    if constexpr (!kExact) {
+      const float keep = b0 + u < b_end ? 1.0f : 0.0f;
+      cs = make_float4(cs.x * keep, cs.y * keep, cs.z * keep, cs.w * keep);
+      if constexpr (kAsym) co = make_float4(co.x * keep, co.y * keep, co.z * keep, co.w * keep);
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 4; t2 += 2) {
       v4i d[2], e[2];
@@ -1187,11 +1192,11 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   return check_launch("a8w4 gemm");
 }
 
-template <int BPW, bool kPerm, int kKind>
+template <int BPW, bool kPerm, int kKind, bool kExact>
 qp_status launch_gemm_m16_one(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
                               int64_t M, const W4& w, const float* bias, float lo, float hi,
                               float* Y, int64_t ldy, hipStream_t stream) {
-  auto kern = a8w4_gemm_m16_kernel<BPW, kPerm, kKind>;
+  auto kern = a8w4_gemm_m16_kernel<BPW, kPerm, kKind, kExact>;
   // The LDS limit is raised once per instantiation and device, for the
   // deepest K the instantiation takes (threads may race to set it;
   // repeating it is harmless).
@@ -1216,8 +1221,12 @@ template <int BPW>
 qp_status launch_gemm_m16(const int8_t* qa, int64_t lda, bool perm, const float* sa,
                           const int32_t* za, int64_t M, const W4& w, const float* bias, float lo,
                           float hi, float* Y, int64_t ldy, hipStream_t stream) {
-#define QP_M16(PERM, KIND) \
-  return launch_gemm_m16_one<BPW, PERM, KIND>(qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, stream)
+  const bool exact = BPW == 8 && w.nblk == 4 * BPW;
+#define QP_M16(PERM, KIND)                                                                       \
+  return exact ? launch_gemm_m16_one<BPW, PERM, KIND, BPW == 8>(qa, lda, sa, za, M, w, bias, lo,  \
+                                                                hi, Y, ldy, stream)              \
+               : launch_gemm_m16_one<BPW, PERM, KIND, false>(qa, lda, sa, za, M, w, bias, lo, hi, \
+                                                             Y, ldy, stream)
   if (perm) {
     if (w.kind == 1) QP_M16(true, 1);
     if (w.kind == 2) QP_M16(true, 2);
