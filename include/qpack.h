@@ -309,7 +309,12 @@ qp_status qquantize_rows_s8_blocked(const float* x, int64_t M, int64_t K, int64_
  *   out      QP_S8 or QP_S32 [M,N], stride (ldc, 1); scale/zero_point used
  *            for int8; qmin/qmax must be -128/127 for int8.
  *   ws, ws_bytes  device workspace of qgemm_s8s8_requant_ws_size bytes
- *            (may be 0: then ws may be NULL).
+ *            (may be 0: then ws may be NULL).  The size is 0 for GEMMs on
+ *            64x64 tiles (fewer than 256 tiles of 128x128) with Kpad <= 960:
+ *            their activations are read byte-exact at any stride and
+ *            alignment.  Other GEMMs need it when K != Kpad, when the rows
+ *            are not 16-byte aligned, or when the weights carry zero points
+ *            (a padded copy of A and/or its row sums).
  *   max_abs_bias  host upper bound of |bias[n]| (>= 0; ignored when
  *            bias_dev is NULL).  The bias lives on the device, so the INT32
  *            check of [NPU] section 4 uses this bound: K*65025 + max_abs_bias
