@@ -1265,11 +1265,13 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   // 64 rows x 32 channels a workgroup (two row and two channel groups):
   // measured faster than 64 x 64 with four channel groups, whose 256-VGPR
   // waves fit two a SIMD
-  // K a multiple of eight blocks: four blocks in flight and no range tests,
-  // 32 rows x 64 channels a workgroup (one row group, four channel groups:
-  // half the staged activation bytes of 64 x 32; measured 7% faster)
-  if (nblocks % 8 == 0)
-    return launch_gemm_cfg<2, 1, 1, 4, 1, 4, true>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y,
+  // K a multiple of four blocks: no range tests, two weight blocks in flight
+  // in a four-slot ring (fewer registers, more resident waves: measured
+  // faster than four or eight in flight), 32 rows x 64 channels a workgroup
+  // (one row group, four channel groups: half the staged activation bytes
+  // of 64 x 32, measured 7% faster)
+  if (nblocks % 4 == 0)
+    return launch_gemm_cfg<2, 1, 1, 4, 1, 2, true>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y,
                                                    ldy, ldsz, stream);
   return launch_gemm_cfg<2, 1, 2, 2, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz,
                                         stream);
