@@ -539,8 +539,16 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   const int rw = wave / (KS * CW);
   const int slot = rw * CW + cw;
   const int c = lane >> 4;
-  const int64_t n0 = ((int64_t)blockIdx.x * CW + cw) * 16 * FN;  // n0 + 16*FN <= Npad
-  const int64_t mw = (int64_t)blockIdx.y * MT;                    // workgroup's first row
+  // Workgroups are dispatched round-robin over the 8 XCDs in launch order
+  // (x fastest).  Remapped so that each XCD takes a contiguous run of
+  // (channel group, row group) pairs, row groups fastest: the row groups of
+  // one channel group then share their weight tiles through one L2.
+  const uint32_t gx = gridDim.x, gy = gridDim.y;
+  uint32_t lin = blockIdx.y * gx + blockIdx.x;
+  if (gy > 1 && ((gx * gy) & 7) == 0) lin = (lin & 7) * ((gx * gy) >> 3) + (lin >> 3);
+  const uint32_t cgi = gy > 1 ? lin / gy : blockIdx.x, rgi = gy > 1 ? lin % gy : blockIdx.y;
+  const int64_t n0 = ((int64_t)cgi * CW + cw) * 16 * FN;  // n0 + 16*FN <= Npad
+  const int64_t mw = (int64_t)rgi * MT;                    // workgroup's first row
   // (block indices in 32 bits, wave-uniform: the clamps below are scalar
   // compares; the host keeps Kpad <= 2^24)
   const int nblocks = (int)(w.Kpad / 128);
