@@ -63,7 +63,7 @@ def test_a8w4_gemm_repeats_bitwise(qp, M):
 
 
 def test_a8w4_rows_agree_across_configurations(qp):
-    """Rows 0..15 of an M = 128 call (64x32 workgroups) and the same rows as
+    """Rows 0..15 of an M = 128 call (32-row x 64-channel workgroups) and the same rows as
     an M = 16 call (K split over the waves) agree to the f32 tolerance."""
     print("geometry: A8W4 M=128 vs M=16", flush=True)
     a = synth.a8w4(synth.BASE_SEED + 52, 128, 1024, 4096)
