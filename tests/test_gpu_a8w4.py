@@ -63,7 +63,12 @@ def test_a8w4_gemm_workload(qp, orc, M):
                                    (33, 48, 160), (65, 40, 256), (130, 48, 320),
                                    (1, 40, 32768), (1, 37, 40000), (7, 50, 1500),
                                    (16, 64, 2048), (12, 200, 3000), (4, 40, 5000),
-                                   (48, 96, 512), (100, 33, 1536), (128, 64, 1024)])
+                                   (48, 96, 512), (100, 33, 1536), (128, 64, 1024),
+                                   # K exactly four ranges of eight blocks at a ragged N;
+                                   # grids whose workgroups are placed by XCD (row groups
+                                   # of a channel group together), exact and ragged K
+                                   (16, 40, 4096), (60, 250, 512), (100, 330, 512),
+                                   (100, 250, 640)])
 def test_a8w4_small_shapes_and_tails(qp, orc, M, N, K):
     _case(qp, orc, synth.a8w4(synth.BASE_SEED + 7 * M + N + K, M, N, K))
 
@@ -136,7 +141,8 @@ def test_a8w4_bf16_scales_gemm_workload(qp, orc, M):
                                             (5, 77, 1000, False), (33, 48, 160, True),
                                             (130, 48, 320, False), (9, 40, 1800, True),
                                             (14, 33, 2500, False), (64, 40, 1024, False),
-                                            (33, 70, 512, True)])
+                                            (33, 70, 512, True), (60, 250, 512, True),
+                                            (100, 250, 640, False)])
 def test_a8w4_bf16_scales_shapes(qp, orc, M, N, K, prequant):
     _case_bf16(qp, orc, synth.a8w4(synth.BASE_SEED + 11 * M + N + K, M, N, K), prequant=prequant)
 
@@ -188,7 +194,8 @@ def test_a8w4_asym_gemm_workload(qp, orc, M):
                                             (33, 48, 160, True), (40, 33, 64, False),
                                             (130, 48, 320, False), (9, 40, 1800, True),
                                             (14, 33, 2500, False), (64, 40, 1024, False),
-                                            (33, 70, 512, True)])
+                                            (33, 70, 512, True), (100, 330, 512, False),
+                                            (16, 40, 4096, True)])
 def test_a8w4_asym_shapes(qp, orc, M, N, K, prequant):
     d = synth.a8w4(synth.BASE_SEED + 13 * M + N + K, M, N, K)
     _case_asym(qp, orc, d, _offsets(d, M + N + K), prequant=prequant)
