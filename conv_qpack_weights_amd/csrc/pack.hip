@@ -412,7 +412,6 @@ extern "C" qp_status qpack_weights(const qp_qtensor* w, const void* w_dev, int32
     g.has_zero_points = 0;
   } else {
     QP_REQUIRE(w->scales != nullptr, QP_EINVAL, "blockwise weights need a scales array");
-    QP_REQUIRE(g.Kpad <= 65536, QP_EUNSUPPORTED, "int4 packing supports K <= 65536");
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, stream, h, blob);
     if ((st = check_launch("qpack_weights header"))) return st;
     size_t lds = sizeof(int32_t) * (size_t)(g.Kpad / 32);

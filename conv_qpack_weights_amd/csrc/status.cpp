@@ -50,6 +50,11 @@ qp_status blob_geometry(int32_t format, int32_t scheme, int64_t N, int64_t K, in
                (long long)group);
     g.group = group;
     g.Kpad = round_up(K, group > kBlockK4 ? group : kBlockK4);
+    // the int4 packer keeps a row's group sums in LDS, and the int4 product
+    // kernels count 128-K blocks in 32 bits: a blob restored from bytes is
+    // held to the same limit as one packed here
+    QP_REQUIRE(g.Kpad <= 65536, QP_EUNSUPPORTED, "int4 weights support K <= 65536 (Kpad %lld)",
+               (long long)g.Kpad);
     g.data_bytes = g.Npad * g.Kpad / 2;
     g.scale_off = g.data_off + round_up(g.data_bytes, kRegionAlign);
     // scales in quads of 4 groups: [Npad/16][ceil(G/4)][16][4] of f32

@@ -145,7 +145,9 @@ const char* qp_last_error(void);
  *           OIHW convolution weights with n_axis = 0, k_axis = 1 (then
  *           K = KH*KW*IC in (kh, kw, ic) order, the order of [MNN]
  *           reorderWeight).  dtype QP_S8 (per-tensor or per-channel) or
- *           QP_S4 (QP_BLOCKWISE, group_size a multiple of 32).
+ *           QP_S4 (QP_BLOCKWISE, group_size a multiple of 32, K <= 65536
+ *           after padding, else QP_EUNSUPPORTED; a restored int4 header is
+ *           held to the same limit).
  *   bytes   out: blob size.      align  out: required alignment (256).
  */
 qp_status qpack_weights_size(const qp_qtensor* w, int32_t k_axis, int32_t n_axis,

@@ -85,6 +85,11 @@ def test_header_parser_reads_the_reference_blob(qp, orc):
     bad[0] ^= 0xFF
     with pytest.raises(qp.QPackError):
         qp.qp_packed_info_from_header(bytes(bad))
+    # an int4 blob deeper than the packer accepts is refused on restore too
+    deep = orc.pack_s4_ref(rng.integers(-8, 8, (1, 65537)).astype(np.int8),
+                           np.ones((1, 2049), np.float32))
+    with pytest.raises(qp.QPackError, match="65536"):
+        qp.qp_packed_info_from_header(deep[:256].tobytes())
 
 
 def test_pack_rejects_bad_descriptors(qp):
@@ -102,6 +107,9 @@ def test_pack_rejects_bad_descriptors(qp):
                     zero_point=3)
     _expect(qp, L.qpack_weights_size(C.byref(dz), 1, 0, C.byref(nb), C.byref(al)),
             qp.QP_EUNSUPPORTED, "zero points")
+    dk = qp.qtensor(qp.QP_S4, [8, 65537], [65537, 1], scheme=qp.QP_BLOCKWISE, group_size=32)
+    _expect(qp, L.qpack_weights_size(C.byref(dk), 1, 0, C.byref(nb), C.byref(al)),
+            qp.QP_EUNSUPPORTED, "65536")
     dr = _w8_desc(qp, rounding=1)
     _expect(qp, L.qpack_weights_size(C.byref(dr), 1, 0, C.byref(nb), C.byref(al)),
             qp.QP_EUNSUPPORTED, "half-to-even")
