@@ -241,8 +241,10 @@ def main():
 
     timed_first("qgemm_s8s8_requant_8192x8192x8192", step)
     # The same warm-up and timed steps straight after process start, reported
-    # apart: from idle the part takes some 20-30 ms of load to raise its
-    # clock, and until then each launch runs about 12% slower.
+    # apart: under a load that starts from idle the power controller lets the
+    # clock run high for a few launches, then pulls it down and brings it
+    # back over some 20-30 launches, so these steps run slower on average
+    # than under sustained load.
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -326,8 +328,8 @@ def main():
     out["clock_ramp"] = {
         "ms_per_step_from_idle": round(ms_from_idle, 4),
         "note": "the same %d warm-up and %d timed steps run straight after process start, "
-                "before the part has raised its clock; the timed steps of this line follow "
-                "the MFMA ceiling loops with no idle gap" % (a.warmup, a.steps)}
+                "while the part's clock settles under the new load; the timed steps of this "
+                "line follow the MFMA ceiling loops with no idle gap" % (a.warmup, a.steps)}
     empty_us = graph_time(lambda: F.qpf_empty(cur_stream()), 100) * 1e3
 
     tr = _measured_traffic()
