@@ -562,7 +562,9 @@ def main():
                 "cold_us": round(msw * 1e3, 2), "GBps": round(bytw / msw / 1e6, 1),
                 "frac_hbm_peak": round(bytw / msw / 1e6 / PEAK_HBM_GBS, 4),
                 "TOPS": round(2 * Mw * Nw * 4096 / msw / 1e9, 2),
-                "note": "dynamic row quantization + product; weights rotated (cold)"}
+                "note": ("one launch: the row quantized inside the GEMV" if Mw == 1 else
+                         "dynamic row quantization + product, two launches") +
+                        "; weights rotated (cold)"}
             del blw, Ww
 
         # dynamic per-row activation quantization (asymmetric and symmetric),

@@ -27,6 +27,7 @@
 // constant wait count covers all steps.
 #include "dev_util.hpp"
 #include "qp_internal.hpp"
+#include "quant_row.hpp"
 
 #pragma clang fp contract(off)
 
@@ -240,6 +241,153 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
     }
 }
 
+// ---- GEMV (M = 1) with the row's dynamic quantization --------------------
+// One workgroup per 16-channel fragment and two kinds of waves, as in the
+// A8W4 GEMV: four quantizer waves load the f32 row (bounded, branch-free
+// loads) and quantize it with the steps of qquantize_rows_s8 into LDS; four
+// weight waves, one K range each, put the weight and scale loads of their
+// first P steps in flight before anything waits.  Loads complete in issue
+// order within a wave, so with the two jobs in different waves neither
+// waits behind the other.  The steps are those of a8w8b_gemm_kernel, with
+// the row's codes read from LDS as row 0 of the MFMA tile (rows 1..15 are
+// zero); the four K ranges are summed in a fixed order.
+template <int BS, int P>
+__global__ __launch_bounds__(512) void a8w8b_gemv_fused_kernel(const float* __restrict__ X,
+                                                               int64_t K, W8B w,
+                                                               const float* __restrict__ bias,
+                                                               float lo, float hi,
+                                                               float* __restrict__ Y) {
+  static_assert(BS == 64 || BS == 128, "block of 64 or 128 K");
+  constexpr int NQ = 4, QT = NQ * 64, QE = 16;  // quantizer waves, threads, values a pass
+  constexpr int KS = 4;                         // weight waves: K ranges
+  constexpr int NSC = 128 / BS;                 // block scales per step
+  extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];  // [Kpad] codes
+  __shared__ float red[2 * NQ];
+  __shared__ float part[KS - 1][4][64];
+  __shared__ float row_param[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < NQ) {
+    const bool xvec = (((uintptr_t)X) & 15) == 0;
+    const RowFirst xf = quantize_row_first<QT, QE>(X, K, xvec);
+    // one pass of whole vectors (e.g. K = 4096) runs without the loops and
+    // fallbacks of the general case
+    const bool one = xvec && K == (int64_t)QT * QE && w.Kpad == K;
+    float4 first[4];
+    if (one)
+      row_extremes_partial<QT, QE, false, true>(X, K, xvec, red, first, &xf);
+    else
+      row_extremes_partial<QT, QE, false>(X, K, xvec, red, first, &xf);
+    __syncthreads();  // (1) the waves' extremes
+    float s;
+    int32_t z;
+    row_params<QT, false>(red, &s, &z);
+    if (tid == 0) {
+      row_param[0] = s;
+      row_param[1] = __builtin_bit_cast(float, z);
+    }
+    if (one)
+      row_codes<QT, QE, false, false, true>(X, K, w.Kpad, xvec, true, qa_lds, s, z, first);
+    else
+      row_codes<QT, QE, false, false>(X, K, w.Kpad, xvec, true, qa_lds, s, z, first);
+    __syncthreads();  // (2) the codes
+    __syncthreads();  // (3) the K ranges' partial sums
+    return;
+  }
+  const int ks = wave - NQ;
+  const int c = lane >> 4;
+  const int64_t n = (int64_t)blockIdx.x * 16 + (lane & 15);  // < Npad
+  const int64_t nsteps = w.Kpad / 128;
+  const int64_t bpw = (nsteps + KS - 1) / KS;  // steps per K range
+  auto range_step = [&](int64_t j) {
+    const int64_t b_begin = ks * bpw;
+    int64_t last = (b_begin + bpw < nsteps ? b_begin + bpw : nsteps) - 1;
+    if (last < b_begin) last = nsteps - 1;  // empty range: park on a real step
+    const int64_t b = b_begin + j;
+    return b < last ? b : last;
+  };
+  const int64_t my_end = (ks * bpw + bpw < nsteps ? ks * bpw + bpw : nsteps);
+  const int8_t* wsrc =
+      w.data + ((n >> 5) * w.kblocks + (c >> 1)) * 1024 + (n & 31) * 32 + (c & 1) * 16;
+  const float* ssrc = w.scale + n;  // + block * Npad
+  v4i wr[P][2];
+  float sr[P][NSC];
+  auto load_w = [&](int u, int64_t b) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) wr[u][h] = *reinterpret_cast<const v4i*>(wsrc + b * 4096 + h * 2048);
+#pragma unroll
+    for (int h = 0; h < NSC; ++h) sr[u][h] = ssrc[(b * NSC + h) * w.Npad];
+  };
+#pragma unroll
+  for (int u = 0; u < P; ++u) load_w(u, range_step(u));
+  const float wsum_n = ks == 0 ? w.wsum[n] : 0.0f;  // the epilogue's inputs, needed last
+  const float bias_n = (ks == 0 && bias && n < w.N) ? bias[n] : 0.0f;
+  __syncthreads();  // (1)
+  __syncthreads();  // (2): the codes are in LDS
+
+  const bool row0 = (lane & 15) == 0;
+  float acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[0][i] = acc[1][i] = 0.0f;
+  auto step = [&](int u, int64_t j) {
+    const int64_t b = range_step(j);
+    v4i af[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const v4i v = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(
+          (const lds_i8*)qa_lds + b * 128 + 64 * h + 16 * c);
+      af[h] = row0 ? v : v4i{0, 0, 0, 0};
+    }
+    // (the first use of this step's loads stays after the barriers above)
+    asm volatile("" : "+v"(wr[u][0]), "+v"(wr[u][1]));
+#pragma unroll
+    for (int h = 0; h < NSC; ++h) asm volatile("" : "+v"(sr[u][h]));
+    const bool live = ks * bpw + j < my_end;
+    v4i cw2[2];
+    float cs[NSC];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cw2[h] = wr[u][h];
+#pragma unroll
+    for (int h = 0; h < NSC; ++h) cs[h] = live ? sr[u][h] : 0.0f;
+    load_w(u, range_step(j + P));
+    v4i d[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[h], cw2[h], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (BS == 64) {
+        acc[0][i] = __builtin_fmaf(cs[0], (float)d[0][i], acc[0][i]);
+        acc[1][i] = __builtin_fmaf(cs[NSC - 1], (float)d[1][i], acc[1][i]);
+      } else {
+        acc[0][i] = __builtin_fmaf(cs[0], (float)(d[0][i] + d[1][i]), acc[0][i]);
+      }
+    }
+  };
+  for (int64_t j0 = 0; j0 < bpw; j0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) step(u, j0 + u);
+  }
+  wait_vmcnt<0>();  // the clamped refills must land before the workgroup ends
+
+  float out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = acc[0][i] + acc[1][i];
+  if (ks > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[ks - 1][i][lane] = out[i];
+  }
+  __syncthreads();  // (3)
+  // lane l < 16 holds row 0 (register 0) of channel l
+  if (ks != 0 || lane >= 16 || n >= w.N) return;
+  float S = out[0];
+#pragma unroll
+  for (int r = 0; r < KS - 1; ++r) S = S + part[r][0][lane];
+  Y[n] = finish_w8(S, row_param[0], __builtin_bit_cast(int32_t, row_param[1]), wsum_n, bias_n,
+                   lo, hi);
+}
+
 W8B w8b_of(const qp_packed_info* b, const void* blob) {
   const uint8_t* p = static_cast<const uint8_t*>(blob);
   return W8B{reinterpret_cast<const int8_t*>(p + b->data_off),
@@ -275,6 +423,22 @@ qp_status launch_cfg(const int8_t* qa, int64_t lda, const float* sa, const int32
   return check_launch("a8w8 blockwise gemm");
 }
 
+// Largest Kpad of the fused GEMV: its codes live in the workgroup's LDS.
+constexpr int64_t kFusedGemvMaxKpad = 32768;
+
+qp_status launch_gemv_fused(const float* X, int64_t K, const W8B& w, int64_t bs,
+                            const float* bias, float lo, float hi, float* Y, hipStream_t stream) {
+  const unsigned blocks = (unsigned)(w.Npad / 16);
+  const size_t lds = (size_t)w.Kpad;
+  if (bs == 64)
+    hipLaunchKernelGGL((a8w8b_gemv_fused_kernel<64, 8>), dim3(blocks), dim3(512), lds, stream, X,
+                       K, w, bias, lo, hi, Y);
+  else
+    hipLaunchKernelGGL((a8w8b_gemv_fused_kernel<128, 8>), dim3(blocks), dim3(512), lds, stream, X,
+                       K, w, bias, lo, hi, Y);
+  return check_launch("a8w8 blockwise gemv");
+}
+
 qp_status launch_a8w8b(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
                        int64_t M, const W8B& w, int64_t bs, const float* bias, float lo, float hi,
                        float* Y, int64_t ldy, hipStream_t stream) {
@@ -300,7 +464,9 @@ extern "C" qp_status qgemm_a8w8_blockwise_f32_ws_size(int64_t M, const qp_packed
                                                       size_t* bytes) {
   using namespace qp;
   QP_REQUIRE(w && bytes && M >= 0, QP_EINVAL, "qgemm_a8w8_blockwise_f32_ws_size: bad argument");
-  *bytes = (size_t)(round_up(M * w->Kpad, 256) + round_up(8 * M, 256));
+  // one row with its codes fitting the fused GEMV's LDS needs no workspace
+  const bool fused = M <= 1 && w->Kpad <= kFusedGemvMaxKpad;
+  *bytes = fused ? 0 : (size_t)(round_up(M * w->Kpad, 256) + round_up(8 * M, 256));
   return QP_OK;
 }
 
@@ -338,6 +504,9 @@ extern "C" qp_status qgemm_a8w8_blockwise_f32(const float* X, int64_t M, int64_t
   QP_REQUIRE(!(clamp_lo > clamp_hi), QP_EINVAL, "a8w8 blockwise: clamp_lo > clamp_hi");
   if (M == 0) return QP_OK;
   QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "a8w8 blockwise: null data pointer");
+  if (M == 1 && w->Kpad <= kFusedGemvMaxKpad)
+    return launch_gemv_fused(X, K, w8b_of(w, packedW_dev), w->group, bias, clamp_lo, clamp_hi, Y,
+                             stream);
   size_t need = 0;
   qgemm_a8w8_blockwise_f32_ws_size(M, w, &need);
   QP_REQUIRE(ws_bytes >= need, QP_ESIZE, "a8w8 blockwise: workspace holds %zu bytes, needs %zu",

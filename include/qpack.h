@@ -443,7 +443,10 @@ qp_status qgemm_a8w4_blockq_prequant_f32(const int8_t* qa, int64_t M, int64_t ld
  *   exact int32 inside a block, f32 across blocks; the rows quantized as by
  *   qquantize_rows_s8.  For a GEMM (a linear layer, or a 1x1 convolution
  *   whose OIHW weights were packed as K = C).
- *   ws       device workspace of qgemm_a8w8_blockwise_f32_ws_size bytes.
+ *   ws       device workspace of qgemm_a8w8_blockwise_f32_ws_size bytes:
+ *            0 for one row with Kpad <= 32768 (quantized inside the
+ *            product's own launch; ws may then be null), else the quantized
+ *            rows and their parameters.
  * qgemm_a8w8_blockwise_prequant_f32 is the matmul step alone (qa [M][lda],
  * lda >= Kpad and a multiple of 16, zero for K <= k < Kpad; sa, za [M]).
  */

@@ -83,6 +83,34 @@ def test_a8w8b_shapes_and_tails(qp, orc, M, N, K, bs, prequant):
     _case(qp, orc, M, N, K, bs, M + N + K, prequant=prequant)
 
 
+@pytest.mark.parametrize("N,K,bs", [(33, 1000, 128), (48, 20000, 64), (16, 32768, 128),
+                                    (17, 32769, 64), (40, 4096, 64)])
+def test_a8w8b_gemv_fused_shapes(qp, orc, N, K, bs):
+    """One row from f32: the fused GEMV (the row quantized inside every
+    workgroup, no workspace) for Kpad <= 32768, the two launches beyond;
+    ragged N and K, several batches of K steps per wave."""
+    _case(qp, orc, 1, N, K, bs, N + K)
+    Kpad = (K + 127) // 128 * 128
+    info = qp.pack_s8_blockwise(_dev(np.zeros((N, K), np.int8)),
+                                _dev(np.ones((N, (K + bs - 1) // bs), np.float32)), block=bs)[1]
+    assert (qp.qgemm_a8w8_blockwise_f32_ws_size(1, info) == 0) == (Kpad <= 32768)
+
+
+def test_a8w8b_gemv_fused_unaligned_row(qp, orc):
+    """A row that starts 4 bytes past a 16-byte boundary takes the
+    quantizer's scalar loads."""
+    import torch
+    X, W, sw, bias = _inputs(1, 70, 900, 64, 77)
+    blob, info = qp.pack_s8_blockwise(_dev(W), _dev(sw), block=64)
+    big = torch.zeros((1, 904), dtype=torch.float32, device="cuda")
+    big[:, 1:901] = _dev(X)
+    Xv = big[:, 1:901]
+    assert Xv.data_ptr() % 16 == 4
+    Y = _host(qp.qgemm_a8w8_blockwise_f32(Xv, blob, info, _dev(bias), -6.0, 6.0))
+    want = orc.a8w4_forward(X, W, sw, bias, -6.0, 6.0, group=64)
+    _check_close(Y, want, "fused a8w8 GEMV, unaligned row")
+
+
 def test_a8w8b_unpack_and_conv_weights(qp, orc):
     """A 1x1 convolution's OIHW weights pack as K = C; unpack returns the
     values, the block scales and the dequantized weights (O9)."""
