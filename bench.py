@@ -468,7 +468,7 @@ def main():
             "quantize_plus_gemv_cold_us": round(msq * 1e3, 3),
             "GBps_cold": round(nbytes_alg / msq / 1e6, 1),
             "frac_hbm_peak_cold": round(nbytes_alg / msq / 1e6 / PEAK_HBM_GBS, 4),
-            "note": "activations quantized per block of 32; two launches"}
+            "note": "activations quantized per block of 32 inside the GEMV; one launch"}
         del blobs, blobs16
 
         # asymmetric int4 (a float offset per group, blob format 4)

@@ -198,14 +198,23 @@ __device__ __forceinline__ void gemv_block_terms(const Nibbles& nb, const uint2 
 // are in LDS the weight waves form the exact int32 group dots and the f32
 // scaled sum, reduce over the four lanes of a channel (DPP) and then over
 // the weight waves through LDS in a fixed order.
-template <int NQ, int NWW, int BB, int QE, int kKind>
+// kBQ: the row is quantized per block of 32 instead (the steps of
+// qquantize_rows_s8_blocked): a quantizer thread takes 16 values, the
+// neighbouring lane the other 16 of the block, and one DPP lane swap gives
+// the block's extremes; each block's scale and zero point go to LDS after
+// the codes, and every group piece contributes sa*sw * (dot - za * sum q).
+template <int NQ, int NWW, int BB, int QE, int kKind, bool kBQ = false>
 __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
     const float* __restrict__ X, int64_t K, W4 w, const float* __restrict__ bias, float lo,
     float hi, float* __restrict__ Y) {
+  static_assert(!kBQ || kKind != 2, "per-block activations: symmetric weights");
   constexpr int QT = NQ * 64;  // quantizer threads
   constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
-  extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];  // [Kpad] codes
+  // [Kpad] codes; kBQ: then [Kpad/32] f32 block scales, [Kpad/32] zero points
+  extern __shared__ __attribute__((aligned(16))) int8_t qa_lds[];
+  float* const bq_s = reinterpret_cast<float*>(qa_lds + w.Kpad);
+  int32_t* const bq_z = reinterpret_cast<int32_t*>(qa_lds + w.Kpad) + w.Kpad / 32;
   __shared__ float red[2 * NQ];
   __shared__ float part_w[NWW][16];
   __shared__ float row_param[2];
@@ -216,7 +225,64 @@ __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
   const int64_t nb = w.nblk;
   const int64_t n_out = tile * 16 + (lane & 15);  // the final step's channel (weight wave 0)
   float wsum_c = 0.0f, bias_c = 0.0f;
-  if (wave < NQ) {
+  if (kBQ && wave < NQ) {
+    const bool xvec = (((uintptr_t)X) & 15) == 0;
+    for (int64_t k0 = (int64_t)tid * 16; k0 < w.Kpad; k0 += QT * 16) {
+      // (both lanes of a block take the same branches: Kpad % 32 == 0)
+      float v[16];
+      if (xvec && k0 + 16 <= K) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *reinterpret_cast<const float4*>(X + k0 + 4 * q);
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = k0 + j < K ? X[k0 + j] : 0.0f;
+      }
+      // the block's range, widened to include 0 (values past K read as 0)
+      float lo_b = 0.0f, hi_b = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        lo_b = qp_min(lo_b, v[j]);
+        hi_b = qp_max(hi_b, v[j]);
+      }
+      lo_b = qp_min(lo_b, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                              0, __builtin_bit_cast(int, lo_b), 0xB1, 0xF, 0xF, false)));
+      hi_b = qp_max(hi_b, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                              0, __builtin_bit_cast(int, hi_b), 0xB1, 0xF, 0xF, false)));
+      float s;
+      int32_t z;
+      params_from_range(lo_b, hi_b, &s, &z);
+      uint32_t q4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k0 + 4 * q + j < K) acc |= quantize_one(v[4 * q + j], s, z) << (8 * j);
+        q4[q] = acc;
+      }
+      // the 8-byte piece holding k = 128b + 32g + 8cc .. +8 goes to 128b + 32cc + 8g
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t kk = k0 + 8 * h;
+        const int64_t b = kk >> 7, g = (kk >> 5) & 3, cc = (kk >> 3) & 3;
+        *reinterpret_cast<uint2*>(qa_lds + b * 128 + cc * 32 + g * 8) =
+            make_uint2(q4[2 * h], q4[2 * h + 1]);
+      }
+      if ((tid & 1) == 0) {
+        bq_s[k0 >> 5] = s;
+        bq_z[k0 >> 5] = z;
+      }
+    }
+    __syncthreads();  // (1)
+    __syncthreads();  // (2) the codes and block parameters
+    __syncthreads();  // (3) the partial sums
+  } else if (wave < NQ) {
     const bool xvec = (((uintptr_t)X) & 15) == 0;
     const RowFirst xf = quantize_row_first<QT, QE>(X, K, xvec);
     // one pass of whole vectors (e.g. K = 4096) runs without the loops and
@@ -290,7 +356,21 @@ __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
         const Nibbles nb4 = nibble_ops(wv[u]);
         const uint2 a[4] = {make_uint2(p0[u].x, p0[u].y), make_uint2(p0[u].z, p0[u].w),
                             make_uint2(p1[u].x, p1[u].y), make_uint2(p1[u].z, p1[u].w)};
-        gemv_block_terms<kKind>(nb4, a, sv[u], ov[u], part);
+        if constexpr (kBQ) {  // the block's four group parameters of the row
+          const float4 sq = *reinterpret_cast<const float4*>(bq_s + 4 * blk[u]);
+          const int4 zq = *reinterpret_cast<const int4*>(bq_z + 4 * blk[u]);
+          const uint4 wq = wv[u];
+          const int32_t e0 = word_dot16(wq.x, a[0].x, a[0].y) - zq.x * word_wsum16(wq.x);
+          const int32_t e1 = word_dot16(wq.y, a[1].x, a[1].y) - zq.y * word_wsum16(wq.y);
+          const int32_t e2 = word_dot16(wq.z, a[2].x, a[2].y) - zq.z * word_wsum16(wq.z);
+          const int32_t e3 = word_dot16(wq.w, a[3].x, a[3].y) - zq.w * word_wsum16(wq.w);
+          part = part + (sq.x * sv[u].x) * (float)e0;
+          part = part + (sq.y * sv[u].y) * (float)e1;
+          part = part + (sq.z * sv[u].z) * (float)e2;
+          part = part + (sq.w * sv[u].w) * (float)e3;
+        } else {
+          gemv_block_terms<kKind>(nb4, a, sv[u], ov[u], part);
+        }
       }
     };
     load_batch(0);
@@ -320,9 +400,13 @@ __global__ __launch_bounds__((NQ + NWW) * 64) void a8w4_gemv_fused_kernel(
     float S = 0.0f;
 #pragma unroll
     for (int v = 0; v < NWW; ++v) S = S + part_w[v][lane];
-    const float sa = row_param[0];
-    const int32_t za = __builtin_bit_cast(int32_t, row_param[1]);
-    if (n_out < w.N) Y[n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
+    if constexpr (kBQ) {
+      if (n_out < w.N) Y[n_out] = finish_bq(S, bias_c, lo, hi);
+    } else {
+      const float sa = row_param[0];
+      const int32_t za = __builtin_bit_cast(int32_t, row_param[1]);
+      if (n_out < w.N) Y[n_out] = finish(S, sa, za, wsum_c, bias_c, lo, hi);
+    }
   }
 }
 
@@ -1134,6 +1218,23 @@ qp_status launch_gemv_fused(const float* X, int64_t K, const W4& w, const float*
   return check_launch("a8w4 gemv");
 }
 
+// M = 1 from f32 with the row quantized per block of 32 inside the GEMV
+// (symmetric weights: f32 or bf16 scales); LDS holds the codes and the
+// blocks' parameters.
+qp_status launch_gemv_fused_bq(const float* X, int64_t K, const W4& w, const float* bias,
+                               float lo, float hi, float* Y, hipStream_t stream) {
+  const unsigned blocks = (unsigned)(w.Npad / 16);
+  const size_t lds = (size_t)w.Kpad + 8 * (size_t)(w.Kpad / 32);
+  constexpr int NQ = 4, NWW = 8, BB = 4, QE = 16;
+  if (w.kind == 1)
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, QE, 1, true>), dim3(blocks),
+                       dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
+  else
+    hipLaunchKernelGGL((a8w4_gemv_fused_kernel<NQ, NWW, BB, QE, 0, true>), dim3(blocks),
+                       dim3((NQ + NWW) * 64), lds, stream, X, K, w, bias, lo, hi, Y);
+  return check_launch("a8w4 gemv (per-block activations)");
+}
+
 // M <= 4 quantized rows (row-major, lda >= Kpad).
 qp_status launch_gemv(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za, int64_t M,
                       const W4& w, const float* bias, float lo, float hi, float* Y, int64_t ldy,
@@ -1425,7 +1526,10 @@ extern "C" qp_status qgemm_a8w4_blockq_f32_ws_size(int64_t M, const qp_packed_in
   using namespace qp;
   QP_REQUIRE(w && bytes && M >= 0, QP_EINVAL, "qgemm_a8w4_blockq_f32_ws_size: bad argument");
   const int64_t nb = w->Kpad / 32;
-  *bytes = (size_t)(round_up(M * w->Kpad, 256) + 2 * round_up(4 * M * nb, 256));
+  // one row whose codes and block parameters fit the fused GEMV's LDS needs
+  // no workspace
+  const bool fused = M <= 1 && w->Kpad <= kFusedGemvMaxKpad;
+  *bytes = fused ? 0 : (size_t)(round_up(M * w->Kpad, 256) + 2 * round_up(4 * M * nb, 256));
   return QP_OK;
 }
 
@@ -1477,6 +1581,8 @@ extern "C" qp_status qgemm_a8w4_blockq_f32(const float* X, int64_t M, int64_t K,
   QP_REQUIRE(!(clamp_lo > clamp_hi), QP_EINVAL, "a8w4: clamp_lo > clamp_hi");
   if (M == 0) return QP_OK;
   QP_REQUIRE(X && packedW_dev && Y, QP_EINVAL, "a8w4: null data pointer");
+  if (M == 1 && w->Kpad <= kFusedGemvMaxKpad)
+    return launch_gemv_fused_bq(X, K, w4_of(w, packedW_dev), bias, clamp_lo, clamp_hi, Y, stream);
   size_t need = 0;
   qgemm_a8w4_blockq_f32_ws_size(M, w, &need);
   QP_REQUIRE(ws_bytes >= need, QP_ESIZE, "a8w4: workspace holds %zu bytes, needs %zu", ws_bytes,

@@ -415,7 +415,9 @@ qp_status qgemm_a8w4_prequant_f32(const int8_t* qa, int64_t M, int64_t lda, cons
  *                  + bias[n], lo, hi)
  *   the sum inside a group exact in int32, across groups f32.
  * Weights: int4 blobs with f32 or bf16 scales (not the asymmetric format).
- *   ws       device workspace of qgemm_a8w4_blockq_f32_ws_size bytes.
+ *   ws       device workspace of qgemm_a8w4_blockq_f32_ws_size bytes: 0
+ *            for one row with Kpad <= 32768 (quantized inside the GEMV's
+ *            own launch; ws may then be null).
  * qgemm_a8w4_blockq_prequant_f32 is the matmul step alone:
  *   qa       device int8 [M][lda], lda >= Kpad, a multiple of 16, 16-byte
  *            aligned, zero for K <= k < Kpad.

@@ -248,6 +248,8 @@ def test_a8w4_blockq_gemm_workload(qp, orc, M):
                                                 (1, 33, 1000, True, "bf16"),
                                                 (1, 40, 1000, False, "bf16"),
                                                 (1, 16, 53248, False, "f32"),
+                                                (1, 48, 32768, False, "f32"),
+                                                (1, 50, 20000, False, "bf16"),
                                                 (2, 130, 200, False, "f32"),
                                                 (5, 77, 1000, True, "f32"),
                                                 (17, 100, 256, False, "bf16"),
@@ -256,6 +258,24 @@ def test_a8w4_blockq_gemm_workload(qp, orc, M):
 def test_a8w4_blockq_shapes(qp, orc, M, N, K, prequant, sdt):
     _case_bq(qp, orc, synth.a8w4(synth.BASE_SEED + 17 * M + N + K, M, N, K), prequant=prequant,
              scale_dtype=sdt)
+
+
+def test_a8w4_blockq_gemv_unaligned_row(qp, orc):
+    """One row quantized per block inside the GEMV (no workspace), read
+    from 4 bytes past a 16-byte boundary."""
+    import torch
+    d = synth.a8w4(synth.BASE_SEED + 95, 1, 70, 900)
+    blob, info = qp.pack_s4(_dev(d["W"]), _dev(d["sw"]))
+    assert qp.qgemm_a8w4_blockq_f32_ws_size(1, info) == 0
+    big = torch.zeros((1, 904), dtype=torch.float32, device="cuda")
+    big[:, 1:901] = _dev(d["X"])
+    Xv = big[:, 1:901]
+    assert Xv.data_ptr() % 16 == 4
+    Y = _host(qp.qgemm_a8w4_blockq_f32(Xv, blob, info, _dev(d["bias"]), d["clamp_lo"],
+                                       d["clamp_hi"]))
+    want = orc.a8w4_forward_blockq(d["X"], d["W"], d["sw"], d["bias"], d["clamp_lo"],
+                                   d["clamp_hi"])
+    _check_close(Y, want, "per-block a8w4 GEMV, unaligned row")
 
 
 def test_a8w4_blockq_rejects_asymmetric_weights(qp):
