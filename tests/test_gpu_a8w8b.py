@@ -84,7 +84,7 @@ def test_a8w8b_shapes_and_tails(qp, orc, M, N, K, bs, prequant):
 
 
 @pytest.mark.parametrize("N,K,bs", [(33, 1000, 128), (48, 20000, 64), (16, 32768, 128),
-                                    (17, 32769, 64), (40, 4096, 64)])
+                                    (17, 32769, 64), (40, 4096, 64), (1, 64, 64), (3, 1, 128)])
 def test_a8w8b_gemv_fused_shapes(qp, orc, N, K, bs):
     """One row from f32: the fused GEMV (the row quantized inside every
     workgroup, no workspace) for Kpad <= 32768, the two launches beyond;
