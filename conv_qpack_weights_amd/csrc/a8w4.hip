@@ -51,6 +51,16 @@ __device__ __forceinline__ int32_t word_wsum16(uint32_t w) {
                                 false);
 }
 
+// 16 bytes of LDS as a float4.  The elements are copied to scalars before
+// the casts: __builtin_bit_cast applied straight to an element of a vector
+// (u.y) compiles, with this compiler, to a cast of element 0.
+__device__ __forceinline__ float4 lds_f4(const lds_i8* p) {
+  const u32x4 u = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+  const uint32_t x = u.x, y = u.y, z = u.z, w = u.w;
+  return make_float4(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y),
+                     __builtin_bit_cast(float, z), __builtin_bit_cast(float, w));
+}
+
 // Per-block activation quantization: S16 already holds
 // 16 * sum_g sa[g]*sw[g]*sum (qa - za[g])*q, so only the bias remains.
 __device__ __forceinline__ float finish_bq(float S16, float bias, float lo, float hi) {
@@ -584,8 +594,13 @@ __global__ __launch_bounds__(NT) void a8w4_gemv_kernel(const int8_t* __restrict_
 // kBQ (activations quantized per block of 32: sa, za are [M][ldsz]): the
 // MFMA is issued the other way round, (weights, activations), so a lane
 // holds channels 4*(l/16)+i of row l%16 and needs one row's group
-// parameters; a second MFMA against the row's zero point replicated over K
-// gives za*sum q, and each group adds sa*sw * (d - that) per output.
+// parameters.  The group's integer sum over (q - za) * w is one MFMA chain:
+// the weights against ones (sum w, shared by the rows), then against the
+// codes, then against ~za replicated over K (~za = -za - 1, which fits a
+// byte where -za may not); each group then adds sa*sw times that sum per
+// output.  The block's weight scales and the rows' group parameters travel
+// with the codes through the LDS ring (4-byte direct loads), so only the
+// weights are held in registers ahead of use.
 // PW: weight prefetch depth in blocks.  kExact: every K range holds a
 // multiple of 2*PW blocks (the host checks), so no step runs past its range
 // and the per-step range test and zeroed scales drop out.
@@ -600,20 +615,33 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
                                                         int64_t ldy, int64_t ldsz) {
   static_assert(!kBQ || kKind != 2, "per-block activations take symmetric weights");
   static_assert(RW * CW * KS == 4, "four waves");
-  // weight prefetch depth in blocks (kBQ holds more per block: two)
-  constexpr int P = kBQ ? 2 : PW;
+  constexpr int P = PW;                     // weight prefetch depth in blocks
   constexpr int R = 4;                      // activation ring stages
   constexpr int MT = 16 * FM * RW;          // rows per workgroup
   constexpr int SLOTS = KS * MT * 8;        // 16-byte pieces per stage
   constexpr int ND = SLOTS / 256;           // direct loads per thread per stage
-  constexpr int STAGE = SLOTS * 16;         // bytes per stage
+  constexpr int STAGE = SLOTS * 16;         // bytes of codes per stage
   static_assert(SLOTS % 256 == 0, "a stage must split evenly over the workgroup");
+  // kBQ: after the codes, each stage holds the block's weight scales of the
+  // workgroup's tiles, [K range][tile][64 values] (256 bytes a tile; bf16
+  // scales fill the first half), and the rows' group parameters,
+  // [K range][sa, za][row][4 groups]; both arrive as 4-byte direct loads,
+  // NS and NP per thread.
+  constexpr int SCB = kBQ ? KS * CW * FN * 256 : 0;
+  constexpr int PAB = kBQ ? KS * MT * 32 : 0;
+  constexpr int NS = SCB / 1024, NP = PAB / 1024;
+  static_assert(SCB % 1024 == 0 && PAB % 1024 == 0, "kBQ: stage extras must split evenly");
+  constexpr int STRIDE = STAGE + SCB + PAB;  // bytes per stage
   // Each wave its own K range (one row and one channel group): a wave loads
   // and reads only its own rows of a stage, so the waves need no barrier in
   // the K loop and run decoupled (a late weight block stalls only its wave).
   constexpr bool kPrivA = RW * CW == 1;
   static_assert(!kPrivA || MT * 8 == 64 * ND, "a wave's rows of a stage: ND loads per lane");
-  __shared__ __attribute__((aligned(16))) int8_t ring[R * STAGE];
+  // (kBQ without a barrier: a wave's scale and parameter pieces must be its
+  // own K range's, which the piece mapping below gives for one tile a
+  // workgroup, four K ranges and one scale piece a thread)
+  static_assert(!kBQ || !kPrivA || (KS == 4 && CW * FN == 1 && NS == 1), "kBQ wave-private ring");
+  __shared__ __attribute__((aligned(16))) int8_t ring[R * STRIDE];
   __shared__ float red[KS > 1 ? (KS - 1) * RW * CW : 1][FM][FN][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -659,22 +687,9 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     const int64_t n = n0 + q * 16 + (lane & 15);
     wsrc[q] = reinterpret_cast<const int8_t*>(w.data) + (n >> 4) * w.nblk * 1024 +
               (lane & 15) * 64 + 16 * c;
-    // kBQ: the scales of channels 4c..4c+3 (16 consecutive values) instead
-    ssrc[q] = kBQ ? w.scale + ((n >> 4) * w.nblk * 64 + 16 * c) * ES
-                  : w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
+    ssrc[q] = w.scale + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * ES;
     osrc[q] = kAsym ? w.offs + ((n >> 4) * w.nblk * 64 + (lane & 15) * 4) * 4 : nullptr;
   }
-  // kBQ: this lane's rows' per-block activation parameters
-  const float* sap[FM];
-  const int32_t* zap[FM];
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    int64_t m = mw + rw * 16 * FM + f * 16 + (lane & 15);
-    m = m < M ? m : M - 1;
-    sap[f] = kBQ ? sa_g + m * ldsz : nullptr;
-    zap[f] = kBQ ? za_g + m * ldsz : nullptr;
-  }
-
   // ---- activation direct loads: thread slot s = tid + 256*i of a stage ->
   // (K range, row, chunk position); the global chunk is position ^ swizzle.
   const int8_t* const a_base = qa + mw * lda;
@@ -692,8 +707,40 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     m = m < M ? m : M - 1;
     a_voff[i] = (uint32_t)((m - mw) * lda + 16 * p);
   }
+  // kBQ: this thread's scale and parameter pieces.  Piece i of a wave is
+  // the 64-dword chunk wave + 4i: of the scales, chunk -> (K range, tile);
+  // of the parameters, chunk -> (K range, sa or za, 16 rows), lane -> (row
+  // lane/4, group lane%4).  Rows past M repeat row M-1.
+  constexpr int NSA = NS > 0 ? NS : 1, NPA = NP > 0 ? NP : 1;
+  const uint8_t* sc_base[NSA];
+  int sc_rng[NSA], sc_dst[NSA];
+  const void* pa_base[NPA];
+  int pa_rng[NPA], pa_dst[NPA];
+  uint32_t pa_voff[NPA];
+  const uint32_t sc_voff = kBf16 ? 4u * (lane & 31) : 4u * lane;  // bf16: 128 bytes a tile
+  if constexpr (kBQ) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int ch = wave + 4 * i;
+      sc_rng[i] = ch / (CW * FN);
+      sc_base[i] = w.scale + ((int64_t)cgi * CW * FN + ch % (CW * FN)) * w.nblk * 64 * ES;
+      sc_dst[i] = STAGE + ch * 256;
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int ch = wave + 4 * i;
+      const int kr = ch % KS, within = ch / KS;
+      const int kind = within / (MT / 16), rb = within % (MT / 16);
+      pa_rng[i] = kr;
+      pa_base[i] = kind ? (const void*)(za_g + mw * ldsz) : (const void*)(sa_g + mw * ldsz);
+      int64_t m = mw + rb * 16 + (lane >> 2);
+      m = m < M ? m : M - 1;
+      pa_voff[i] = (uint32_t)(((m - mw) * ldsz + (lane & 3)) * 4);
+      pa_dst[i] = STAGE + SCB + ((kr * 2 + kind) * MT + rb * 16) * 16;
+    }
+  }
   auto issue_stage = [&](int j) {
-    lds_i8* st = (lds_i8*)ring + (int)(j % R) * STAGE;
+    lds_i8* st = (lds_i8*)ring + (int)(j % R) * STRIDE;
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int64_t b = range_block(a_rng[i], j);
@@ -701,15 +748,28 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       dma16_to_lds(a_base, (lds_void_t*)(st + s0 * 16), a_voff[i],
                    (uint32_t)(b * 128));
     }
+    if constexpr (kBQ) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        dma4_to_lds(sc_base[i], (lds_void_t*)(st + sc_dst[i]), sc_voff,
+                    (uint32_t)(range_block(sc_rng[i], j) * 64 * ES));
+#pragma unroll
+      for (int i = 0; i < NP; ++i)
+        dma4_to_lds(pa_base[i], (lds_void_t*)(st + pa_dst[i]), pa_voff[i],
+                    (uint32_t)(range_block(pa_rng[i], j) * 16));
+    }
   };
 
   // ---- accumulators ----
+  // (f64 sums: asymmetric weights after every block; per-block activations
+  // after every PR blocks, so that the f32 chains stay short at deep K)
+  constexpr bool kD = kAsym || kBQ;
   float acc[2][FM][FN][4];
-  double accd[kAsym ? FM : 1][kAsym ? FN : 1][4];
+  double accd[kD ? FM : 1][kD ? FN : 1][4];
 #pragma unroll
-  for (int f = 0; f < (kAsym ? FM : 1); ++f)
+  for (int f = 0; f < (kD ? FM : 1); ++f)
 #pragma unroll
-    for (int q = 0; q < (kAsym ? FN : 1); ++q)
+    for (int q = 0; q < (kD ? FN : 1); ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) accd[f][q][i] = 0.0;
 #pragma unroll
@@ -724,37 +784,22 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   // The weight ring holds PR = 2P slots when K ranges are exact: step u
   // consumes slot u and refills slot (u + P) % PR, which nothing reads any
   // more, so the refill needs no register copies at the loop's back edge.
-  constexpr int PR = (kExact && !kBQ) ? 2 * P : P;
+  constexpr int PR = kExact ? 2 * P : P;
   uint4 wr[PR][FN];
-  float4 sr[PR][FN], orr[PR][FN];
-  float4 sr4[kBQ ? P : 1][FN][4];     // kBQ: [channel 4c+i] x 4 groups
-  float4 sar[kBQ ? P : 1][FM];        // kBQ: the row's 4 group scales
-  int4 zar[kBQ ? P : 1][FM];          //      and zero points
+  float4 sr[kBQ ? 1 : PR][FN], orr[PR][FN];
   auto load_w = [&](int u, int64_t b) {
 #pragma unroll
     for (int q = 0; q < FN; ++q) {
       wr[u][q] = *reinterpret_cast<const uint4*>(wsrc[q] + b * 1024);
-      if constexpr (kBQ) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sr4[u][q][i] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b + 4 * ES * i);
-      } else {
-        sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
-      }
+      if constexpr (!kBQ) sr[u][q] = load_scale4<kBf16>(ssrc[q] + 64 * ES * b);
       if constexpr (kAsym) orr[u][q] = load_scale4<false>(osrc[q] + 64 * 4 * b);
-    }
-    if constexpr (kBQ) {
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        sar[u][f] = *reinterpret_cast<const float4*>(sap[f] + 4 * b);
-        zar[u][f] = *reinterpret_cast<const int4*>(zap[f] + 4 * b);
-      }
     }
   };
 
   // one block: activation operands from the stage, MFMAs, refill, rescale
   auto step = [&](int u, int j) {
-    const lds_i8* st = (const lds_i8*)ring + (int)(j % R) * STAGE + ks * MT * 128;
+    const lds_i8* stage = (const lds_i8*)ring + (int)(j % R) * STRIDE;
+    const lds_i8* st = stage + ks * MT * 128;
     uint2 ca[FM][4];
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
@@ -783,25 +828,50 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
     float4 cs[FN], co[FN];
     const bool live = kExact || ks * bpw + j < my_end;
     if constexpr (kBQ) {
-      // per output (channel 4c+i, row): sa[row, g] * sw[channel, g], with
-      // the row scales zeroed past the end of the K range
-      float4 a4[FM], s4[FN][4];
+      // the block's weight scales of channels 4c..4c+3 (16 consecutive
+      // values of the tile's 64) and the rows' group parameters, from the
+      // stage; past the end of the K range the row scales are zeroed
+      float4 s4[FN][4], a4[FM];
       int4 zq[FM];
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        a4[f] = live ? sar[u][f] : make_float4(0.f, 0.f, 0.f, 0.f);
-        zq[f] = zar[u][f];
-      }
-#pragma unroll
       for (int q = 0; q < FN; ++q) {
-        cw4[q] = wr[u][q];
+        const lds_i8* sp = stage + STAGE + ((ks * CW + cw) * FN + q) * 256;
+        if constexpr (kBf16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s4[q][i] = sr4[u][q][i];
+          for (int h = 0; h < 2; ++h) {
+            const u32x4 u = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                sp + 32 * c + 16 * h);
+            s4[q][2 * h] = make_float4(__builtin_bit_cast(float, u.x << 16),
+                                       __builtin_bit_cast(float, u.x & 0xFFFF0000u),
+                                       __builtin_bit_cast(float, u.y << 16),
+                                       __builtin_bit_cast(float, u.y & 0xFFFF0000u));
+            s4[q][2 * h + 1] = make_float4(__builtin_bit_cast(float, u.z << 16),
+                                           __builtin_bit_cast(float, u.z & 0xFFFF0000u),
+                                           __builtin_bit_cast(float, u.w << 16),
+                                           __builtin_bit_cast(float, u.w & 0xFFFF0000u));
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s4[q][i] = lds_f4(sp + 64 * c + 16 * i);
+        }
       }
-      load_w(u, range_block(ks, j + P));
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const int r = rw * 16 * FM + f * 16 + (lane & 15);
+        const lds_i8* pp = stage + STAGE + SCB + (ks * 2 * MT + r) * 16;
+        a4[f] = lds_f4(pp);
+        const u32x4 z4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            pp + MT * 16);
+        zq[f] = make_int4((int)z4.x, (int)z4.y, (int)z4.z, (int)z4.w);
+        if (!live) a4[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < FN; ++q) cw4[q] = wr[u][q];
+      load_w((u + P) % PR, range_block(ks, j + P));
 #pragma unroll
       for (int t2 = 0; t2 < 4; t2 += 2) {
-        v4i d[2][FM][FN], e[2][FM][FN];
+        v4i d[2][FM][FN];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int t = t2 + h;
@@ -810,13 +880,19 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
             const uint32_t wd = h == 0 ? (t2 == 0 ? cw4[q].x : cw4[q].z)
                                        : (t2 == 0 ? cw4[q].y : cw4[q].w);
             const long bop = (long)(((uint64_t)nib_hi16(wd) << 32) | nib_lo16(wd));
+            // 16 * sum w of the group, the same for every row
+            const v4i ws16 = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                bop, (long)0x0101010101010101LL, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
             for (int f = 0; f < FM; ++f) {
               const long aop = (long)(((uint64_t)ca[f][t].y << 32) | ca[f][t].x);
               const int32_t z = t == 0 ? zq[f].x : (t == 1 ? zq[f].y : (t == 2 ? zq[f].z : zq[f].w));
-              const long zop = (long)((uint64_t)(uint8_t)(int8_t)z * 0x0101010101010101ull);
-              d[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, aop, v4i{0, 0, 0, 0}, 0, 0, 0);
-              e[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, zop, v4i{0, 0, 0, 0}, 0, 0, 0);
+              const uint32_t nz = ~__builtin_amdgcn_perm((uint32_t)z, (uint32_t)z, 0u);
+              const long zop = (long)(((uint64_t)nz << 32) | nz);
+              // 16 * (sum w + sum q*w + sum (-za - 1)*w) = 16 * sum (q - za)*w
+              d[h][f][q] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                  bop, zop, __builtin_amdgcn_mfma_i32_16x16x32_i8(bop, aop, ws16, 0, 0, 0), 0,
+                  0, 0);
             }
           }
         }
@@ -832,8 +908,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
               for (int i = 0; i < 4; ++i) {
                 const float4 k4 = s4[q][i];
                 const float sc = t == 0 ? k4.x : (t == 1 ? k4.y : (t == 2 ? k4.z : k4.w));
-                acc[h][f][q][i] = __builtin_fmaf(ar * sc, (float)(d[h][f][q][i] - e[h][f][q][i]),
-                                                 acc[h][f][q][i]);
+                acc[h][f][q][i] = __builtin_fmaf(ar * sc, (float)d[h][f][q][i], acc[h][f][q][i]);
               }
           }
         }
@@ -922,10 +997,11 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   // Loads issued after stage j+1's direct loads, in the steady state: the
   // weights refilled by step j+2-R, and R-2 whole steps (direct loads and a
   // weight refill each).  Earlier stages were drained in the prologue.
-  // loads per weight refill: weights and scales (kBQ: four scale vectors
-  // and the rows' two parameter vectors; asymmetric: the offsets too)
-  constexpr int LW = kBQ ? 5 * FN + 2 * FM : (kAsym ? 3 * FN : 2 * FN);
-  constexpr int A_WAIT = LW + (R - 2) * (ND + LW);
+  // loads per weight refill: weights and scales (kBQ: the weights only;
+  // asymmetric: the offsets too); direct loads per stage: the codes (kBQ:
+  // and the scale and parameter pieces)
+  constexpr int LW = kBQ ? FN : (kAsym ? 3 * FN : 2 * FN);
+  constexpr int A_WAIT = LW + (R - 2) * (ND + NS + NP + LW);
   static_assert(A_WAIT < 64, "vmcnt range");
   // The step loop is unrolled by PR so the weight ring index is static.
   for (int j0 = 0; j0 < bpw; j0 += PR) {
@@ -940,6 +1016,18 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       step(u, j);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kBQ) {  // the f32 chains of these PR blocks into the f64 sums
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int q = 0; q < FN; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            accd[f][q][i] = accd[f][q][i] + (double)(acc[0][f][q][i] + acc[1][f][q][i]);
+            acc[0][f][q][i] = 0.0f;
+            acc[1][f][q][i] = 0.0f;
+          }
+    }
   }
   wait_vmcnt<0>();  // the clamped direct loads must land before the workgroup ends
 
@@ -951,6 +1039,8 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (kAsym)
+          out[f][q][i] = (float)accd[f][q][i];
+        else if constexpr (kBQ)
           out[f][q][i] = (float)accd[f][q][i];
         else
           out[f][q][i] = acc[0][f][q][i] + acc[1][f][q][i];
@@ -1284,13 +1374,7 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
   hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, PERM, KIND, false, PW, kExact>), grid, \
                      dim3(256), 0, \
                      stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, (int64_t)0)
-#define QP_GEMM_BQ(KIND)                                                                      \
-  hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, KIND, true>), grid, dim3(256), \
-                     0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz)
-  if (ldsz > 0) {  // per-block activation parameters
-    if (w.kind == 1) QP_GEMM_BQ(1);
-    else QP_GEMM_BQ(0);
-  } else if (perm) {
+  if (perm) {
     if (w.kind == 1) QP_GEMM(true, 1);
     else if (w.kind == 2) QP_GEMM(true, 2);
     else QP_GEMM(true, 0);
@@ -1300,8 +1384,26 @@ qp_status launch_gemm_cfg(const int8_t* qa, int64_t lda, bool perm, const float*
     else QP_GEMM(false, 0);
   }
 #undef QP_GEMM
-#undef QP_GEMM_BQ
   return check_launch("a8w4 gemm");
+}
+
+// Per-block activation parameters (sa, za are [M][ldsz]), row-major codes.
+template <int FM, int FN, int RW, int CW, int KS, int PW, bool kExact>
+qp_status launch_gemm_bq_cfg(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
+                             int64_t M, const W4& w, const float* bias, float lo, float hi,
+                             float* Y, int64_t ldy, int64_t ldsz, hipStream_t stream) {
+  static_assert(64 % (16 * FN * CW) == 0, "channel tiles must tile the 64-channel padding");
+  const unsigned bx = (unsigned)ceil_div(w.N, 16 * FN * CW);
+  const int64_t by = ceil_div(M, 16 * FM * RW);
+  QP_REQUIRE(by <= 65535, QP_EUNSUPPORTED, "a8w4: M too large");
+  const dim3 grid(bx, (unsigned)by);
+  if (w.kind == 1)
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, 1, true, PW, kExact>), grid,
+                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz);
+  else
+    hipLaunchKernelGGL((a8w4_gemm_kernel<FM, FN, RW, CW, KS, false, 0, true, PW, kExact>), grid,
+                       dim3(256), 0, stream, qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy, ldsz);
+  return check_launch("a8w4 gemm (per-block activations)");
 }
 
 template <int BPW, bool kPerm, int kKind, bool kExact>
@@ -1367,11 +1469,26 @@ qp_status launch_gemm(const int8_t* qa, int64_t lda, bool perm, const float* sa,
   // <FM, FN, RW, CW, KS>: rows per workgroup 16*FM*RW, channels 16*FN*CW.
   // Small M splits K over the waves (enough waves stream the weights); larger
   // M shares each staged activation row among several channel groups.
+  // Exact K ranges (a multiple of 2*PW blocks each) drop the range tests and
+  // hold two weight blocks in flight in a four-slot ring.
+  if (ldsz > 0) {
+    if (M <= 16) {
+      if (nblocks % 16 == 0)
+        return launch_gemm_bq_cfg<1, 1, 1, 1, 4, 2, true>(qa, lda, sa, za, M, w, bias, lo, hi, Y,
+                                                          ldy, ldsz, stream);
+      return launch_gemm_bq_cfg<1, 1, 1, 1, 4, 2, false>(qa, lda, sa, za, M, w, bias, lo, hi, Y,
+                                                         ldy, ldsz, stream);
+    }
+    if (nblocks % 4 == 0)
+      return launch_gemm_bq_cfg<2, 1, 1, 4, 1, 2, true>(qa, lda, sa, za, M, w, bias, lo, hi, Y,
+                                                        ldy, ldsz, stream);
+    return launch_gemm_bq_cfg<2, 1, 1, 4, 1, 2, false>(qa, lda, sa, za, M, w, bias, lo, hi, Y,
+                                                       ldy, ldsz, stream);
+  }
   if (M <= 16)
     return launch_gemm_cfg<1, 1, 1, 1, 4>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
-  // (the per-block variant holds more per row fragment: two fragments a wave)
-  if (M <= 32 || ldsz > 0)
+  if (M <= 32)
     return launch_gemm_cfg<2, 1, 1, 4, 1>(qa, lda, perm, sa, za, M, w, bias, lo, hi, Y, ldy,
                                           ldsz, stream);
   // 64 rows x 32 channels a workgroup (two row and two channel groups):

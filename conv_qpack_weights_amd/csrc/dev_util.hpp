@@ -38,4 +38,14 @@ __device__ __forceinline__ void dma16_to_lds(const void* base, lds_void_t* dst, 
 #endif
 }
 
+// The same with 4 bytes per lane (lane i lands at dst + 4*i).
+__device__ __forceinline__ void dma4_to_lds(const void* base, lds_void_t* dst, uint32_t voff,
+                                            uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000), dst,
+      4, voff, soff, 0, 0);
+#endif
+}
+
 }  // namespace qp

@@ -254,7 +254,12 @@ def test_a8w4_blockq_gemm_workload(qp, orc, M):
                                                 (5, 77, 1000, True, "f32"),
                                                 (17, 100, 256, False, "bf16"),
                                                 (33, 48, 160, True, "f32"),
-                                                (130, 48, 320, False, "f32")])
+                                                (130, 48, 320, False, "f32"),
+                                                (3, 40, 2048, False, "bf16"),
+                                                (16, 70, 2100, True, "f32"),
+                                                (18, 100, 1000, False, "bf16"),
+                                                (40, 64, 40000, False, "f32"),
+                                                (97, 130, 2048, True, "f32")])
 def test_a8w4_blockq_shapes(qp, orc, M, N, K, prequant, sdt):
     _case_bq(qp, orc, synth.a8w4(synth.BASE_SEED + 17 * M + N + K, M, N, K), prequant=prequant,
              scale_dtype=sdt)
