@@ -48,6 +48,9 @@ def _args():
     p.add_argument("--a8w4-n", type=int, default=11008, metavar="N",
                    help="output channels of the --a8w4-only run (11008; 4096 for the GEMV "
                         "workload)")
+    p.add_argument("--blockq", action="store_true",
+                   help="with --a8w4-only: activations quantized per block of 32 instead of "
+                        "per row")
     return p.parse_args()
 
 
@@ -140,12 +143,18 @@ def main():
         Xo = torch.from_numpy(go["X"]).to(dev)
         bias_o = torch.from_numpy(go["bias"]).to(dev)
         Yo = torch.empty((Mo, No), dtype=torch.float32, device=dev)
-        wso = torch.empty(max(qp.qgemm_a8w4_blockwise_f32_ws_size(Mo, io), 256),
-                          dtype=torch.uint8, device=dev)
-        for _ in range(5):
-            qp.qgemm_a8w4_blockwise_f32(Xo, bo, io, bias_o, -6.0, 6.0, out=Yo, ws=wso)
+        if a.blockq:
+            wso = torch.empty(max(qp.qgemm_a8w4_blockq_f32_ws_size(Mo, io), 256),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(5):
+                qp.qgemm_a8w4_blockq_f32(Xo, bo, io, bias_o, -6.0, 6.0, out=Yo, ws=wso)
+        else:
+            wso = torch.empty(max(qp.qgemm_a8w4_blockwise_f32_ws_size(Mo, io), 256),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(5):
+                qp.qgemm_a8w4_blockwise_f32(Xo, bo, io, bias_o, -6.0, 6.0, out=Yo, ws=wso)
         torch.cuda.synchronize()
-        print(json.dumps({"a8w4_only_M": Mo, "N": No, "launches": 5}))
+        print(json.dumps({"a8w4_only_M": Mo, "N": No, "launches": 5, "blockq": a.blockq}))
         return
 
     def d(x):
