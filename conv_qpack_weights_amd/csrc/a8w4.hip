@@ -1098,16 +1098,18 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 }
 
 // ---- GEMM for at most 16 rows and K <= 4096 --------------------------------
-// A workgroup of 8 waves covers 32 channels (two 16-channel tiles) and all
-// of K: wave w takes tile w%2 and K range w/2 (a quarter of the 128-K
-// blocks, at most BPW).  The 16 rows of activation codes go from memory
+// A workgroup of 4*TPW waves covers TPW 16-channel tiles (two or three) and
+// all of K: wave w takes tile w%TPW and K range w/TPW (a quarter of the
+// 128-K blocks, at most BPW).  The 16 rows of activation codes go from memory
 // straight into LDS once per workgroup (rows padded by 16 bytes, so that
 // the 16 rows a read instruction touches fall in different banks); every
 // activation read after that is an LDS read.  Reading the codes from
 // memory in every wave instead (16 KiB per wave, the same lines in every
 // workgroup) measured slower than the whole weight stream.  Two tiles a
 // workgroup measured fastest of one, two and four (one: the codes are read
-// twice as often; four: a quarter of the CUs get no workgroup).
+// twice as often; four: a quarter of the CUs get no workgroup); three, where
+// they fit one workgroup a CU, beat two that put two workgroups on some CUs
+// (11008 channels: 13.9-14.2 against 15.0 us with the row quantization).
 // Each wave issues every weight and scale load of its range before it
 // waits for anything; it then waits only for the codes (issued first, so
 // complete first) and computes block by block as the weights arrive.  The
@@ -1115,25 +1117,32 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 // block is that of a8w4_gemm_kernel.
 // kExact: K is exactly four ranges of BPW blocks, so every block of every
 // range is real and the scales need no zeroing.
-template <int BPW, bool kPerm, int kKind, bool kExact = false>
-__global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
+template <int BPW, bool kPerm, int kKind, bool kExact = false, int TPW = 2>
+__global__ __launch_bounds__(TPW * 256) void a8w4_gemm_m16_kernel(
     const int8_t* __restrict__ qa, int64_t lda, const float* __restrict__ sa_g,
     const int32_t* __restrict__ za_g, int64_t M, W4 w, const float* __restrict__ bias, float lo,
     float hi, float* __restrict__ Y, int64_t ldy) {
   constexpr bool kBf16 = kKind == 1, kAsym = kKind == 2;
   constexpr int ES = kBf16 ? 2 : 4;  // bytes per stored scale
+  constexpr int NW = 4 * TPW;        // waves: TPW tiles x 4 K ranges
   extern __shared__ __attribute__((aligned(16))) int8_t a_lds[];  // [16][Kpad + 16]
-  __shared__ float red[3][2][4][64];
+  __shared__ float red[3][TPW][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tq = wave & 1;   // the wave's tile
-  const int ks = wave >> 1;  // and K range
+  const int tq = wave % TPW;  // the wave's tile
+  const int ks = wave / TPW;  // and K range
   const int c = lane >> 4;
-  // tiles w and w + G of the G-workgroup grid (2G <= Npad/16): neighbouring
-  // workgroups read neighbouring tiles, which measured 12% faster than
-  // tiles 2w, 2w+1 with the weights cache-resident (the same cold)
-  const int64_t tile = (int64_t)tq * gridDim.x + blockIdx.x;
+  // tiles w, w + G, ... of the G-workgroup grid: neighbouring workgroups
+  // read neighbouring tiles, which measured 12% faster than consecutive
+  // tiles per workgroup with the weights cache-resident (the same cold).
+  // A grid that covers the tiles unevenly gives its last tiles' waves the
+  // final tile again: they load and compute like the others (every wave
+  // takes part in the barriers) and store nothing.
+  const int64_t ntile = w.Npad / 16;
+  const int64_t tile_g = (int64_t)tq * gridDim.x + blockIdx.x;
+  const bool tile_real = tile_g < ntile;
+  const int64_t tile = tile_real ? tile_g : ntile - 1;
   const int64_t nblocks = w.Kpad / 128;
   const int64_t bpw = (nblocks + 3) / 4;
   const int64_t b0 = ks * bpw;
@@ -1144,8 +1153,7 @@ __global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
   // (a piece: 64 lanes x 16 bytes of one row); wave w takes pieces
   // w, w+8, ...  Rows past M repeat row M-1 (their outputs are not written).
   const int ppr = (int)((w.Kpad + 1023) / 1024);  // pieces per row (<= 4)
-  for (int i = 0; i < 2 * ppr; ++i) {
-    const int pc = wave + 8 * i;
+  for (int pc = wave; pc < 16 * ppr; pc += NW) {
     const int r = pc / ppr, j = pc - r * ppr;
     const int64_t rr = r < M ? r : M - 1;
     if (j * 1024 + lane * 16 < w.Kpad)
@@ -1254,7 +1262,7 @@ __global__ __launch_bounds__(512) void a8w4_gemm_m16_kernel(
     for (int i = 0; i < 4; ++i) red[ks - 1][tq][i][lane] = out[i];
   }
   __syncthreads();
-  if (ks != 0) return;
+  if (ks != 0 || !tile_real) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1406,11 +1414,11 @@ qp_status launch_gemm_bq_cfg(const int8_t* qa, int64_t lda, const float* sa, con
   return check_launch("a8w4 gemm (per-block activations)");
 }
 
-template <int BPW, bool kPerm, int kKind, bool kExact>
-qp_status launch_gemm_m16_one(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
+template <int BPW, bool kPerm, int kKind, bool kExact, int TPW>
+qp_status launch_gemm_m16_tpw(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
                               int64_t M, const W4& w, const float* bias, float lo, float hi,
                               float* Y, int64_t ldy, hipStream_t stream) {
-  auto kern = a8w4_gemm_m16_kernel<BPW, kPerm, kKind, kExact>;
+  auto kern = a8w4_gemm_m16_kernel<BPW, kPerm, kKind, kExact, TPW>;
   // The LDS limit is raised once per instantiation and device, for the
   // deepest K the instantiation takes (threads may race to set it;
   // repeating it is harmless).
@@ -1426,9 +1434,33 @@ qp_status launch_gemm_m16_one(const int8_t* qa, int64_t lda, const float* sa, co
     lds_attr_devices.fetch_or(bit, std::memory_order_release);
   }
   const size_t lds = (size_t)16 * (w.Kpad + 16);
-  hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(w.N, 32)), dim3(512), lds, stream, qa, lda,
-                     sa, za, M, w, bias, lo, hi, Y, ldy);
+  const int64_t ntile = w.Npad / 16;
+  hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(ntile, TPW)), dim3(TPW * 256), lds, stream,
+                     qa, lda, sa, za, M, w, bias, lo, hi, Y, ldy);
   return check_launch("a8w4 gemm (up to 16 rows)");
+}
+
+// Two or three 16-channel tiles a workgroup, whichever leaves the fewest
+// tiles on the busiest CU (one workgroup of either size per CU while the
+// grid fits 256 CUs; ties go to two): 11008 channels (688 tiles) take
+// three, 230 workgroups of at most one a CU, against 344 workgroups of two,
+// which put four tiles on 88 CUs.
+inline int m16_tiles_per_workgroup(const W4& w) {
+  const int64_t t = w.Npad / 16;
+  const int64_t busiest2 = 2 * ceil_div(ceil_div(t, 2), 256);
+  const int64_t busiest3 = 3 * ceil_div(ceil_div(t, 3), 256);
+  return busiest3 < busiest2 ? 3 : 2;
+}
+
+template <int BPW, bool kPerm, int kKind, bool kExact>
+qp_status launch_gemm_m16_one(const int8_t* qa, int64_t lda, const float* sa, const int32_t* za,
+                              int64_t M, const W4& w, const float* bias, float lo, float hi,
+                              float* Y, int64_t ldy, hipStream_t stream) {
+  if (m16_tiles_per_workgroup(w) == 3)
+    return launch_gemm_m16_tpw<BPW, kPerm, kKind, kExact, 3>(qa, lda, sa, za, M, w, bias, lo, hi,
+                                                             Y, ldy, stream);
+  return launch_gemm_m16_tpw<BPW, kPerm, kKind, kExact, 2>(qa, lda, sa, za, M, w, bias, lo, hi, Y,
+                                                           ldy, stream);
 }
 
 template <int BPW>

@@ -68,7 +68,10 @@ def test_a8w4_gemm_workload(qp, orc, M):
                                    # grids whose workgroups are placed by XCD (row groups
                                    # of a channel group together), exact and ragged K
                                    (16, 40, 4096), (60, 250, 512), (100, 330, 512),
-                                   (100, 250, 640)])
+                                   (100, 250, 640),
+                                   # 513..768 channel tiles: three tiles a workgroup at
+                                   # M <= 16, the grid's last waves on a repeated tile
+                                   (5, 8300, 1000), (16, 9050, 4096), (2, 12280, 384)])
 def test_a8w4_small_shapes_and_tails(qp, orc, M, N, K):
     _case(qp, orc, synth.a8w4(synth.BASE_SEED + 7 * M + N + K, M, N, K))
 
