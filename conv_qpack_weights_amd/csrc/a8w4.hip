@@ -1151,7 +1151,7 @@ __global__ __launch_bounds__(TPW * 256) void a8w4_gemm_m16_kernel(
 
   // ---- the codes: 16 rows x Kpad bytes straight into LDS, in 1 KiB pieces
   // (a piece: 64 lanes x 16 bytes of one row); wave w takes pieces
-  // w, w+8, ...  Rows past M repeat row M-1 (their outputs are not written).
+  // w, w+NW, ...  Rows past M repeat row M-1 (their outputs are not written).
   const int ppr = (int)((w.Kpad + 1023) / 1024);  // pieces per row (<= 4)
   for (int pc = wave; pc < 16 * ppr; pc += NW) {
     const int r = pc / ppr, j = pc - r * ppr;
@@ -1161,6 +1161,30 @@ __global__ __launch_bounds__(TPW * 256) void a8w4_gemm_m16_kernel(
                    (uint32_t)(rr * lda + j * 1024 + lane * 16), 0);
   }
   __builtin_amdgcn_sched_barrier(0);  // the codes' loads first
+
+  // ---- the epilogue operands of the waves that write the tile (K range 0),
+  // issued before the weights: loaded after the last barrier they put a
+  // memory round trip (the weight sums live in the cold blob) between the
+  // final sums and the stores of every workgroup, which measured about
+  // 1 us at 16 x 11008.  Issued ahead of the weights, the waits for the
+  // weights stay the same in every wave.  Every load is unconditional
+  // (clamped indices, a stand-in array where there is no bias).
+  constexpr int NL = (kAsym ? 3 : 2) * BPW;  // weight-side loads of a wave
+  const int64_t n_e = tile * 16 + (lane & 15);
+  float ws_e = 0.0f, bn_e = 0.0f, sa_e[4] = {0.f, 0.f, 0.f, 0.f};
+  int32_t za_e[4] = {0, 0, 0, 0};
+  if (ks == 0) {
+    const int64_t nb_c = n_e < w.N ? n_e : w.N - 1;
+    ws_e = w.wsum[n_e];  // [Npad]
+    bn_e = (bias ? bias : w.wsum)[nb_c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = 4 * c + i < M ? 4 * c + i : M - 1;
+      sa_e[i] = sa_g[m];
+      za_e[i] = za_g[m];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- every weight and scale load of the range (blocks past the range
   // read the range's last real block and get zero scales below)
@@ -1177,9 +1201,9 @@ __global__ __launch_bounds__(TPW * 256) void a8w4_gemm_m16_kernel(
     sr[u] = load_scale4<kBf16>(sp + 64 * ES * b);
     if constexpr (kAsym) orr[u] = load_scale4<false>(op + 256 * b);
   }
-  // the codes (issued first, so complete first) are in LDS once no more
-  // than the weight loads are outstanding
-  wait_vmcnt<kAsym ? 3 * BPW : 2 * BPW>();
+  // the codes (issued first, so complete first; then the epilogue
+  // operands) are in LDS once no more than the weight loads are outstanding
+  wait_vmcnt<NL>();
   __syncthreads();
 
   float acc[2][4];
@@ -1267,14 +1291,12 @@ __global__ __launch_bounds__(TPW * 256) void a8w4_gemm_m16_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 3; ++r) out[i] = out[i] + red[r][tq][i][lane];
-  const int64_t n = tile * 16 + (lane & 15);
-  if (n >= w.N) return;
-  const float ws = w.wsum[n];
-  const float bn = bias ? bias[n] : 0.0f;
+  if (n_e >= w.N) return;
+  const float bn = bias ? bn_e : 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t m = 4 * c + i;
-    if (m < M) Y[m * ldy + n] = finish(out[i], sa_g[m], za_g[m], ws, bn, lo, hi);
+    if (m < M) Y[m * ldy + n_e] = finish(out[i], sa_e[i], za_e[i], ws_e, bn, lo, hi);
   }
 }
 
