@@ -991,6 +991,42 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   for (int j = 0; j < R - 1; ++j) issue_stage(j);
 #pragma unroll
   for (int u = 0; u < P; ++u) load_w(u, range_block(ks, u));
+  // With K split over the waves (KS > 1) the epilogue operands of the
+  // writing waves (K range 0) come in with the prologue, which is drained
+  // anyway: loaded after the last barrier they put a memory round trip (the
+  // weight sums live in the cold blob) between the final sums and the
+  // stores.  Unconditional loads (clamped indices, a stand-in array where
+  // there is no bias).  With KS = 1 they are loaded at the end: held in
+  // registers through the loop they would cost a wave a SIMD (and staged
+  // in an LDS array of their own they made the compiler drain the direct
+  // loads at every step).
+  constexpr bool kEpPre = KS > 1;
+  constexpr int EW = kEpPre ? (kBQ ? 4 : 1) : 1;  // channel values per fragment
+  float e_ws[kEpPre ? FN : 1], e_bn[kEpPre ? FN : 1][EW], e_sa[kEpPre && !kBQ ? FM : 1][4];
+  int32_t e_za[kEpPre && !kBQ ? FM : 1][4];
+  if constexpr (kEpPre) {
+    if (ks == 0) {
+#pragma unroll
+      for (int q = 0; q < FN; ++q) {
+#pragma unroll
+        for (int i = 0; i < EW; ++i) {
+          const int64_t n = n0 + q * 16 + (kBQ ? 4 * c + i : (lane & 15));
+          e_bn[q][i] = (bias ? bias : w.wsum)[n < w.N ? n : w.N - 1];
+          if (!kBQ) e_ws[q] = w.wsum[n];
+        }
+      }
+      if constexpr (!kBQ) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t m = mw + rw * 16 * FM + f * 16 + 4 * c + i;
+            e_sa[f][i] = sa_g[m < M ? m : M - 1];
+            e_za[f][i] = za_g[m < M ? m : M - 1];
+          }
+      }
+    }
+  }
   wait_vmcnt<0>();
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): settle the scalar loads too
 
@@ -1076,7 +1112,12 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t n = n0 + q * 16 + 4 * c + i;
-          if (n < w.N) Y[m * ldy + n] = finish_bq(out[f][q][i], bias ? bias[n] : 0.0f, lo, hi);
+          float bn = 0.0f;
+          if (bias) {
+            if constexpr (kEpPre) bn = e_bn[q][i];
+            else bn = bias[n];
+          }
+          if (n < w.N) Y[m * ldy + n] = finish_bq(out[f][q][i], bn, lo, hi);
         }
     }
     return;
@@ -1085,14 +1126,25 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   for (int q = 0; q < FN; ++q) {
     const int64_t n = n0 + q * 16 + (lane & 15);
     if (n >= w.N) continue;
-    const float ws = w.wsum[n];
-    const float bn = bias ? bias[n] : 0.0f;
+    float ws, bn = 0.0f;
+    if constexpr (kEpPre) {
+      ws = e_ws[q];
+      if (bias) bn = e_bn[q][0];
+    } else {
+      ws = w.wsum[n];
+      if (bias) bn = bias[n];
+    }
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = mw + rw * 16 * FM + f * 16 + 4 * c + i;
-        if (m < M) Y[m * ldy + n] = finish(out[f][q][i], sa_g[m], za_g[m], ws, bn, lo, hi);
+        if (m < M) {
+          if constexpr (kEpPre)
+            Y[m * ldy + n] = finish(out[f][q][i], e_sa[f][i], e_za[f][i], ws, bn, lo, hi);
+          else
+            Y[m * ldy + n] = finish(out[f][q][i], sa_g[m], za_g[m], ws, bn, lo, hi);
+        }
       }
   }
 }

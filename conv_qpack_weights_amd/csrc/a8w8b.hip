@@ -187,6 +187,34 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
   for (int j = 0; j < R - 1; ++j) issue_stage(j);
 #pragma unroll
   for (int u = 0; u < P; ++u) load_w(u, range_step(ks, u));
+  // The epilogue operands of the waves that write (K range 0) come in with
+  // the prologue, which is drained anyway: loaded after the last barrier
+  // they would put a memory round trip (the weight sums live in the cold
+  // blob) between the final sums and the stores.  Unconditional loads
+  // (clamped indices, a stand-in array where there is no bias).
+  float ws_e = 0.0f, bn_e = 0.0f, sa_e[FM][4];
+  int32_t za_e[FM][4];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa_e[f][i] = 0.0f;
+      za_e[f][i] = 0;
+    }
+  if (ks == 0) {
+    const int64_t nc = n < w.N ? n : w.N - 1;
+    ws_e = w.wsum[nc];
+    bn_e = (bias ? bias : w.wsum)[nc];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mw + f * 16 + 4 * c + i;
+        const int64_t mc = m < M ? m : M - 1;
+        sa_e[f][i] = sa_g[mc];
+        za_e[f][i] = za_g[mc];
+      }
+  }
   wait_vmcnt<0>();
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
@@ -230,14 +258,13 @@ __global__ __launch_bounds__(256) void a8w8b_gemm_kernel(const int8_t* __restric
         for (int r = 0; r < KS - 1; ++r) out[f][i] = out[f][i] + red[cw * (KS - 1) + r][f][i][lane];
   }
   if (n >= w.N) return;
-  const float ws = w.wsum[n];
-  const float bn = bias ? bias[n] : 0.0f;
+  const float bn = bias ? bn_e : 0.0f;
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = mw + f * 16 + 4 * c + i;
-      if (m < M) Y[m * ldy + n] = finish_w8(out[f][i], sa_g[m], za_g[m], ws, bn, lo, hi);
+      if (m < M) Y[m * ldy + n] = finish_w8(out[f][i], sa_e[f][i], za_e[f][i], ws_e, bn, lo, hi);
     }
 }
 
