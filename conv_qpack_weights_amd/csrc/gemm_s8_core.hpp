@@ -101,15 +101,17 @@ __device__ __forceinline__ int64_t rhe_shift64(int32_t acc, int32_t m0, int32_t 
 
 // The same rounding when sh >= 32, in 32-bit pieces: u = t + 2^(sh-1) (one
 // 32x32+64 multiply-add); floor(u / 2^sh) is the high word shifted by sh-32;
-// u being a multiple of 2^sh marks an exact tie, which rounds to even.
+// u being a multiple of 2^sh marks an exact tie t/2^sh = r - 1/2, whose
+// even neighbour is r with its lowest bit cleared (r - 1 when r is odd, r
+// when even, in two's complement for either sign).
 __device__ __forceinline__ int32_t rhe_shift_hi(int32_t acc, int32_t m0, int64_t half,
                                                 int32_t s2, uint32_t mask) {
   const int64_t u = (int64_t)acc * (int64_t)m0 + half;
   const int32_t hi = (int32_t)(u >> 32);
   const uint32_t lo = (uint32_t)u;
-  int32_t r = hi >> s2;
-  const bool tie = (lo == 0u) & (((uint32_t)hi & mask) == 0u);
-  return r - (int32_t)(tie & (r & 1));
+  const int32_t r = hi >> s2;
+  const bool tie = (lo | ((uint32_t)hi & mask)) == 0u;
+  return tie ? (r & ~1) : r;
 }
 
 __device__ __forceinline__ int32_t clamp_i64(int64_t v, int32_t lo, int32_t hi) {
@@ -118,8 +120,12 @@ __device__ __forceinline__ int32_t clamp_i64(int64_t v, int32_t lo, int32_t hi) 
   return (int32_t)v;
 }
 
+// One v_med3_i32 (the compiler forms it from min/max only for constant
+// bounds); lo <= hi, so the median of (v, lo, hi) is v clamped to [lo, hi].
 __device__ __forceinline__ int32_t clamp_i32(int32_t v, int32_t lo, int32_t hi) {
-  return min(max(v, lo), hi);
+  int32_t r;
+  asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(lo), "s"(hi));
+  return r;
 }
 
 // Chunk c of LDS row r sits at chunk position c ^ swz(r): conflict-free
