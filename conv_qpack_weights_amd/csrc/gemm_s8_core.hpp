@@ -562,6 +562,29 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   auto outputs = [&](int i, int q, int j, const v4i& cc, const v4i& mm, const v4i& ss,
                      const v4i& zb, const int64_t (&half)[4], const int32_t (&s2)[4],
                      const uint32_t (&mask)[4], int32_t (&out)[4]) {
+    if constexpr (kShiftHi && !kF32 && !kOut32) {
+      // The rounding in 32-bit pieces with the exact-tie step taken only
+      // when some lane of the wave meets a tie among these four outputs
+      // (rare on real data): the common path is the rounded-up quotient.
+      int32_t rq[4];
+      bool tie[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
+        if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
+        const int64_t u = (int64_t)(int32_t)a * (int64_t)mm[r] + half[r];
+        const int32_t hi = (int32_t)(u >> 32);
+        rq[r] = hi >> s2[r];
+        tie[r] = ((uint32_t)u | ((uint32_t)hi & mask[r])) == 0u;
+      }
+      if (__builtin_amdgcn_ballot_w64(tie[0] | tie[1] | tie[2] | tie[3]) != 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rq[r] = tie[r] ? (rq[r] & ~1) : rq[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[r] = clamp_i32(rq[r] + g.zp_out, lo_v, g.hi);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
