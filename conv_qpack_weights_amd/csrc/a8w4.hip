@@ -641,7 +641,14 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   // own K range's, which the piece mapping below gives for one tile a
   // workgroup, four K ranges and one scale piece a thread)
   static_assert(!kBQ || !kPrivA || (KS == 4 && CW * FN == 1 && NS == 1), "kBQ wave-private ring");
-  __shared__ __attribute__((aligned(16))) int8_t ring[R * STRIDE];
+  // KS = 1: behind the stages, the epilogue operands of the workgroup's
+  // channels and rows ([NCH] weight sums, [NCH] biases, [MT] row scales,
+  // [MT] row zero points), written once after the prologue
+  constexpr int NCH = CW * FN * 16;  // channels per workgroup
+  constexpr bool kEpLds = KS == 1;
+  constexpr int EPB = kEpLds ? (2 * NCH + 2 * MT) * 4 : 0;
+  static_assert(!kEpLds || (NCH <= 256 && MT <= 256), "one epilogue operand per thread");
+  __shared__ __attribute__((aligned(16))) int8_t ring[R * STRIDE + EPB];
   __shared__ float red[KS > 1 ? (KS - 1) * RW * CW : 1][FM][FN][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -991,15 +998,16 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
   for (int j = 0; j < R - 1; ++j) issue_stage(j);
 #pragma unroll
   for (int u = 0; u < P; ++u) load_w(u, range_block(ks, u));
-  // With K split over the waves (KS > 1) the epilogue operands of the
-  // writing waves (K range 0) come in with the prologue, which is drained
-  // anyway: loaded after the last barrier they put a memory round trip (the
+  // The epilogue operands come in with the prologue, which is drained
+  // anyway: loaded after the main loop they put a memory round trip (the
   // weight sums live in the cold blob) between the final sums and the
   // stores.  Unconditional loads (clamped indices, a stand-in array where
-  // there is no bias).  With KS = 1 they are loaded at the end: held in
-  // registers through the loop they would cost a wave a SIMD (and staged
-  // in an LDS array of their own they made the compiler drain the direct
-  // loads at every step).
+  // there is no bias).  With K split over the waves (KS > 1) the writing
+  // waves (K range 0) keep theirs in registers; with KS = 1 every wave
+  // writes, and registers held through the loop would cost a wave a SIMD,
+  // so one thread per channel and row loads them and they wait in LDS
+  // behind the ring's stages (in an LDS array of their own they made the
+  // compiler drain the direct loads at every step).
   constexpr bool kEpPre = KS > 1;
   constexpr int EW = kEpPre ? (kBQ ? 4 : 1) : 1;  // channel values per fragment
   float e_ws[kEpPre ? FN : 1], e_bn[kEpPre ? FN : 1][EW], e_sa[kEpPre && !kBQ ? FM : 1][4];
@@ -1027,8 +1035,41 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       }
     }
   }
+  const int64_t ng0 = (int64_t)cgi * NCH;  // the workgroup's first channel (ng0 + NCH <= Npad)
+  float* const ep_ws = reinterpret_cast<float*>(ring + R * STRIDE);
+  float* const ep_bn = ep_ws + NCH;
+  float* const ep_sa = ep_bn + NCH;
+  int32_t* const ep_za = reinterpret_cast<int32_t*>(ep_sa + MT);
+  float l_ws = 0.0f, l_bn = 0.0f, l_sa = 0.0f;
+  int32_t l_za = 0;
+  if constexpr (kEpLds) {
+    if (tid < NCH) {
+      const int64_t n = ng0 + tid;
+      if constexpr (!kBQ) l_ws = w.wsum[n];
+      l_bn = (bias ? bias : w.wsum)[n < w.N ? n : w.N - 1];
+    }
+    if constexpr (!kBQ) {
+      if (tid < MT) {
+        const int64_t m = mw + tid < M ? mw + tid : M - 1;
+        l_sa = sa_g[m];
+        l_za = za_g[m];
+      }
+    }
+  }
   wait_vmcnt<0>();
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): settle the scalar loads too
+  if constexpr (kEpLds) {
+    if (tid < NCH) {
+      ep_ws[tid] = l_ws;
+      ep_bn[tid] = l_bn;
+    }
+    if (tid < MT) {
+      ep_sa[tid] = l_sa;
+      ep_za[tid] = l_za;
+    }
+  }
+  // lgkmcnt(0): settle the scalar loads (and the LDS writes above, which the
+  // main loop's barriers order before the epilogue's reads)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
 
   // Loads issued after stage j+1's direct loads, in the steady state: the
   // weights refilled by step j+2-R, and R-2 whole steps (direct loads and a
@@ -1115,7 +1156,7 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
           float bn = 0.0f;
           if (bias) {
             if constexpr (kEpPre) bn = e_bn[q][i];
-            else bn = bias[n];
+            else bn = ep_bn[n - ng0];
           }
           if (n < w.N) Y[m * ldy + n] = finish_bq(out[f][q][i], bn, lo, hi);
         }
@@ -1131,8 +1172,8 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       ws = e_ws[q];
       if (bias) bn = e_bn[q][0];
     } else {
-      ws = w.wsum[n];
-      if (bias) bn = bias[n];
+      ws = ep_ws[n - ng0];
+      if (bias) bn = ep_bn[n - ng0];
     }
 #pragma unroll
     for (int f = 0; f < FM; ++f)
@@ -1140,10 +1181,12 @@ __global__ __launch_bounds__(256) void a8w4_gemm_kernel(const int8_t* __restrict
       for (int i = 0; i < 4; ++i) {
         const int64_t m = mw + rw * 16 * FM + f * 16 + 4 * c + i;
         if (m < M) {
-          if constexpr (kEpPre)
+          if constexpr (kEpPre) {
             Y[m * ldy + n] = finish(out[f][q][i], e_sa[f][i], e_za[f][i], ws, bn, lo, hi);
-          else
-            Y[m * ldy + n] = finish(out[f][q][i], sa_g[m], za_g[m], ws, bn, lo, hi);
+          } else {
+            const int ml = (int)(m - mw);  // the row within the workgroup
+            Y[m * ldy + n] = finish(out[f][q][i], ep_sa[ml], ep_za[ml], ws, bn, lo, hi);
+          }
         }
       }
   }
