@@ -113,23 +113,39 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
   const int64_t m0 = tile_m * BM + (KSP == 1 ? wave * FM * 16 : 0);
   const int64_t n0 = (int64_t)tile_n * BN;
 
-  // ---- per-column epilogue constants (read after the main loop) ----
+  // ---- per-column epilogue inputs: loaded now, ahead of the main loop's
+  // loads, and turned into constants after the loop.  Forming them here
+  // would wait for these loads before any pixel or weight load is issued:
+  // one memory round trip in front of the whole convolution.  The loads are
+  // unconditional (the column clamped into range, a stand-in array where
+  // there is no bias).
+  float e_sb = 0.0f;
+  int32_t e_zb = 0, e_bias = 0, e_cs = 0;
   if (!kBlk && tid < BN) {
-    const int64_t n = n0 + tid;
-    int32_t mm = 0, ss = 1, cc = 0, zb = 0;
-    if (n < g.N) {
-      derive_mult(g.sA, g.sB[n], g.sOut, &mm, &ss);
-      zb = g.zpB[n];
-      uint32_t c = (uint32_t)(g.bias ? g.bias[n] : 0);
-      c -= (uint32_t)g.zA * (uint32_t)g.colsum[n];
-      c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
-      cc = (int32_t)c;
-    }
-    col_m0[tid] = mm;
-    col_sh[tid] = ss;
-    col_c[tid] = cc;
-    col_zb[tid] = zb;
+    const int64_t nc = n0 + tid < g.N ? n0 + tid : g.N - 1;
+    e_sb = g.sB[nc];
+    e_zb = g.zpB[nc];
+    e_bias = (g.bias ? g.bias : g.zpB)[nc];
+    e_cs = g.colsum[nc];
   }
+  auto column_constants = [&]() {
+    if (!kBlk && tid < BN) {
+      const int64_t n = n0 + tid;
+      int32_t mm = 0, ss = 1, cc = 0, zb = 0;
+      if (n < g.N) {
+        derive_mult(g.sA, e_sb, g.sOut, &mm, &ss);
+        zb = e_zb;
+        uint32_t c = (uint32_t)(g.bias ? e_bias : 0);
+        c -= (uint32_t)g.zA * (uint32_t)e_cs;
+        c += (uint32_t)g.K * (uint32_t)g.zA * (uint32_t)zb;
+        cc = (int32_t)c;
+      }
+      col_m0[tid] = mm;
+      col_sh[tid] = ss;
+      col_c[tid] = cc;
+      col_zb[tid] = zb;
+    }
+  };
 
   // ---- this lane's pixels ----
   int32_t iy0[FM], ix0[FM];
@@ -282,6 +298,7 @@ __global__ __launch_bounds__(256) void conv_implicit_kernel(ConvKArgs g) {
     }
   }
   wait_vmcnt<0>();
+  column_constants();
   if constexpr (KSP > 1) {  // add the waves' partial sums (this barrier also publishes
                             // the column constants)
     if (wave > 0) {
