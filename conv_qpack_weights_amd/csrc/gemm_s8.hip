@@ -245,9 +245,15 @@ qp_status run_gemm_s8(const int8_t* A, int64_t M, int64_t lda, float sA, int32_t
     return p.rowsum ? launch_gemm_sel<true, true, false>(a, p.resident, stream)
                     : launch_gemm_sel<true, false, false>(a, p.resident, stream);
   // All shifts >= 32 <=> every multiplier < 1/2 (with margin for the m0
-  // rounding bump); known only when the scales were seen at pack time.
-  const bool hi = b->scale_max > 0.0f &&
-                  ((double)sA * (double)b->scale_max / (double)sOut) * (1.0 + 1e-6) < 0.5;
+  // rounding bump); known only when the scales were seen at pack time.  The
+  // kernel for this case also folds the zero-point terms and the output
+  // zero point into one 64-bit addend, which stays exact while every shift
+  // is at most 53, i.e. every multiplier is at least 2^-23 (smaller ones
+  // take the general 64-bit rounding).
+  const double m_hi = (double)sA * (double)b->scale_max / (double)sOut;
+  const double m_lo = (double)sA * (double)b->scale_min / (double)sOut;
+  const bool hi = b->scale_max > 0.0f && m_hi * (1.0 + 1e-6) < 0.5 &&
+                  m_lo * (1.0 - 1e-6) >= 0x1p-23;
   if (hi)
     return p.rowsum ? launch_gemm_sel<false, true, true>(a, p.resident, stream)
                     : launch_gemm_sel<false, false, true>(a, p.resident, stream);

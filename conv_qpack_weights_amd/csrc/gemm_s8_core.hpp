@@ -256,6 +256,10 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
 
   extern __shared__ __attribute__((aligned(1024))) int8_t smem[];
   __shared__ int32_t col_m0[BN], col_sh[BN], col_c[BN], col_zb[BN];
+  // kShiftHi: the column's whole 64-bit addend of the rounding step,
+  // c*m0 + 2^(sh-1) + zp_out*2^sh (c the zero-point and bias terms, exact)
+  constexpr bool kFold = kShiftHi && !kF32 && !kOut32;
+  __shared__ int64_t col_ad[kFold ? BN : 1];
   __shared__ int32_t row_sum[kResident ? BM : 1];
 
   const int tid = threadIdx.x;
@@ -449,6 +453,20 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
     col_sh[j] = ss;
     col_c[j] = cc;
     col_zb[j] = zb;
+    if constexpr (kFold) {
+      // (acc + c)*m0 + 2^(sh-1) + zp*2^sh is below 2^63 in magnitude: |acc + c|
+      // < 2^31 (the host's INT32 bound), m0 < 2^31, and the host takes this
+      // path only while every shift is at most 53; the addend itself is
+      // formed modulo 2^64, which the multiply-add's result is too.
+      uint64_t ad = 0;
+      if (n < g.N) {
+        const int64_t c64 = (int64_t)(g.bias ? bl : 0) - (int64_t)g.zA * (int64_t)csl +
+                            (int64_t)g.K * (int64_t)g.zA * (int64_t)zb;
+        ad = (uint64_t)c64 * (uint64_t)(int64_t)mm + ((uint64_t)1 << (ss - 1)) +
+             ((uint64_t)(int64_t)g.zp_out << ss);
+      }
+      col_ad[j] = (int64_t)ad;
+    }
   }
 
   accv acc[FN][FM];
@@ -562,15 +580,18 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
   auto outputs = [&](int i, int q, int j, const v4i& cc, const v4i& mm, const v4i& ss,
                      const v4i& zb, const int64_t (&half)[4], const int32_t (&s2)[4],
                      const uint32_t (&mask)[4], int32_t (&out)[4]) {
-    if constexpr (kShiftHi && !kF32 && !kOut32) {
-      // The rounding in 32-bit pieces with the exact-tie step taken only
-      // when some lane of the wave meets a tie among these four outputs
-      // (rare on real data): the common path is the rounded-up quotient.
+    if constexpr (kFold) {
+      // The rounding in 32-bit pieces, u = acc*m0 + the column's addend
+      // (zero-point terms times m0, the half, the output zero point times
+      // 2^sh: one multiply-add), so floor(u / 2^sh) is already the rounded-up
+      // quotient plus zp_out.  The exact-tie step runs only when some lane of
+      // the wave meets a tie among these four outputs (rare on real data);
+      // the tie's even neighbour is taken before the zero point is added.
       int32_t rq[4];
       bool tie[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint32_t a = (uint32_t)acc[i][j][4 * q + r] + (uint32_t)cc[r];
+        uint32_t a = (uint32_t)acc[i][j][4 * q + r];
         if (kRowSum) a -= (uint32_t)zb[r] * (uint32_t)rs[j];
         const int64_t u = (int64_t)(int32_t)a * (int64_t)mm[r] + half[r];
         const int32_t hi = (int32_t)(u >> 32);
@@ -579,10 +600,11 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
       }
       if (__builtin_amdgcn_ballot_w64(tie[0] | tie[1] | tie[2] | tie[3]) != 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rq[r] = tie[r] ? (rq[r] & ~1) : rq[r];
+        for (int r = 0; r < 4; ++r)
+          rq[r] = tie[r] ? ((rq[r] - g.zp_out) & ~1) + g.zp_out : rq[r];
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[r] = clamp_i32(rq[r] + g.zp_out, lo_v, g.hi);
+      for (int r = 0; r < 4; ++r) out[r] = clamp_i32(rq[r], lo_v, g.hi);
       return;
     }
 #pragma unroll
@@ -623,6 +645,10 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
         s2[r] = 0;
         half[r] = 0;
         mask[r] = 0;
+      } else if constexpr (kFold) {  // `half` carries the column's whole addend
+        s2[r] = (*ss)[r] - 32;
+        half[r] = col_ad[jn + r];
+        mask[r] = (1u << (s2[r] & 31)) - 1u;
       } else {
         s2[r] = (*ss)[r] - 32;
         half[r] = (int64_t)1 << ((*ss)[r] - 1);
