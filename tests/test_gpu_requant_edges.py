@@ -13,9 +13,10 @@ once:
     bias of column n are multiples of 2^b with b that valuation, so about
     half of the column's accumulators are exact ties (the test counts them in
     integers and requires many, rounding both up and down);
-  * all multipliers below 1/2 select the epilogue that rounds in 32-bit
-    pieces (shift >= 32); one multiplier of 1/2 or more selects the 64-bit
-    one (shift 21 for 1000, 29 for 3, 31 for 1/2 and 3/4);
+  * all multipliers in [2^-23, 1/2) select the epilogue that rounds in
+    32-bit pieces (shifts 32..53) from one folded 64-bit addend per column;
+    one multiplier of 1/2 or more (shift 21 for 1000, 29 for 3, 31 for 1/2
+    and 3/4), or one below 2^-23, selects the 64-bit one;
   * M = 2^-70 (shift >= 63: every output is the output zero point) and
     M = 2^30 (shift 0: every non-zero accumulator saturates);
   * ReLU with a non-zero output zero point; M = 2^31 (shift < 0) is refused.
@@ -49,8 +50,13 @@ def _host(t):
 _TIES_HI = ([(1.0, s, s - 1) for s in range(2, 9)] + [(0.75, s, s + 1) for s in range(1, 7)] +
             [(0.625, s, s + 2) for s in range(1, 6)])
 # no ties possible or wanted: shifts 32..61 away from the tie columns, and
-# M = 2^-70 (shift >= 63) in a launch that rounds in 32-bit pieces
+# M = 2^-70 (shift >= 63); multipliers below 2^-23 (shifts above 53) move a
+# launch whose multipliers are all below 1/2 from the 32-bit-piece rounding
+# with the folded 64-bit addend to the general 64-bit rounding
 _WIDE_HI = [(1.0, 12, 0), (1.0, 20, 0), (1.0, 30, 0), (0.75, 25, 0), (1.0, 70, 0)]
+# the same without the multipliers below 2^-23 (shifts up to 53: 0.75 * 2^-22
+# has shift 53), so the launch keeps the 32-bit-piece rounding
+_FOLD_HI = [(1.0, 12, 0), (1.0, 20, 0), (1.0, 22, 0), (0.75, 22, 0)]
 # columns that force the 64-bit rounding (multiplier >= 1/2), plus the
 # shift >= 63 and shift == 0 mappings
 _LO_ONLY = [(1.0, 1, 0), (0.75, 0, 1), (3.0, 0, 0), (1000.0, 0, 0), (1.0, -30, 0), (1.0, 70, 0)]
@@ -129,12 +135,17 @@ def _activations(rng, M, K):
     return A
 
 
-@pytest.mark.parametrize("zp_out,relu", [(0, False), (-2, False), (5, True), (-7, True)])
-def test_gemm_ties_shift_ge_32(qp, orc, zp_out, relu):
-    """All multipliers < 1/2: the epilogue that rounds in 32-bit pieces."""
-    print("requant ties, shift >= 32, zp_out", zp_out, "relu", relu, flush=True)
-    rng = np.random.default_rng(40 + zp_out)
-    mult, val = _columns(_TIES_HI * 3 + _WIDE_HI)
+@pytest.mark.parametrize("wide", [False, True])
+@pytest.mark.parametrize("zp_out,relu", [(0, False), (-2, False), (5, True), (-7, True),
+                                         (127, False), (-128, False)])
+def test_gemm_ties_shift_ge_32(qp, orc, zp_out, relu, wide):
+    """All multipliers < 1/2: with every multiplier at least 2^-23 the
+    epilogue that rounds in 32-bit pieces from one folded 64-bit addend per
+    column (zero-point terms, half, output zero point); with smaller ones in
+    the launch (wide) the general 64-bit rounding."""
+    print("requant ties, shift >= 32, zp_out", zp_out, "relu", relu, "wide", wide, flush=True)
+    rng = np.random.default_rng((40 + zp_out) % 997 + 1000 * wide)
+    mult, val = _columns(_TIES_HI * 3 + (_WIDE_HI if wide else _FOLD_HI))
     M, K = 200, 128
     A = _activations(rng, M, K)
     B = _operand_cols(rng, K, val)
@@ -162,12 +173,14 @@ def test_gemm_ties_and_edges_64bit_rounding(qp, orc, zp_out, relu):
     assert (acc[:, c70] != 0).any() and (acc[:, c30] != 0).any()
 
 
-def test_gemm_large_tiles_ties(qp, orc):
+@pytest.mark.parametrize("wide", [False, True])
+def test_gemm_large_tiles_ties(qp, orc, wide):
     """The same tie columns in the 256x256 tile configuration the large GEMM
-    uses (>= 256 tiles of 256x256, K a multiple of 128)."""
-    print("requant ties, 256x256 tiles", flush=True)
+    uses (>= 256 tiles of 256x256, K a multiple of 128): the folded-addend
+    rounding in 32-bit pieces, and (wide) the general 64-bit one."""
+    print("requant ties, 256x256 tiles, wide", wide, flush=True)
     rng = np.random.default_rng(91)
-    base, bval = _columns(_TIES_HI + _WIDE_HI)
+    base, bval = _columns(_TIES_HI + (_WIDE_HI if wide else _FOLD_HI))
     reps = 4096 // base.size + 1
     mult, val = np.tile(base, reps)[:4096], np.tile(bval, reps)[:4096]
     M, K = 4096, 256
