@@ -99,21 +99,6 @@ __device__ __forceinline__ int64_t rhe_shift64(int32_t acc, int32_t m0, int32_t 
   return (t + half_m1 + odd) >> sh;
 }
 
-// The same rounding when sh >= 32, in 32-bit pieces: u = t + 2^(sh-1) (one
-// 32x32+64 multiply-add); floor(u / 2^sh) is the high word shifted by sh-32;
-// u being a multiple of 2^sh marks an exact tie t/2^sh = r - 1/2, whose
-// even neighbour is r with its lowest bit cleared (r - 1 when r is odd, r
-// when even, in two's complement for either sign).
-__device__ __forceinline__ int32_t rhe_shift_hi(int32_t acc, int32_t m0, int64_t half,
-                                                int32_t s2, uint32_t mask) {
-  const int64_t u = (int64_t)acc * (int64_t)m0 + half;
-  const int32_t hi = (int32_t)(u >> 32);
-  const uint32_t lo = (uint32_t)u;
-  const int32_t r = hi >> s2;
-  const bool tie = (lo | ((uint32_t)hi & mask)) == 0u;
-  return tie ? (r & ~1) : r;
-}
-
 __device__ __forceinline__ int32_t clamp_i64(int64_t v, int32_t lo, int32_t hi) {
   v = v < lo ? lo : v;
   v = v > hi ? hi : v;
@@ -212,8 +197,13 @@ __device__ __forceinline__ void gemm_ktile(AccV (&acc)[FN][FM], v4i (&af)[FM],
   }
 }
 
-// kShiftHi: every column's shift is >= 32 (all multipliers below 1/2, known
-// on the host from the weight scales), so the rounding runs in 32-bit pieces.
+// kShiftHi: every column's shift is in 32..53 (all multipliers in [2^-23,
+// 1/2), known on the host from the weight scales), so the rounding runs in
+// 32-bit pieces: u = acc*m0 + one 64-bit addend per column (the zero-point
+// terms and bias times m0, 2^(sh-1), zp_out*2^sh); floor(u / 2^sh) is the
+// high word shifted by sh-32 and already holds zp_out; u a multiple of 2^sh
+// marks an exact tie t/2^sh = r - 1/2, whose even neighbour is r with its
+// lowest bit cleared (before zp_out is added).
 //
 // Data movement (per workgroup tile BM x BN, K in steps of BK bytes):
 //  * A (activations, row-major) goes HBM/L2 -> LDS with direct loads into an
@@ -621,9 +611,6 @@ __global__ __launch_bounds__(NW * 64) void qgemm_s8_kernel(GemmArgs g) {
         out[r] = __builtin_bit_cast(int32_t, y);
       } else if constexpr (kOut32) {
         out[r] = (int32_t)a;
-      } else if constexpr (kShiftHi) {
-        out[r] = clamp_i32(rhe_shift_hi((int32_t)a, mm[r], half[r], s2[r], mask[r]) + g.zp_out,
-                           lo_v, g.hi);
       } else {
         out[r] = clamp_i64(rhe_shift64((int32_t)a, mm[r], ss[r]) + g.zp_out, lo_v, g.hi);
       }
